@@ -1,0 +1,272 @@
+"""Pins for the fp64 oracle: closed forms, special cases, brute force.
+
+Each test checks the oracle against something other than itself, chosen so a
+plausible slip (a dropped term, a wrong sign or index, a transposed operand,
+routing on z instead of x, a linear instead of squared activation, a wrong
+tie-break) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.formats import bf16_to_f64
+from sparse_moe_layer_logits_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small(T=6, d=32, latent=16, n=8, k=3, m=24, ms=40, router="normal", seed=0, experts="bf16"):
+    wl = synth.Workload("t", T=T, d=d, latent=latent, n_experts=n, top_k=k,
+                        expert_hidden=m, shared_hidden=ms, router=router, experts=experts)
+    x, W = synth.make(wl, seed, threads=2)
+    return wl, x, W
+
+
+def bits(a):
+    """float -> bf16 bits; the values used here are exact in bf16."""
+    a = np.asarray(a, dtype=np.float32)
+    b = synth.f32_to_bf16_bits(a)
+    assert np.array_equal(bf16_to_f64(b), a.astype(np.float64)), "value not exact in bf16"
+    return b
+
+
+def scale_bf16(b, c):
+    """Multiply bf16-coded weights by a power of two c (exact)."""
+    return bits(bf16_to_f64(b) * c)
+
+
+# ---------------------------------------------------------------------------
+# worked example computed by hand
+# ---------------------------------------------------------------------------
+
+def test_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    W = dict(router_w=np.array(g["router_w"], np.float32), router_bias=None,
+             w_down=bits(g["w_down"]), w_up=bits(g["w_up"]),
+             expert_w1=bits(g["expert_w1"]), expert_w2=bits(g["expert_w2"]),
+             shared_w1=bits(g["shared_w1"]), shared_w2=bits(g["shared_w2"]))
+    r = oracle.forward(bits(g["x"]), W, g["top_k"], intermediates=True)
+    s = 1.0 / (1.0 + math.exp(-1.0))
+    assert r["idx"].tolist() == g["expected_idx"]
+    np.testing.assert_allclose(r["gates"], [[s, 1 - s]], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(r["z"], g["expected_z"])
+    np.testing.assert_array_equal(r["y_shared"], g["expected_y_shared"])
+    np.testing.assert_allclose(r["y"], [[1 + 2 * s, 1.5 - s]], rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# router: selection, tie-break, softmax
+# ---------------------------------------------------------------------------
+
+def test_zero_router_selects_lowest_indices_with_equal_gates():
+    wl, x, W = small(n=10, k=4)
+    W["router_w"] = np.zeros_like(W["router_w"])
+    r = oracle.forward(x, W, wl.top_k)
+    assert (r["idx"] == np.arange(4)[None, :]).all()
+    assert (r["gates"] == 0.25).all()
+
+
+def _brute_force_set_ok(l, sel):
+    """Every selected expert beats every unselected one under (value, lower index)."""
+    n = len(l)
+    rest = [f for f in range(n) if f not in set(sel)]
+    for e in sel:
+        for f in rest:
+            if not (l[e] > l[f] or (l[e] == l[f] and e < f)):
+                return False
+    return True
+
+
+def test_topk_brute_force_random_and_planted_ties():
+    rng = np.random.default_rng(123)
+    for trial in range(300):
+        n = int(rng.integers(2, 9))
+        k = int(rng.integers(1, n + 1))
+        if trial % 2:
+            l = rng.integers(-2, 3, size=n).astype(np.float64)   # many exact ties
+        else:
+            l = rng.standard_normal(n)
+        idx = oracle.select_topk(l[None, :], k)[0]
+        assert len(set(idx.tolist())) == k
+        assert _brute_force_set_ok(l, idx.tolist())
+        # brute force: the unique K-subset that passes the pairwise test
+        winners = [c for c in itertools.combinations(range(n), k) if _brute_force_set_ok(l, c)]
+        assert len(winners) == 1 and set(winners[0]) == set(idx.tolist())
+        # order inside the selection: descending value, ties to lower index
+        for a, b in zip(idx[:-1], idx[1:]):
+            assert l[a] > l[b] or (l[a] == l[b] and a < b)
+
+
+def test_softmax_closed_forms():
+    l = np.array([[0.3, -1.2, 2.5, 0.0]])
+    idx1 = oracle.select_topk(l, 1)
+    assert idx1.tolist() == [[2]]
+    assert oracle.softmax_selected(l, idx1).tolist() == [[1.0]]
+    idx2 = oracle.select_topk(l, 2)
+    assert idx2.tolist() == [[2, 0]]
+    g = oracle.softmax_selected(l, idx2)[0]
+    sig = 1.0 / (1.0 + math.exp(-(2.5 - 0.3)))
+    assert abs(g[0] - sig) < 1e-15 and abs(g[1] - (1 - sig)) < 1e-15
+    # large logits do not overflow (shift by the max)
+    big = np.array([[1000.0, 999.0]])
+    g = oracle.softmax_selected(big, oracle.select_topk(big, 2))[0]
+    assert abs(g[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_gates_sum_to_one_and_positive():
+    wl, x, W = small(T=16, n=12, k=5, router="zipf")
+    r = oracle.forward(x, W, wl.top_k)
+    assert np.all(np.abs(r["gates"].sum(1) - 1.0) <= 1e-12)
+    assert np.all(r["gates"] > 0)
+    # gates follow the order of the selection (non-increasing)
+    assert np.all(np.diff(r["gates"], axis=1) <= 1e-15)
+
+
+def test_topk_gap():
+    l = np.array([[3.0, 1.0, 2.0, 0.5], [1.0, 1.0, 1.0, 1.0]])
+    assert oracle.topk_gap(l, 2).tolist() == [1.0, 0.0]
+    assert np.isinf(oracle.topk_gap(l, 4)).all()
+
+
+def test_router_bias_enters_selection_and_softmax():
+    wl, x, W = small(T=4, n=6, k=2)
+    W["router_w"] = np.zeros_like(W["router_w"])
+    W["router_bias"] = np.array([0.0, 0.0, 1.0, 0.0, 3.0, 0.0], np.float32)
+    r = oracle.forward(x, W, 2)
+    assert (r["idx"] == [4, 2]).all()
+    s = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(r["gates"], np.tile([s, 1 - s], (4, 1)), atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# whole-layer invariants
+# ---------------------------------------------------------------------------
+
+def _dense_mixture(x_bits, W):
+    """K = N: every expert weighted by a softmax over all N logits.  Written with
+    plain Python loops, independently of the oracle (no selection code)."""
+    x = bf16_to_f64(x_bits)
+    wr = W["router_w"].astype(np.float64)
+    wd, wu = bf16_to_f64(W["w_down"]), bf16_to_f64(W["w_up"])
+    w1, w2 = bf16_to_f64(W["expert_w1"]), bf16_to_f64(W["expert_w2"])
+    s1, s2 = bf16_to_f64(W["shared_w1"]), bf16_to_f64(W["shared_w2"])
+    T, d = x.shape
+    n, m, lat = w1.shape
+    y = np.zeros((T, d))
+    for t in range(T):
+        logit = [math.fsum(wr[e, i] * x[t, i] for i in range(d)) for e in range(n)]
+        mx = max(logit)
+        w = [math.exp(v - mx) for v in logit]
+        tot = math.fsum(w)
+        z = [math.fsum(wd[j, i] * x[t, i] for i in range(d)) for j in range(lat)]
+        acc = [0.0] * lat
+        for e in range(n):
+            h = [max(0.0, math.fsum(w1[e, a, j] * z[j] for j in range(lat))) ** 2 for a in range(m)]
+            for j in range(lat):
+                acc[j] += (w[e] / tot) * math.fsum(w2[e, j, a] * h[a] for a in range(m))
+        hs = [max(0.0, math.fsum(s1[a, i] * x[t, i] for i in range(d))) ** 2 for a in range(s1.shape[0])]
+        for i in range(d):
+            y[t, i] = (math.fsum(wu[i, j] * acc[j] for j in range(lat))
+                       + math.fsum(s2[i, a] * hs[a] for a in range(len(hs))))
+    return y
+
+
+def test_k_equals_n_is_dense_gated_mixture():
+    wl, x, W = small(T=3, d=12, latent=6, n=5, k=5, m=7, ms=9)
+    r = oracle.forward(x, W, 5)
+    y_ref = _dense_mixture(x, W)
+    np.testing.assert_allclose(r["y"], y_ref, rtol=1e-12, atol=1e-12)
+
+
+def _standard_moe(x_bits, W, k):
+    """Standard (non-latent) MoE: y = sum_k g_k E_k(x) + S(x), own selection by sort."""
+    x = bf16_to_f64(x_bits)
+    wr = W["router_w"].astype(np.float64)
+    w1, w2 = bf16_to_f64(W["expert_w1"]), bf16_to_f64(W["expert_w2"])
+    s1, s2 = bf16_to_f64(W["shared_w1"]), bf16_to_f64(W["shared_w2"])
+    out = []
+    for t in range(x.shape[0]):
+        logit = wr @ x[t]
+        chosen = sorted(range(len(logit)), key=lambda e: (-logit[e], e))[:k]
+        ex = np.array([math.exp(logit[e] - logit[chosen[0]]) for e in chosen])
+        g = ex / ex.sum()
+        y = np.zeros(x.shape[1])
+        for gk, e in zip(g, chosen):
+            y += gk * (w2[e] @ (np.maximum(w1[e] @ x[t], 0) ** 2))
+        y += s2 @ (np.maximum(s1 @ x[t], 0) ** 2)
+        out.append(y)
+    return np.array(out)
+
+
+def test_identity_projections_reduce_to_standard_moe():
+    d = 16
+    wl, x, W = small(T=5, d=d, latent=d, n=7, k=3, m=11, ms=13)
+    eye = bits(np.eye(d))
+    W["w_down"], W["w_up"] = eye, eye.copy()
+    r = oracle.forward(x, W, 3)
+    np.testing.assert_allclose(r["y"], _standard_moe(x, W, 3), rtol=1e-12, atol=1e-12)
+
+
+def test_token_permutation_equivariance():
+    wl, x, W = small(T=9, router="zipf")
+    r = oracle.forward(x, W, wl.top_k)
+    p = np.random.default_rng(7).permutation(wl.T)
+    rp = oracle.forward(x[p], W, wl.top_k)
+    np.testing.assert_array_equal(rp["idx"], r["idx"][p])
+    np.testing.assert_allclose(rp["gates"], r["gates"][p], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(rp["y"], r["y"][p], rtol=1e-13, atol=1e-13)
+    # and evaluating a subset of tokens equals the same rows of the full batch
+    rs = oracle.forward(x, W, wl.top_k, tokens=[4, 1])
+    np.testing.assert_allclose(rs["y"], r["y"][[4, 1]], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("which,c,routed_pow,shared_pow", [
+    ("w_down", 2.0, 2, 0),      # routed part is degree-2 homogeneous in z (squared ReLU)
+    ("w_up", 2.0, 1, 0),
+    ("expert_w1", 0.5, 2, 0),
+    ("expert_w2", 4.0, 1, 0),
+    ("shared_w1", 2.0, 0, 2),
+    ("shared_w2", 0.5, 0, 1),
+])
+def test_homogeneity(which, c, routed_pow, shared_pow):
+    wl, x, W = small()
+    r = oracle.forward(x, W, wl.top_k, intermediates=True)
+    W2 = dict(W)
+    W2[which] = scale_bf16(W[which], c)
+    r2 = oracle.forward(x, W2, wl.top_k, intermediates=True)
+    np.testing.assert_array_equal(r2["idx"], r["idx"])   # routing reads x only
+    routed, routed2 = r["y"] - r["y_shared"], r2["y"] - r2["y_shared"]
+    np.testing.assert_allclose(routed2, c ** routed_pow * routed, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r2["y_shared"], c ** shared_pow * r["y_shared"], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_experts_leave_shared_and_zero_shared_leaves_routed():
+    wl, x, W = small()
+    r = oracle.forward(x, W, wl.top_k, intermediates=True)
+    Wz = dict(W, expert_w2=np.zeros_like(W["expert_w2"]))
+    np.testing.assert_allclose(oracle.forward(x, Wz, wl.top_k)["y"], r["y_shared"], atol=1e-13)
+    Ws = dict(W, shared_w1=np.zeros_like(W["shared_w1"]))
+    np.testing.assert_allclose(oracle.forward(x, Ws, wl.top_k)["y"], r["y"] - r["y_shared"], atol=1e-13)
+
+
+def test_only_selected_experts_matter():
+    """Overwriting an expert that no token selected changes nothing; overwriting
+    a selected one changes exactly the tokens that selected it."""
+    wl, x, W = small(T=4, n=12, k=2)
+    r = oracle.forward(x, W, 2)
+    used = set(r["idx"].ravel().tolist())
+    unused = [e for e in range(12) if e not in used][0]
+    W2 = dict(W, expert_w2=W["expert_w2"].copy())
+    W2["expert_w2"][unused] = bits(np.full(W["expert_w2"].shape[1:], 8.0))
+    np.testing.assert_array_equal(oracle.forward(x, W2, 2)["y"], r["y"])
+    e = int(r["idx"][0, 1])
+    W3 = dict(W, expert_w2=W["expert_w2"].copy())
+    W3["expert_w2"][e] = scale_bf16(W["expert_w2"][e], 2.0)
+    y3 = oracle.forward(x, W3, 2)["y"]
+    changed = np.any(np.abs(y3 - r["y"]) > 0, axis=1)
+    assert changed.tolist() == [bool((r["idx"][t] == e).any()) for t in range(4)]

