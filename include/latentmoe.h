@@ -1,0 +1,186 @@
+/*
+ * latentmoe.h -- C ABI of the LatentMoE layer forward for AMD Instinct MI355X (gfx950).
+ *
+ * The layer ("Nemotron 3 Super: Open, Efficient Mixture-of-Experts Hybrid
+ * Mamba-Transformer Model for Agentic Reasoning", section 3.2 LatentMoE): every
+ * token x in R^d gets router logits over N experts at the full width d and a
+ * top-K selection; it is projected by W_down (l x d) into the latent space,
+ * run through its K selected experts in latent width (each expert l -> m -> l),
+ * the gated sum is projected back by W_up (d x l) and added to a full-width
+ * shared expert (d -> m_s -> d).  Shapes of the Super model are in the same
+ * page's section 3.1 table; expert weights may be stored in the block-scaled
+ * 4-bit format of section 3.6 (per-tensor and per-block scales) with E2M1
+ * elements and E4M3 block scales ("Nemotron 3 Ultra", NVFP4 description).
+ *
+ * Readings of points the pages leave open (fixed by this library):
+ *   - router: fp32 logits l = W_r x (+ b), the K largest logits with ties going
+ *     to the lower expert index, gates = softmax over the K selected logits;
+ *   - experts: two matrices per expert with a squared-ReLU activation,
+ *     o = W2 relu(W1 z)^2; the shared expert has the same form at width d and
+ *     is added without a gate; no biases or norms inside the layer;
+ *   - FP4 experts: one E4M3FN scale per 16 consecutive input-dim elements and
+ *     one fp32 scale per expert matrix; element 2j in the low nibble of byte j.
+ *
+ * Conventions: all matrices are row-major; a weight [out, in] computes
+ * y = x * W^T.  bf16 tensors are passed as raw 16-bit patterns.  Every pointer
+ * argument named "device" is HIP device memory of the current device; "host"
+ * pointers are ordinary host memory.  No function throws or aborts; each
+ * returns a status code (LATENTMOE_OK == 0 on success).
+ */
+#ifndef LATENTMOE_H_
+#define LATENTMOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define LATENTMOE_OK 0
+#define LATENTMOE_ERR_INVALID_ARG (-1)  /* null pointer, bad size, T > max_tokens, ... */
+#define LATENTMOE_ERR_UNSUPPORTED (-2)  /* shape outside what the kernels handle      */
+#define LATENTMOE_ERR_OUT_OF_MEMORY (-3) /* workspace allocation failed               */
+#define LATENTMOE_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
+
+/* ---- expert weight formats ---- */
+#define LATENTMOE_EXPERTS_BF16 0
+#define LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 1
+
+typedef struct latentmoe_handle_s* latentmoe_handle_t;
+
+/* Layer shape (host struct).  Requirements, checked by latentmoe_init:
+ * d, latent, expert_hidden, shared_hidden multiples of 64; n_experts a
+ * multiple of 16 and at most 1024; 1 <= top_k <= min(n_experts, 64);
+ * max_tokens >= 1. */
+typedef struct {
+  int32_t d;             /* model width                                   */
+  int32_t latent;        /* latent width l                                */
+  int32_t n_experts;     /* N                                             */
+  int32_t top_k;         /* K                                             */
+  int32_t expert_hidden; /* m (each expert l -> m -> l)                   */
+  int32_t shared_hidden; /* m_s (shared expert d -> m_s -> d)             */
+  int32_t max_tokens;    /* largest T a forward call may pass             */
+  int32_t expert_format; /* LATENTMOE_EXPERTS_*                           */
+} latentmoe_config;
+
+/* Weights (host struct holding device pointers).  The library BORROWS every
+ * buffer: it must stay allocated and unchanged until latentmoe_destroy.
+ * Alignment: every pointer 16-byte aligned. */
+typedef struct {
+  const float* router_w;          /* [N, d] fp32                                  */
+  const float* router_bias;       /* [N] fp32, or NULL for no bias                */
+  const uint16_t* w_down;         /* [l, d] bf16   (W_down)                       */
+  const uint16_t* w_up;           /* [d, l] bf16   (W_up)                         */
+  const void* expert_w1;          /* bf16 [N, m, l]  | FP4 codes u8 [N, m, l/2]   */
+  const void* expert_w2;          /* bf16 [N, l, m]  | FP4 codes u8 [N, l, m/2]   */
+  const uint8_t* expert_w1_scale; /* FP4 only: E4M3FN [N, m, l/16], else NULL     */
+  const uint8_t* expert_w2_scale; /* FP4 only: E4M3FN [N, l, m/16], else NULL     */
+  const float* expert_w1_tscale;  /* FP4 only: fp32 [N], else NULL                */
+  const float* expert_w2_tscale;  /* FP4 only: fp32 [N], else NULL                */
+  const uint16_t* shared_w1;      /* [m_s, d] bf16                                */
+  const uint16_t* shared_w2;      /* [d, m_s] bf16                                */
+} latentmoe_weights;
+
+/* Create a layer handle.  Validates the shape and pointers, allocates the
+ * workspace for cfg->max_tokens tokens (device memory owned by the handle) and
+ * derives the router's split weights on `stream` (the only work enqueued).
+ * cfg, w: host pointers, read during the call only.  out: host pointer that
+ * receives the handle (set to NULL on failure).
+ * Errors: INVALID_ARG (null pointer, format/pointer mismatch), UNSUPPORTED
+ * (shape requirements above), OUT_OF_MEMORY, HIP. */
+int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
+                   latentmoe_handle_t* out);
+
+/* LatentMoE forward for T tokens, enqueued on `stream`, asynchronous: no host
+ * synchronisation and no allocation happen inside.
+ *   x         device, [T, d] bf16 tokens
+ *   y         device, [T, d] fp32 output (fully overwritten)
+ *   topk_idx  device, [T, K] int32 selected experts, largest logit first (ties
+ *             to the lower index), or NULL
+ *   topk_gate device, [T, K] fp32 gates in the same order, or NULL
+ * T == 0 returns OK and enqueues nothing.  Errors (returned before anything is
+ * enqueued): INVALID_ARG for a null handle/x/y, T < 0 or T > max_tokens;
+ * HIP if a launch fails.  Calls that share a handle must not overlap: the
+ * workspace is per handle (use one handle per concurrent stream). */
+int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
+                      int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+/* Free the handle and its workspace.  Work still queued on a stream that uses
+ * the handle must have completed.  NULL is accepted (returns OK). */
+int latentmoe_destroy(latentmoe_handle_t h);
+
+/* Static description of a status code (never NULL). */
+const char* latentmoe_status_string(int status);
+
+/* Bytes of device workspace latentmoe_init would allocate for cfg (host
+ * pointers).  Errors as latentmoe_init's shape checks. */
+int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
+
+/* Intermediates of the last forward on this handle, for tests and tools.
+ * Copies `bytes` bytes of intermediate `which` into device buffer dst on
+ * `stream` (asynchronous).  Layouts for the last call's T:
+ *   LATENTMOE_INTER_Z        [T, l] bf16       latent tokens W_down x
+ *   LATENTMOE_INTER_Y_LAT    [T, l] bf16       gated expert sum (latent), high part
+ *   LATENTMOE_INTER_Y_LAT_LO [T, l] bf16       gated expert sum, remainder
+ *   LATENTMOE_INTER_COUNTS   [N] int32         tokens routed to each expert
+ *   LATENTMOE_INTER_OFFSETS  [N+1] int32       first permuted row of each expert
+ *   LATENTMOE_INTER_ROW_SRC  [T*K] int32       token of each permuted row
+ *   LATENTMOE_INTER_INV      [T*K] int32       permuted row of (t, k)
+ *   LATENTMOE_INTER_H        [T*K, m] bf16     expert hidden activations (permuted)
+ *   LATENTMOE_INTER_HS_HI    [T, m_s] bf16     shared hidden, high part
+ *   LATENTMOE_INTER_HS_LO    [T, m_s] bf16     shared hidden, remainder
+ * Errors: INVALID_ARG for an unknown `which`, a null pointer or more bytes
+ * than the intermediate holds. */
+#define LATENTMOE_INTER_Z 0
+#define LATENTMOE_INTER_Y_LAT 1
+#define LATENTMOE_INTER_COUNTS 2
+#define LATENTMOE_INTER_OFFSETS 3
+#define LATENTMOE_INTER_ROW_SRC 4
+#define LATENTMOE_INTER_INV 5
+#define LATENTMOE_INTER_H 6
+#define LATENTMOE_INTER_HS_HI 7
+#define LATENTMOE_INTER_HS_LO 8
+#define LATENTMOE_INTER_Y_LAT_LO 9
+int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t bytes,
+                         hipStream_t stream);
+
+/* Stage timing with HIP events recorded on the forward's stream.
+ * latentmoe_profile_begin reserves events for up to max_calls forward calls
+ * (host allocation of HIP events; call it outside any timed or captured
+ * region); every later forward records one start/stop pair per stage.
+ * latentmoe_profile_end synchronises those events, writes the summed
+ * milliseconds of each stage to stage_ms (host, n_stages entries, order of
+ * LATENTMOE_STAGE_*), the number of recorded calls to *calls (host), and
+ * stops recording.  Errors: INVALID_ARG (null handle/pointers, max_calls < 1),
+ * HIP. */
+#define LATENTMOE_STAGE_ROUTER 0      /* router logits GEMM                       */
+#define LATENTMOE_STAGE_TOPK 1        /* top-K + softmax                          */
+#define LATENTMOE_STAGE_BUCKET 2      /* counts, offsets, permutation             */
+#define LATENTMOE_STAGE_DOWN_PROJ 3   /* z = W_down x                             */
+#define LATENTMOE_STAGE_EXPERT_UP 4   /* h = relu(W1_e z)^2, grouped               */
+#define LATENTMOE_STAGE_EXPERT_DOWN 5 /* g * W2_e h, grouped                       */
+#define LATENTMOE_STAGE_COMBINE 6     /* y_lat = sum_k                            */
+#define LATENTMOE_STAGE_SHARED_UP 7   /* h_s = relu(S1 x)^2                       */
+#define LATENTMOE_STAGE_SHARED_DOWN 8 /* y = S2 h_s                               */
+#define LATENTMOE_STAGE_UP_PROJ 9     /* y += W_up (y_lat hi + lo)                */
+#define LATENTMOE_NUM_STAGES 10
+int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls);
+int latentmoe_profile_end(latentmoe_handle_t h, float* stage_ms, int n_stages, int* calls);
+
+/* Decode n_blocks block-scaled FP4 blocks with the same in-register decoder
+ * the expert GEMMs use: codes (device, n_blocks * 8 bytes, element 2j in the
+ * low nibble of byte j), scales (device, n_blocks E4M3FN bytes) -> out (device,
+ * n_blocks * 16 bf16).  The per-tensor scale is not applied.  Asynchronous on
+ * `stream`.  Errors: INVALID_ARG (null pointers, n_blocks < 0), HIP. */
+int latentmoe_fp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
+                         uint16_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENTMOE_H_ */

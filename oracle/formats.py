@@ -19,15 +19,9 @@ import numpy as np
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
-    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
-    sign = np.where(b >> 15, -1.0, 1.0)
-    e = (b >> 7) & 0xFF
-    m = (b & 0x7F).astype(np.float64)
-    normal = sign * np.ldexp(1.0 + m / 128.0, (e - 127).astype(np.int32))
-    sub = sign * np.ldexp(m / 128.0, -126)
-    out = np.where(e == 0, sub, normal)
-    out = np.where(e == 0xFF, np.where(m == 0, sign * np.inf, np.nan), out)
-    return out
+    """bf16 bit patterns -> float64: the pattern is the upper half of a binary32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
 def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -60,9 +54,11 @@ def fp4_dequant(packed: np.ndarray, block_scale: np.ndarray, tensor_scale) -> np
     """
     packed = np.asarray(packed, dtype=np.uint8)
     rows, half = packed.shape
-    codes = np.empty((rows, 2 * half), dtype=np.uint8)
-    codes[:, 0::2] = packed & 0xF
-    codes[:, 1::2] = packed >> 4
-    q = e2m1_to_f64(codes)
-    s = np.repeat(e4m3fn_to_f64(block_scale), 16, axis=1)
-    return q * s * float(np.float32(tensor_scale))
+    # decode through 16- and 256-entry tables built with the field decoders above
+    q_table = e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    s_table = e4m3fn_to_f64(np.arange(256, dtype=np.uint16).astype(np.uint8))
+    q = np.empty((rows, half, 2), dtype=np.float64)
+    q[:, :, 0] = np.take(q_table, packed & 0xF)
+    q[:, :, 1] = np.take(q_table, packed >> 4)
+    s = np.take(s_table, np.asarray(block_scale, dtype=np.uint8)) * float(np.float32(tensor_scale))
+    return (q.reshape(rows, -1, 16) * s[:, :, None]).reshape(rows, 2 * half)

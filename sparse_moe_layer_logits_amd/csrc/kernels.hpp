@@ -1,0 +1,86 @@
+// Kernel launch interface used by the host orchestration (latentmoe.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+// epilogue kinds; each applies to four consecutive output columns of one row
+enum Epi : int {
+  EPI_PARTIAL = 0,      // partial[split][row][n] = acc                         (split-K)
+  EPI_BF16 = 1,         // C bf16 = acc
+  EPI_SQRELU_BF16 = 2,  // C bf16 = relu(acc * tscale[e])^2
+  EPI_SQRELU_HILO = 3,  // v = relu(acc)^2; C bf16 = hi(v), C2 bf16 = bf16(v - hi(v))
+  EPI_F32 = 4,          // C f32 = acc (+ bias[n])
+  EPI_F32_ADD = 5,      // C f32 += acc
+  EPI_GATE_F32 = 6,     // C f32 = acc * tscale[e] * row_scale[row]
+  EPI_GATE_BF16 = 7,    // C bf16 = acc * tscale[e] * row_scale[row]
+};
+
+struct GemmSeg {
+  const void* A;  // [rows, lda] bf16
+  const void* B;  // [N, ldb] bf16, or packed FP4 codes [N, ldb/2] bytes
+  int K;          // multiple of 64
+};
+
+// C[row, n] = sum over segments of sum_k A_seg[row, k] * B_seg[n, k]
+struct GemmParams {
+  GemmSeg seg[3];
+  int nseg;
+  int lda, ldb;      // row strides in elements (ldb counts FP4 elements for packed B)
+  int M, N;          // dense rows, output columns
+  // grouped (expert) mode: work tiles built on the device
+  const int* tile_expert;   // null => dense
+  const int* tile_row0;     // first (permuted) row of the tile
+  const int* tile_rows;     // rows in the tile
+  const int* n_tiles;       // number of valid tiles (device scalar)
+  int max_tiles;            // launch bound on tiles
+  int rows_per_tile;        // tile height the tile list was built for (grouped mode)
+  const int* row_index;     // A row of permuted row p (null => A row = p)
+  long long b_stride;       // elements between consecutive experts' B (FP4: elements, i.e. 2 per byte)
+  // block-scaled FP4 B operand
+  const uint8_t* b_scale;   // [E, N, ldb/16] E4M3FN
+  const float* b_tscale;    // [E] fp32 applied to the accumulator (null => 1)
+  // split-K
+  int splits;
+  int k_split;              // k elements per split (multiple of 64)
+  // epilogue
+  int epi;
+  void* C;
+  void* C2;
+  int ldc;
+  const float* bias;        // [N] or null
+  const float* row_scale;   // [rows] or null (gate per permuted row)
+  float* partial;           // [splits, M, N]
+  long long partial_stride; // elements between splits
+};
+
+// weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes)
+void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
+// LDS-tiled MFMA GEMM, 128 x 128 tiles (prefill-like shapes)
+void launch_gemm_tile(const GemmParams& p, hipStream_t s);
+// sum split-K partials and apply the epilogue
+void launch_reduce(const GemmParams& p, hipStream_t s);
+
+// router weight fp32 [N, d] -> three bf16 pieces whose sum is exact
+void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStream_t s);
+
+// per-token top-K + softmax; builds per-16-token expert masks
+void launch_topk(const float* partial, int splits, long long split_stride, const float* bias,
+                 int T, int N, int K, int* idx, float* gates, uint32_t* masks, hipStream_t s);
+// counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile)
+void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
+                        int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
+                        int* tile_rows, int* n_tiles, int max_tiles, hipStream_t s);
+// permuted positions: row_src[p] = token, row_gate[p] = gate, inv[t*K+k] = p
+void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
+                  const int* block_prefix, int T, int N, int K, int* row_src, float* row_gate,
+                  int* inv, hipStream_t s);
+// y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo
+void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
+                    uint16_t* y_lat_lo, hipStream_t s);
+// FP4 dequantisation check helper: codes/scales -> bf16 (exercises the in-register path)
+void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n_blocks16,
+                        uint16_t* out, hipStream_t s);
+
+}  // namespace lmoe

@@ -1,0 +1,544 @@
+// Host orchestration and C ABI of the LatentMoE layer forward.
+//
+// Step order per forward call ("Nemotron 3 Super", section 3.2; the gating
+// network and the shared expert stay at width d, routing and expert compute
+// happen in the latent width l):
+//   router logits (x, width d)  -> top-K + softmax -> bucketing (counts,
+//   offsets, permutation) -> z = W_down x -> grouped expert up (squared ReLU)
+//   -> grouped expert down (times gate) -> combine in k order -> shared expert
+//   (y = S2 relu(S1 x)^2) -> y += W_up y_lat.
+// Everything is enqueued on the caller's stream; the forward allocates nothing
+// and never waits on the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/latentmoe.h"
+#include "kernels.hpp"
+
+using namespace lmoe;
+
+namespace {
+
+constexpr int STREAM_ROWS_BIG = 64;
+constexpr int STREAM_ROWS_SMALL = 16;
+constexpr int TILE_ROWS = 128;
+constexpr int TARGET_BLOCKS = 512;
+
+struct Plan {
+  bool stream;  // weight-streaming kernel (true) or LDS-tiled kernel
+  int splits;
+  int k_split;
+};
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// split-K plan for a dense GEMM of M rows, N columns, K reduction
+Plan plan_dense(int M, int N, int K) {
+  Plan p;
+  p.stream = M <= STREAM_ROWS_BIG;
+  const int per_split = p.stream ? ceil_div(N, 128) * ceil_div(M, STREAM_ROWS_BIG)
+                                 : ceil_div(N, 128) * ceil_div(M, TILE_ROWS);
+  const int gran = p.stream ? 256 : 64;
+  int want = std::max(1, ceil_div(TARGET_BLOCKS, per_split));
+  want = std::min(want, std::max(1, K / gran));
+  int ks = ceil_div(ceil_div(K, want), gran) * gran;
+  p.k_split = ks;
+  p.splits = ceil_div(K, ks);
+  return p;
+}
+
+struct Buffers {
+  uint16_t* pieces = nullptr;
+  float* partial = nullptr;
+  size_t partial_cap = 0;  // floats
+  int* idx = nullptr;
+  float* gates = nullptr;
+  uint32_t* masks = nullptr;
+  int* block_prefix = nullptr;
+  int* counts = nullptr;
+  int* offsets = nullptr;
+  int* tile_expert = nullptr;
+  int* tile_row0 = nullptr;
+  int* tile_rows = nullptr;
+  int* n_tiles = nullptr;
+  int max_tiles_cap = 0;
+  int* row_src = nullptr;
+  float* row_gate = nullptr;
+  int* inv = nullptr;
+  uint16_t* z = nullptr;
+  uint16_t* h = nullptr;
+  float* og = nullptr;
+  uint16_t* y_lat = nullptr;
+  uint16_t* y_lat_lo = nullptr;
+  uint16_t* hs_hi = nullptr;
+  uint16_t* hs_lo = nullptr;
+};
+
+struct Layout {
+  size_t total = 0;
+  std::vector<std::pair<void**, size_t>> items;
+  void add(void** p, size_t bytes) {
+    items.emplace_back(p, bytes);
+    total += (bytes + 255) & ~size_t(255);
+  }
+};
+
+int check_config(const latentmoe_config* c) {
+  if (!c) return LATENTMOE_ERR_INVALID_ARG;
+  if (c->d <= 0 || c->latent <= 0 || c->n_experts <= 0 || c->top_k <= 0 ||
+      c->expert_hidden <= 0 || c->shared_hidden <= 0 || c->max_tokens <= 0)
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (c->expert_format != LATENTMOE_EXPERTS_BF16 &&
+      c->expert_format != LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16)
+    return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->d % 64 || c->latent % 64 || c->expert_hidden % 64 || c->shared_hidden % 64)
+    return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->n_experts % 16 || c->n_experts > 1024) return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->top_k > c->n_experts || c->top_k > 64) return LATENTMOE_ERR_UNSUPPORTED;
+  return LATENTMOE_OK;
+}
+
+size_t max_partial_floats(const latentmoe_config& c) {
+  // every T a forward may see: the plans only change with the tile counts
+  std::vector<int> Ts;
+  for (int t = 1; t <= std::min(c.max_tokens, STREAM_ROWS_BIG); t = t < 16 ? t + 1 : t + 16) Ts.push_back(t);
+  Ts.push_back(std::min(c.max_tokens, STREAM_ROWS_BIG));
+  for (long long t = STREAM_ROWS_BIG + 1; t <= c.max_tokens; t += TILE_ROWS) Ts.push_back((int)t);
+  for (long long t = TILE_ROWS; t <= c.max_tokens; t += TILE_ROWS) Ts.push_back((int)t);
+  Ts.push_back(c.max_tokens);
+  size_t best = 0;
+  for (int T : Ts) {
+    if (T < 1 || T > c.max_tokens) continue;
+    struct G { int N, K; bool always; };
+    const G gs[] = {{c.n_experts, 3 * c.d, true}, {c.latent, c.d, false},
+                    {c.shared_hidden, c.d, false}, {c.d, 2 * c.shared_hidden, false},
+                    {c.d, 2 * c.latent, false}};
+    for (const G& g : gs) {
+      Plan p = plan_dense(T, g.N, g.K);
+      if (p.splits > 1 || g.always) best = std::max(best, (size_t)p.splits * T * g.N);
+    }
+  }
+  return best;
+}
+
+Layout make_layout(const latentmoe_config& c, Buffers& b) {
+  Layout L;
+  const size_t Tm = c.max_tokens, N = c.n_experts, K = c.top_k;
+  const size_t TK = Tm * K;
+  const size_t nblk = (Tm + 15) / 16;
+  b.partial_cap = max_partial_floats(c);
+  b.max_tiles_cap = (int)(ceil_div(TK, STREAM_ROWS_SMALL) + std::min(N, TK));
+  L.add((void**)&b.pieces, 3 * N * c.d * 2);
+  L.add((void**)&b.partial, b.partial_cap * 4);
+  L.add((void**)&b.idx, TK * 4);
+  L.add((void**)&b.gates, TK * 4);
+  L.add((void**)&b.masks, nblk * N * 4);
+  L.add((void**)&b.block_prefix, nblk * N * 4);
+  L.add((void**)&b.counts, N * 4);
+  L.add((void**)&b.offsets, (N + 1) * 4);
+  L.add((void**)&b.tile_expert, (size_t)b.max_tiles_cap * 4);
+  L.add((void**)&b.tile_row0, (size_t)b.max_tiles_cap * 4);
+  L.add((void**)&b.tile_rows, (size_t)b.max_tiles_cap * 4);
+  L.add((void**)&b.n_tiles, 4);
+  L.add((void**)&b.row_src, TK * 4);
+  L.add((void**)&b.row_gate, TK * 4);
+  L.add((void**)&b.inv, TK * 4);
+  L.add((void**)&b.z, Tm * c.latent * 2);
+  L.add((void**)&b.h, TK * c.expert_hidden * 2);
+  L.add((void**)&b.og, TK * c.latent * 4);
+  L.add((void**)&b.y_lat, Tm * c.latent * 2);
+  L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
+  L.add((void**)&b.hs_hi, Tm * c.shared_hidden * 2);
+  L.add((void**)&b.hs_lo, Tm * c.shared_hidden * 2);
+  return L;
+}
+
+}  // namespace
+
+struct latentmoe_handle_s {
+  latentmoe_config cfg;
+  latentmoe_weights w;
+  Buffers b;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  int last_T = 0;
+  // stage timing
+  std::vector<hipEvent_t> events;
+  int prof_max = 0;
+  int prof_calls = 0;
+  bool profiling = false;
+};
+
+namespace {
+
+struct StageTimer {
+  latentmoe_handle_s* h;
+  hipStream_t s;
+  bool on;
+  StageTimer(latentmoe_handle_s* h_, hipStream_t s_)
+      : h(h_), s(s_), on(h_->profiling && h_->prof_calls < h_->prof_max) {}
+  void start(int stage) {
+    if (on) hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2], s);
+  }
+  void stop(int stage) {
+    if (on) hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2 + 1], s);
+  }
+  void done() {
+    if (on) h->prof_calls++;
+  }
+};
+
+GemmParams base_params() {
+  GemmParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.splits = 1;
+  return p;
+}
+
+// dense GEMM C[T, N] = sum_seg A_seg[T, K_seg] B_seg[N, K_seg]^T with a final epilogue;
+// returns the number of k splits (with force_partial the caller reduces them)
+int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool force_partial) {
+  int Ktot = 0;
+  for (int i = 0; i < p.nseg; ++i) Ktot += p.seg[i].K;
+  Plan pl = plan_dense(T, p.N, Ktot);
+  // keep within the partial buffer (it is sized for every T at init)
+  while (pl.splits > 1 && (size_t)pl.splits * T * p.N > h->b.partial_cap) {
+    pl.k_split *= 2;
+    pl.splits = ceil_div(Ktot, pl.k_split);
+  }
+  p.M = T;
+  p.k_split = pl.k_split;
+  p.splits = pl.splits;
+  const int final_epi = p.epi;
+  const bool use_partial = force_partial || pl.splits > 1;
+  if (use_partial) {
+    p.epi = EPI_PARTIAL;
+    p.partial = h->b.partial;
+    p.partial_stride = (long long)T * p.N;
+  }
+  if (pl.stream)
+    launch_gemm_stream(p, false, s);
+  else
+    launch_gemm_tile(p, s);
+  if (use_partial && !force_partial) {
+    GemmParams r = p;
+    r.epi = final_epi;
+    launch_reduce(r, s);
+  }
+  return pl.splits;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* latentmoe_status_string(int status) {
+  switch (status) {
+    case LATENTMOE_OK: return "ok";
+    case LATENTMOE_ERR_INVALID_ARG: return "invalid argument";
+    case LATENTMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case LATENTMOE_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LATENTMOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes) {
+  int st = check_config(cfg);
+  if (st != LATENTMOE_OK) return st;
+  if (!bytes) return LATENTMOE_ERR_INVALID_ARG;
+  Buffers b;
+  *bytes = make_layout(*cfg, b).total;
+  return LATENTMOE_OK;
+}
+
+int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
+                   latentmoe_handle_t* out) {
+  if (!out) return LATENTMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  int st = check_config(cfg);
+  if (st != LATENTMOE_OK) return st;
+  if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
+      !w->shared_w1 || !w->shared_w2)
+    return LATENTMOE_ERR_INVALID_ARG;
+  const bool fp4 = cfg->expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16;
+  if (fp4 && (!w->expert_w1_scale || !w->expert_w2_scale || !w->expert_w1_tscale ||
+              !w->expert_w2_tscale))
+    return LATENTMOE_ERR_INVALID_ARG;
+
+  latentmoe_handle_s* h = new (std::nothrow) latentmoe_handle_s();
+  if (!h) return LATENTMOE_ERR_OUT_OF_MEMORY;
+  h->cfg = *cfg;
+  h->w = *w;
+  Layout L = make_layout(*cfg, h->b);
+  if (hipMalloc(&h->workspace, L.total) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return LATENTMOE_ERR_OUT_OF_MEMORY;
+  }
+  h->workspace_bytes = L.total;
+  char* base = static_cast<char*>(h->workspace);
+  for (auto& it : L.items) {
+    *it.first = base;
+    base += (it.second + 255) & ~size_t(255);
+  }
+  launch_router_split(w->router_w, h->b.pieces, (long long)cfg->n_experts * cfg->d, stream);
+  if (hipGetLastError() != hipSuccess) {
+    hipFree(h->workspace);
+    delete h;
+    return LATENTMOE_ERR_HIP;
+  }
+  *out = h;
+  return LATENTMOE_OK;
+}
+
+int latentmoe_destroy(latentmoe_handle_t h) {
+  if (!h) return LATENTMOE_OK;
+  for (hipEvent_t e : h->events) hipEventDestroy(e);
+  hipError_t e = hipFree(h->workspace);
+  delete h;
+  return e == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}
+
+int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
+                      int32_t* topk_idx, float* topk_gate, hipStream_t s) {
+  if (!h || T < 0) return LATENTMOE_ERR_INVALID_ARG;
+  if (T == 0) return LATENTMOE_OK;
+  if (!x || !y || T > h->cfg.max_tokens) return LATENTMOE_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+
+  const latentmoe_config& c = h->cfg;
+  const latentmoe_weights& w = h->w;
+  Buffers& b = h->b;
+  const int N = c.n_experts, K = c.top_k, d = c.d, L = c.latent, m = c.expert_hidden,
+            ms = c.shared_hidden;
+  const bool fp4 = c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16;
+  const long long TK = (long long)T * K;
+  StageTimer tm(h, s);
+
+  // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
+  tm.start(LATENTMOE_STAGE_ROUTER);
+  GemmParams pr = base_params();
+  for (int i = 0; i < 3; ++i) pr.seg[i] = GemmSeg{x, b.pieces + (size_t)i * N * d, d};
+  pr.nseg = 3;
+  pr.lda = d;
+  pr.ldb = d;
+  pr.N = N;
+  pr.ldc = N;
+  const int router_splits = run_dense(h, pr, T, s, /*force_partial=*/true);
+  tm.stop(LATENTMOE_STAGE_ROUTER);
+
+  // ---- 2. top-K + softmax (sums the router's split partials, adds the bias) ----
+  tm.start(LATENTMOE_STAGE_TOPK);
+  launch_topk(b.partial, router_splits, (long long)T * N, w.router_bias, T, N, K, b.idx, b.gates,
+              b.masks, s);
+  tm.stop(LATENTMOE_STAGE_TOPK);
+
+  // ---- 3. bucketing ----
+  const double avg_rows = (double)TK / N;
+  const bool expert_stream = fp4 || avg_rows <= 48.0;
+  const int rows_per_tile =
+      expert_stream ? (avg_rows <= 8.0 ? STREAM_ROWS_SMALL : STREAM_ROWS_BIG) : TILE_ROWS;
+  const int max_tiles = ceil_div(TK, rows_per_tile) + (int)std::min<long long>(N, TK);
+  tm.start(LATENTMOE_STAGE_BUCKET);
+  launch_bucket_scan(b.masks, T, N, rows_per_tile, b.counts, b.offsets, b.block_prefix,
+                     b.tile_expert, b.tile_row0, b.tile_rows, b.n_tiles, max_tiles, s);
+  launch_place(b.idx, b.gates, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src, b.row_gate,
+               b.inv, s);
+  tm.stop(LATENTMOE_STAGE_BUCKET);
+
+  // ---- 4. z = W_down x ----
+  tm.start(LATENTMOE_STAGE_DOWN_PROJ);
+  GemmParams pd = base_params();
+  pd.seg[0] = GemmSeg{x, w.w_down, d};
+  pd.nseg = 1;
+  pd.lda = d;
+  pd.ldb = d;
+  pd.N = L;
+  pd.epi = EPI_BF16;
+  pd.C = b.z;
+  pd.ldc = L;
+  run_dense(h, pd, T, s, false);
+  tm.stop(LATENTMOE_STAGE_DOWN_PROJ);
+
+  // ---- 5/6. grouped expert GEMMs ----
+  GemmParams pe = base_params();
+  pe.nseg = 1;
+  pe.tile_expert = b.tile_expert;
+  pe.tile_row0 = b.tile_row0;
+  pe.tile_rows = b.tile_rows;
+  pe.n_tiles = b.n_tiles;
+  pe.max_tiles = max_tiles;
+  pe.rows_per_tile = rows_per_tile;
+  pe.M = rows_per_tile;
+  pe.splits = 1;
+
+  tm.start(LATENTMOE_STAGE_EXPERT_UP);
+  GemmParams pu = pe;
+  pu.seg[0] = GemmSeg{b.z, w.expert_w1, L};
+  pu.lda = L;
+  pu.ldb = L;
+  pu.N = m;
+  pu.k_split = L;
+  pu.row_index = b.row_src;
+  pu.b_stride = (long long)m * L;
+  pu.b_scale = fp4 ? w.expert_w1_scale : nullptr;
+  pu.b_tscale = fp4 ? w.expert_w1_tscale : nullptr;
+  pu.epi = EPI_SQRELU_BF16;
+  pu.C = b.h;
+  pu.ldc = m;
+  if (expert_stream)
+    launch_gemm_stream(pu, fp4, s);
+  else
+    launch_gemm_tile(pu, s);
+  tm.stop(LATENTMOE_STAGE_EXPERT_UP);
+
+  tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
+  GemmParams pw = pe;
+  pw.seg[0] = GemmSeg{b.h, w.expert_w2, m};
+  pw.lda = m;
+  pw.ldb = m;
+  pw.N = L;
+  pw.k_split = m;
+  pw.row_index = nullptr;
+  pw.b_stride = (long long)L * m;
+  pw.b_scale = fp4 ? w.expert_w2_scale : nullptr;
+  pw.b_tscale = fp4 ? w.expert_w2_tscale : nullptr;
+  pw.epi = EPI_GATE_F32;
+  pw.row_scale = b.row_gate;
+  pw.C = b.og;
+  pw.ldc = L;
+  if (expert_stream)
+    launch_gemm_stream(pw, fp4, s);
+  else
+    launch_gemm_tile(pw, s);
+  tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
+
+  // ---- 7. combine ----
+  tm.start(LATENTMOE_STAGE_COMBINE);
+  launch_combine(b.og, b.inv, T, K, L, b.y_lat, b.y_lat_lo, s);
+  tm.stop(LATENTMOE_STAGE_COMBINE);
+
+  // ---- 8. shared expert: h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
+  tm.start(LATENTMOE_STAGE_SHARED_UP);
+  GemmParams ps = base_params();
+  ps.seg[0] = GemmSeg{x, w.shared_w1, d};
+  ps.nseg = 1;
+  ps.lda = d;
+  ps.ldb = d;
+  ps.N = ms;
+  ps.epi = EPI_SQRELU_HILO;
+  ps.C = b.hs_hi;
+  ps.C2 = b.hs_lo;
+  ps.ldc = ms;
+  run_dense(h, ps, T, s, false);
+  tm.stop(LATENTMOE_STAGE_SHARED_UP);
+
+  tm.start(LATENTMOE_STAGE_SHARED_DOWN);
+  GemmParams p2 = base_params();
+  p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
+  p2.seg[1] = GemmSeg{b.hs_lo, w.shared_w2, ms};
+  p2.nseg = 2;
+  p2.lda = ms;
+  p2.ldb = ms;
+  p2.N = d;
+  p2.epi = EPI_F32;
+  p2.C = y;
+  p2.ldc = d;
+  run_dense(h, p2, T, s, false);
+  tm.stop(LATENTMOE_STAGE_SHARED_DOWN);
+
+  // ---- 9. y += W_up y_lat ----
+  tm.start(LATENTMOE_STAGE_UP_PROJ);
+  GemmParams pp = base_params();
+  pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
+  pp.seg[1] = GemmSeg{b.y_lat_lo, w.w_up, L};
+  pp.nseg = 2;
+  pp.lda = L;
+  pp.ldb = L;
+  pp.N = d;
+  pp.epi = EPI_F32_ADD;
+  pp.C = y;
+  pp.ldc = d;
+  run_dense(h, pp, T, s, false);
+  tm.stop(LATENTMOE_STAGE_UP_PROJ);
+  tm.done();
+
+  if (topk_idx) hipMemcpyAsync(topk_idx, b.idx, TK * 4, hipMemcpyDeviceToDevice, s);
+  if (topk_gate) hipMemcpyAsync(topk_gate, b.gates, TK * 4, hipMemcpyDeviceToDevice, s);
+  h->last_T = T;
+  return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}
+
+int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t bytes,
+                         hipStream_t s) {
+  if (!h || !dst) return LATENTMOE_ERR_INVALID_ARG;
+  const latentmoe_config& c = h->cfg;
+  const size_t T = h->last_T, K = c.top_k;
+  const void* src = nullptr;
+  size_t have = 0;
+  switch (which) {
+    case LATENTMOE_INTER_Z: src = h->b.z; have = T * c.latent * 2; break;
+    case LATENTMOE_INTER_Y_LAT: src = h->b.y_lat; have = T * c.latent * 2; break;
+    case LATENTMOE_INTER_COUNTS: src = h->b.counts; have = (size_t)c.n_experts * 4; break;
+    case LATENTMOE_INTER_OFFSETS: src = h->b.offsets; have = (size_t)(c.n_experts + 1) * 4; break;
+    case LATENTMOE_INTER_ROW_SRC: src = h->b.row_src; have = T * K * 4; break;
+    case LATENTMOE_INTER_INV: src = h->b.inv; have = T * K * 4; break;
+    case LATENTMOE_INTER_H: src = h->b.h; have = T * K * c.expert_hidden * 2; break;
+    case LATENTMOE_INTER_HS_HI: src = h->b.hs_hi; have = T * c.shared_hidden * 2; break;
+    case LATENTMOE_INTER_HS_LO: src = h->b.hs_lo; have = T * c.shared_hidden * 2; break;
+    case LATENTMOE_INTER_Y_LAT_LO: src = h->b.y_lat_lo; have = T * c.latent * 2; break;
+    default: return LATENTMOE_ERR_INVALID_ARG;
+  }
+  if (bytes > have) return LATENTMOE_ERR_INVALID_ARG;
+  if (bytes == 0) return LATENTMOE_OK;
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess
+             ? LATENTMOE_OK
+             : LATENTMOE_ERR_HIP;
+}
+
+int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls) {
+  if (!h || max_calls < 1) return LATENTMOE_ERR_INVALID_ARG;
+  for (hipEvent_t e : h->events) hipEventDestroy(e);
+  h->events.assign((size_t)max_calls * LATENTMOE_NUM_STAGES * 2, nullptr);
+  for (auto& e : h->events)
+    if (hipEventCreate(&e) != hipSuccess) return LATENTMOE_ERR_HIP;
+  h->prof_max = max_calls;
+  h->prof_calls = 0;
+  h->profiling = true;
+  return LATENTMOE_OK;
+}
+
+int latentmoe_profile_end(latentmoe_handle_t h, float* stage_ms, int n_stages, int* calls) {
+  if (!h || !stage_ms || !calls || n_stages < 0) return LATENTMOE_ERR_INVALID_ARG;
+  h->profiling = false;
+  std::vector<double> sum(LATENTMOE_NUM_STAGES, 0.0);
+  for (int c = 0; c < h->prof_calls; ++c) {
+    for (int st = 0; st < LATENTMOE_NUM_STAGES; ++st) {
+      hipEvent_t a = h->events[((size_t)c * LATENTMOE_NUM_STAGES + st) * 2];
+      hipEvent_t z = h->events[((size_t)c * LATENTMOE_NUM_STAGES + st) * 2 + 1];
+      if (hipEventSynchronize(z) != hipSuccess) return LATENTMOE_ERR_HIP;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, a, z) != hipSuccess) return LATENTMOE_ERR_HIP;
+      sum[st] += ms;
+    }
+  }
+  for (int st = 0; st < n_stages; ++st) stage_ms[st] = st < LATENTMOE_NUM_STAGES ? (float)sum[st] : 0.f;
+  *calls = h->prof_calls;
+  return LATENTMOE_OK;
+}
+
+int latentmoe_fp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
+                         uint16_t* out, hipStream_t s) {
+  if (!codes || !scales || !out || n_blocks < 0) return LATENTMOE_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  launch_fp4_dequant(codes, scales, n_blocks, out, s);
+  return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}
+
+}  // extern "C"

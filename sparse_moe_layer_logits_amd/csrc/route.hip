@@ -1,0 +1,258 @@
+// Routing kernels: router weight split, top-K + softmax, expert bucketing.
+//
+// Gating runs at the full model width d and picks K of N experts per token
+// ("Nemotron 3 Super", section 3.2: the gating network stays in dimension d;
+// section 3.1 table: 512 experts, top-22).  Selection order is (-logit, index):
+// equal logits go to the lower expert index.  Gates are a softmax over the K
+// selected logits.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lmoe {
+
+// ---------------------------------------------------------------------------
+// router weight split: w = hi + mid + lo exactly, each piece a bf16 (truncated
+// 8-bit significands).  x (bf16) times each piece is exact in fp32, so the
+// logits come from exact products accumulated in fp32.
+// ---------------------------------------------------------------------------
+__global__ void router_split_kernel(const float* __restrict__ w, uint16_t* __restrict__ pieces,
+                                    long long n) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = w[i];
+  uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+  float r1 = v - __uint_as_float(hb);
+  uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+  float r2 = r1 - __uint_as_float(mb);
+  uint32_t lb = __float_as_uint(r2) & 0xFFFF0000u;  // r2 has <= 8 significant bits
+  pieces[i] = (uint16_t)(hb >> 16);
+  pieces[n + i] = (uint16_t)(mb >> 16);
+  pieces[2 * n + i] = (uint16_t)(lb >> 16);
+}
+
+void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStream_t s) {
+  router_split_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(w, pieces, n);
+}
+
+// ---------------------------------------------------------------------------
+// top-K: one wavefront per token.  Logit e lives in lane e % 64, slot e / 64.
+// Keys (orderable float bits << 32 | ~index) make "larger logit, then lower
+// index" a plain unsigned maximum.
+// ---------------------------------------------------------------------------
+constexpr int TOPK_TOKENS_PER_BLOCK = 16;  // one wave each; masks are 16 bits wide
+
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal logits must tie
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int SLOTS>
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ partial, int splits,
+                                                    long long split_stride,
+                                                    const float* __restrict__ bias, int T, int N,
+                                                    int K, int* __restrict__ idx_out,
+                                                    float* __restrict__ gate_out,
+                                                    uint32_t* __restrict__ masks) {
+  __shared__ uint32_t smask[1024];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * TOPK_TOKENS_PER_BLOCK + w;
+  for (int e = threadIdx.x; e < N; e += blockDim.x) smask[e] = 0u;
+  __syncthreads();
+
+  if (t < T) {
+    // this lane's logits: experts lane, lane + 64, ...
+    uint32_t okey[SLOTS];  // orderable logit bits; 0 marks an empty or removed slot
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const int e = j * 64 + lane;
+      okey[j] = 0u;
+      if (e < N) {
+        const float* pp = partial + (long long)t * N + e;
+        float v = 0.0f;
+#pragma unroll 1
+        for (int s = 0; s < splits; ++s) v += pp[s * split_stride];
+        if (bias) v += bias[e];
+        okey[j] = orderable(v);
+      }
+    }
+    // lane-local best: largest value, then lowest slot (= lowest expert index)
+    auto local_best = [&]() -> unsigned long long {
+      uint32_t bv = 0u;
+      int bj = 0;
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) {
+        if (okey[j] > bv) {
+          bv = okey[j];
+          bj = j;
+        }
+      }
+      return bv ? (((unsigned long long)bv << 32) | (uint32_t)(~(uint32_t)(bj * 64 + lane))) : 0ull;
+    };
+    unsigned long long best = local_best();
+
+    float my_val = 0.0f;
+    int my_idx = 0;
+    for (int k = 0; k < K; ++k) {
+      const unsigned long long win = wave_max_u64(best);
+      const int e = (int)(~(uint32_t)win);
+      if (lane == k) {
+        my_idx = e;
+        my_val = from_orderable((uint32_t)(win >> 32));
+      }
+      if ((e & 63) == lane) {  // the owner removes the winner
+        const int jw = e >> 6;
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j)
+          if (j == jw) okey[j] = 0u;
+        best = local_best();
+      }
+    }
+    // softmax over the K selected logits; the first selected one is the maximum
+    const float vmax = __shfl(my_val, 0, 64);
+    const float ex = lane < K ? expf(my_val - vmax) : 0.0f;
+    const float tot = wave_sum(ex);
+    if (lane < K) {
+      idx_out[(long long)t * K + lane] = my_idx;
+      gate_out[(long long)t * K + lane] = ex / tot;
+      atomicOr(&smask[my_idx], 1u << w);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) masks[(long long)blockIdx.x * N + e] = smask[e];
+}
+
+void launch_topk(const float* partial, int splits, long long split_stride, const float* bias,
+                 int T, int N, int K, int* idx, float* gates, uint32_t* masks, hipStream_t s) {
+  const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  if (N <= 512)
+    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(partial, splits, split_stride,
+                                                                  bias, T, N, K, idx, gates, masks);
+  else
+    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(partial, splits, split_stride,
+                                                                   bias, T, N, K, idx, gates, masks);
+}
+
+// ---------------------------------------------------------------------------
+// bucketing.  Permuted order is (expert, token): rows of expert e occupy
+// [offsets[e], offsets[e+1]) sorted by token.  The rank of token t inside
+// expert e is a prefix over 16-token blocks plus a popcount inside the block,
+// so the order is deterministic.  One workgroup, thread e owns expert e.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(
+    const uint32_t* __restrict__ masks, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ block_prefix, int* __restrict__ tile_expert,
+    int* __restrict__ tile_row0, int* __restrict__ tile_rows, int* __restrict__ n_tiles,
+    int max_tiles) {
+  __shared__ int scan_a[1024];
+  __shared__ int scan_b[1024];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < N) {
+    int b = 0;
+    for (; b + 4 <= nblk; b += 4) {
+      uint32_t m0 = masks[(long long)(b + 0) * N + e];
+      uint32_t m1 = masks[(long long)(b + 1) * N + e];
+      uint32_t m2 = masks[(long long)(b + 2) * N + e];
+      uint32_t m3 = masks[(long long)(b + 3) * N + e];
+      block_prefix[(long long)(b + 0) * N + e] = run; run += __popc(m0);
+      block_prefix[(long long)(b + 1) * N + e] = run; run += __popc(m1);
+      block_prefix[(long long)(b + 2) * N + e] = run; run += __popc(m2);
+      block_prefix[(long long)(b + 3) * N + e] = run; run += __popc(m3);
+    }
+    for (; b < nblk; ++b) {
+      uint32_t m = masks[(long long)b * N + e];
+      block_prefix[(long long)b * N + e] = run;
+      run += __popc(m);
+    }
+    counts[e] = run;
+  }
+  const int ntile_e = (e < N) ? (run + tile_rows_max - 1) / tile_rows_max : 0;
+  // two inclusive scans at once (rows and tiles), Hillis-Steele over the block
+  scan_a[e] = (e < N) ? run : 0;
+  scan_b[e] = ntile_e;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int a = scan_a[e], bb = scan_b[e];
+    if (e >= off) { a += scan_a[e - off]; bb += scan_b[e - off]; }
+    __syncthreads();
+    scan_a[e] = a;
+    scan_b[e] = bb;
+    __syncthreads();
+  }
+  const int row_start = scan_a[e] - ((e < N) ? run : 0);
+  const int tile_start = scan_b[e] - ntile_e;
+  if (e < N) {
+    offsets[e] = row_start;
+    for (int i = 0; i < ntile_e; ++i) {
+      const int j = tile_start + i;
+      if (j < max_tiles) {
+        tile_expert[j] = e;
+        tile_row0[j] = row_start + i * tile_rows_max;
+        tile_rows[j] = min(tile_rows_max, run - i * tile_rows_max);
+      }
+    }
+  }
+  if (e == 0) {
+    offsets[N] = scan_a[1023];
+    n_tiles[0] = min(scan_b[1023], max_tiles);
+  }
+}
+
+void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
+                        int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
+                        int* tile_rows, int* n_tiles, int max_tiles, hipStream_t s) {
+  const int nblk = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  bucket_scan_kernel<<<1, 1024, 0, s>>>(masks, nblk, N, tile_rows_max, counts, offsets,
+                                        block_prefix, tile_expert, tile_row0, tile_rows, n_tiles,
+                                        max_tiles);
+}
+
+__global__ void place_kernel(const int* __restrict__ idx, const float* __restrict__ gates,
+                             const uint32_t* __restrict__ masks, const int* __restrict__ offsets,
+                             const int* __restrict__ block_prefix, int T, int N, int K,
+                             int* __restrict__ row_src, float* __restrict__ row_gate,
+                             int* __restrict__ inv) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)T * K) return;
+  const int t = (int)(i / K);
+  const int e = idx[i];
+  const int b = t / TOPK_TOKENS_PER_BLOCK;
+  const int tl = t % TOPK_TOKENS_PER_BLOCK;
+  const uint32_t m = masks[(long long)b * N + e];
+  const int pos = offsets[e] + block_prefix[(long long)b * N + e] + __popc(m & ((1u << tl) - 1u));
+  row_src[pos] = t;
+  row_gate[pos] = gates[i];
+  inv[i] = pos;
+}
+
+void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
+                  const int* block_prefix, int T, int N, int K, int* row_src, float* row_gate,
+                  int* inv, hipStream_t s) {
+  const long long n = (long long)T * K;
+  place_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, gates, masks, offsets,
+                                                           block_prefix, T, N, K, row_src,
+                                                           row_gate, inv);
+}
+
+}  // namespace lmoe

@@ -1,0 +1,123 @@
+"""Helpers shared by the GPU parity tests: run the HIP layer through the C ABI
+and compare it with the fp64 oracle on the same seeded bytes."""
+import sys
+import time
+
+import numpy as np
+
+import oracle
+from sparse_moe_layer_logits_amd import binding, synth
+
+
+def log(*a):
+    print("[gpu-test %s]" % time.strftime("%H:%M:%S"), *a, flush=True)
+    sys.stdout.flush()
+
+
+def run_layer(wl, x, W, max_tokens=None, extra=()):
+    """Upload, run one forward through the C ABI, copy results back."""
+    import torch
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens or wl.T)
+    xd = binding.to_device(x)
+    y, idx, g = layer.forward(xd)
+    inter = {}
+    T, K, L = wl.T, wl.top_k, wl.latent
+    shapes = dict(z=((T, L), torch.int16), y_lat=((T, L), torch.int16), y_lat_lo=((T, L), torch.int16),
+                  counts=((wl.n_experts,), torch.int32), offsets=((wl.n_experts + 1,), torch.int32),
+                  row_src=((T * K,), torch.int32), inv=((T * K,), torch.int32))
+    for name in extra:
+        shp, dt = shapes[name]
+        inter[name] = layer.intermediate(name, shp, dt)
+    torch.cuda.synchronize()
+    out = dict(y=y.cpu().numpy().astype(np.float64), idx=idx.cpu().numpy(), gates=g.cpu().numpy())
+    for k, v in inter.items():
+        a = v.cpu().numpy()
+        out[k] = a.view(np.uint16) if a.dtype == np.int16 else a
+    layer.close()
+    del Wd, xd, y, idx, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def check_topk(idx_gpu, gates_gpu, ref_idx, ref_gates, gate_tol=1e-6):
+    """idx: bit-exact as per-token sets; gates matched by expert id."""
+    assert idx_gpu.shape == ref_idx.shape
+    for t in range(ref_idx.shape[0]):
+        a, b = sorted(idx_gpu[t].tolist()), sorted(ref_idx[t].tolist())
+        assert a == b, "token %d: gpu %s oracle %s" % (t, a, b)
+        gm = dict(zip(idx_gpu[t].tolist(), gates_gpu[t].tolist()))
+        rm = dict(zip(ref_idx[t].tolist(), ref_gates[t].tolist()))
+        for e in rm:
+            assert abs(gm[e] - rm[e]) <= gate_tol, (t, e, gm[e], rm[e])
+    assert np.all(np.abs(gates_gpu.sum(1) - 1.0) <= 1e-6)
+
+
+def check_y(y_gpu, y_ref, tol):
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.max(np.abs(y_gpu - y_ref)))
+    log("max|gpu-oracle| = %.3e, rms(oracle) = %.3e, ratio = %.3e (bound %.0e)" % (err, rms, err / rms, tol))
+    assert err <= tol * rms, (err, rms)
+    return err / rms
+
+
+def check_bucketing(out, idx, N, K):
+    """counts, offsets, stable (expert, token) permutation and its inverse."""
+    T = idx.shape[0]
+    counts = np.bincount(idx.ravel(), minlength=N)
+    assert np.array_equal(out["counts"], counts)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    assert np.array_equal(out["offsets"], offs)
+    row_src, inv = out["row_src"], out["inv"]
+    assert sorted(inv.tolist()) == list(range(T * K))          # a permutation
+    for e in range(N):
+        seg = row_src[offs[e]:offs[e + 1]]
+        toks = np.nonzero((idx == e).any(1))[0]
+        assert np.array_equal(seg, toks), e                    # sorted by token: stable
+    flat_t = np.repeat(np.arange(T), K)
+    assert np.array_equal(row_src[inv], flat_t)                # inverse
+    e_of_pos = np.repeat(np.arange(N), counts)
+    assert np.array_equal(e_of_pos[inv], idx.ravel())
+
+
+def full_check(wl, x, W, tol=1e-2, extra=("z", "y_lat", "y_lat_lo", "counts", "offsets", "row_src", "inv"),
+               max_tokens=None):
+    out = run_layer(wl, x, W, max_tokens=max_tokens, extra=extra)
+    ref = oracle.forward(x, W, wl.top_k, intermediates=True)
+    check_topk(out["idx"], out["gates"], ref["idx"], ref["gates"])
+    ratio = check_y(out["y"], ref["y"], tol)
+    if "z" in out:
+        z = oracle.bf16_to_f64(out["z"])
+        rz = ref["z"]
+        assert np.all(np.abs(z - rz) <= 2.0 ** -8 * np.abs(rz) + 1e-5 * np.sqrt(np.mean(rz ** 2)))
+    if "y_lat" in out:
+        # hi + lo carries the fp32 sum; what remains is the bf16 rounding of z and h
+        yl = oracle.bf16_to_f64(out["y_lat"]) + oracle.bf16_to_f64(out["y_lat_lo"])
+        ry = ref["y_lat"]
+        assert np.max(np.abs(yl - ry)) <= 3e-2 * np.sqrt(np.mean(ry ** 2))
+    if "counts" in out:
+        check_bucketing(out, out["idx"], wl.n_experts, wl.top_k)
+    return out, ref, ratio
+
+
+def sampled_check(name, n_sample, tol, seed=0):
+    """Full-size workload: top-K on every token against the oracle's fp64 logits,
+    bucketing invariants on every token, outputs on a spread sample of tokens."""
+    wl = synth.WORKLOADS[name]
+    t0 = time.time()
+    x, W = synth.make(wl, seed, redraws=synth.load_redraws(name, seed))
+    log("%s: generated inputs in %.1fs" % (name, time.time() - t0))
+    out = run_layer(wl, x, W, extra=("counts", "offsets", "row_src", "inv"))
+    log("%s: gpu forward done" % name)
+    logits = oracle.router_logits(x, W["router_w"], W["router_bias"])
+    assert np.all(oracle.topk_gap(logits, wl.top_k) >= 1e-4)
+    ref_idx = oracle.select_topk(logits, wl.top_k)
+    ref_g = oracle.softmax_selected(logits, ref_idx)
+    check_topk(out["idx"], out["gates"], ref_idx, ref_g)
+    check_bucketing(out, out["idx"], wl.n_experts, wl.top_k)
+    log("%s: top-K and bucketing match on all %d tokens" % (name, wl.T))
+    toks = np.unique(np.linspace(0, wl.T - 1, n_sample).astype(int))
+    ref = oracle.forward(x, W, wl.top_k, tokens=toks)
+    ratio = check_y(out["y"][toks], ref["y"], tol)
+    log("%s: outputs match on %d sampled tokens" % (name, len(toks)))
+    return ratio

@@ -1,0 +1,73 @@
+"""The C-ABI library: it builds, loads without a GPU, and exports every
+function that include/latentmoe.h declares.  No compute calls are made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_layer_logits_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "latentmoe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(latentmoe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("latentmoe_init", "latentmoe_forward", "latentmoe_destroy"):
+        assert must in names
+    assert set(names) == set(binding.EXPORTED)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("liblatentmoe.so not built; run python -m sparse_moe_layer_logits_amd.build")
+    return ctypes.CDLL(binding.LIB_PATH)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_host_side_validation(lib):
+    # host-only entry points: no device work happens in these calls
+    assert binding.status_string(0) == "ok"
+    assert binding.status_string(-1) == "invalid argument"
+    assert binding.status_string(12345) == "unknown status"
+    cfg = binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 0)
+    n = binding.latentmoe_workspace_bytes(cfg)
+    assert n > 0
+    bad = [binding.latentmoe_config(250, 64, 16, 4, 128, 256, 8, 0),   # d not a multiple of 64
+           binding.latentmoe_config(256, 64, 16, 17, 128, 256, 8, 0),  # K > N
+           binding.latentmoe_config(256, 64, 20, 4, 128, 256, 8, 0),   # N not a multiple of 16
+           binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 7)]   # unknown format
+    for c in bad:
+        with pytest.raises(binding.LatentMoEError) as e:
+            binding.latentmoe_workspace_bytes(c)
+        assert e.value.status == binding.LATENTMOE_ERR_UNSUPPORTED
+    with pytest.raises(binding.LatentMoEError) as e:
+        binding.latentmoe_workspace_bytes(binding.latentmoe_config(256, 64, 16, 4, 128, 256, 0, 0))
+    assert e.value.status == binding.LATENTMOE_ERR_INVALID_ARG
+    # init rejects null weight pointers before touching the device
+    w = binding.latentmoe_weights()
+    with pytest.raises(binding.LatentMoEError) as e:
+        binding.latentmoe_init(cfg, w, 0)
+    assert e.value.status == binding.LATENTMOE_ERR_INVALID_ARG
+    # forward / destroy on a null handle
+    assert lib.latentmoe_forward(None, None, 1, None, None, None, None) == binding.LATENTMOE_ERR_INVALID_ARG
+    assert lib.latentmoe_destroy(None) == 0
+
+
+def test_workspace_grows_with_max_tokens():
+    a = binding.latentmoe_workspace_bytes(binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 64, 0))
+    b = binding.latentmoe_workspace_bytes(binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 8192, 0))
+    assert b > a
+    assert b < 4 << 30   # the prefill workspace stays a few GB

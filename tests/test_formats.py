@@ -7,15 +7,29 @@ from oracle.formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant
 from sparse_moe_layer_logits_amd import synth
 
 
-def test_bf16_decoder_against_float32_bit_cast():
-    # every bf16 pattern equals the float32 with the same upper 16 bits
+def _bf16_from_fields(b):
+    """bf16 value from its sign / exponent / mantissa fields (IEEE binary32 layout,
+    8-bit exponent with bias 127, 7 stored mantissa bits, subnormals at exponent 0)."""
+    b = b.astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    m = (b & 0x7F).astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        normal = sign * np.ldexp(1.0 + m / 128.0, (e - 127).astype(np.int32))
+        out = np.where(e == 0, sign * np.ldexp(m / 128.0, -126), normal)
+        return np.where(e == 0xFF, np.where(m == 0, sign * np.inf, np.nan), out)
+
+
+def test_bf16_decoder_against_field_definition():
+    # every one of the 65536 patterns, decoded from its bit fields
     b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
-    with np.errstate(invalid='ignore'):
-        ref = (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    got = bf16_to_f64(b)
-    both_nan = np.isnan(ref) & np.isnan(got)
-    assert np.array_equal(got[~both_nan], ref[~both_nan])
-    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ref = _bf16_from_fields(b)
+    with np.errstate(invalid="ignore"):
+        got = bf16_to_f64(b)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
 def test_bf16_known_values():
