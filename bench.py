@@ -1,0 +1,225 @@
+"""LatentMoE layer forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload super_decode]
+
+One step is one whole layer forward (router, top-K, bucketing, W_down, grouped
+expert GEMMs, combine, shared expert, W_up) over one batch of seeded synthetic
+tokens already resident in HBM.  Prints one JSON line with the throughput, the
+roofline of the dominant kernel (timed with HIP events on the forward's stream
+during the timed steps) and the fp64 oracle timed on the host cores over a
+bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "LatentMoE layer tokens/s; % HBM peak (decode) / % MFMA peak (prefill)"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {  # kernel -> source file whose hash pins stored counter data
+    "gemm_stream_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_stream.hip",
+    "gemm_tile_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_tile.hip",
+}
+
+
+def log(*a):
+    print("[bench %s]" % time.strftime("%H:%M:%S"), *a, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    h = hashlib.sha256()
+    for p in (path, "sparse_moe_layer_logits_amd/csrc/epilogue.hpp",
+              "sparse_moe_layer_logits_amd/csrc/common.hpp", "sparse_moe_layer_logits_amd/csrc/fp4.hpp"):
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(wl, touched):
+    """Whole-layer algorithmic bytes and flops (what the method must move and
+    compute; intermediates excluded, multiply-add = 2 flops)."""
+    d, l, n, k, m, ms, T = wl.d, wl.latent, wl.n_experts, wl.top_k, wl.expert_hidden, wl.shared_hidden, wl.T
+    beta = 2.0 if wl.experts == "bf16" else 0.5 + 1.0 / 16
+    per_expert_extra = 0 if wl.experts == "bf16" else 8
+    bytes_ = (n * d * 4 + 2 * l * d * 2 + touched * (2 * l * m * beta + per_expert_extra)
+              + 2 * d * ms * 2 + T * d * 2 + T * d * 4)
+    flops = 2.0 * T * (d * n + 2 * d * l + 2 * k * l * m + 2 * d * ms)
+    return bytes_, flops
+
+
+def expert_kernel_units(wl, touched, stage):
+    """Algorithmic bytes and flops of one launch of a grouped expert GEMM:
+    the touched experts' weight matrix, the T*K routed input rows, the T*K
+    output rows (bf16 rows for the method's activations)."""
+    l, m, TK = wl.latent, wl.expert_hidden, wl.T * wl.top_k
+    wbytes = l * m * (2.0 if wl.experts == "bf16" else 0.5 + 1.0 / 16)
+    if stage == "expert_up":
+        io = TK * l * 2 + TK * m * 2
+    else:
+        io = TK * m * 2 + TK * l * 2
+    return touched * wbytes + io, 2.0 * TK * l * m
+
+
+def cpu_baseline(wl, x, W, budget_s=15.0):
+    """The fp64 oracle on the host cores over a bounded sample of tokens."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = 2
+    t0 = time.time()
+    oracle.forward(x[:n], W, wl.top_k)
+    dt = time.time() - t0
+    # grow the sample to fill about budget_s of CPU work
+    n2 = int(min(wl.T, max(n, n * budget_s / max(dt, 1e-3))))
+    if n2 > n:
+        t0 = time.time()
+        oracle.forward(x[:n2], W, wl.top_k)
+        dt = time.time() - t0
+        n = n2
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "first %d of the %d tokens of the %s batch, fp64 numpy, %.1f s" % (n, wl.T, wl.name, dt)}
+
+
+def stored_traffic(kernel, workload):
+    path = os.path.join(PROFILES, "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None    # the kernel changed since the counters were taken
+    return d
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="super_decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain fp32 copy kernel of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel "
+              "sharding is described in DESIGN.md, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_moe_layer_logits_amd import binding, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    x, W = synth.make(wl, args.seed, redraws=synth.load_redraws(wl.name, args.seed))
+    log("generated %s inputs in %.1fs" % (wl.name, time.time() - t0))
+    torch.cuda.set_device(0)
+    Wd = binding.upload_weights(W)
+    xd = binding.to_device(x)
+    stream = torch.cuda.current_stream()
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T, stream=stream)
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.T, wl.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((wl.T, wl.top_k), dtype=torch.float32, device="cuda")
+
+    for _ in range(args.warmup):
+        layer.forward(xd, y, idx, gates)
+    torch.cuda.synchronize()
+    counts = layer.intermediate("counts", (wl.n_experts,), torch.int32).cpu().numpy()
+    touched = int((counts > 0).sum())
+    log("warmup done; %d experts touched" % touched)
+
+    # timed region 1: the step as a serving loop runs it (graph replay of the forward)
+    for _ in range(3):
+        layer.forward(xd, y, idx, gates, graph=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(xd, y, idx, gates, graph=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_per_s = wl.T * args.steps / elapsed
+    log("timed %d graph-replayed steps: %.4f ms/step" % (args.steps, ms_per_step))
+
+    # timed region 2: the same steps launched eagerly, with HIP events on the
+    # forward's streams around each stage (per-kernel durations for the roofline)
+    layer.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(xd, y, idx, gates)
+    torch.cuda.synchronize()
+    eager_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    stage_ms, calls = layer.profile_end()
+    log("timed %d eager steps with stage events: %.4f ms/step" % (args.steps, eager_ms))
+    for k, v in stage_ms.items():
+        log("  stage %-12s %.4f ms" % (k, v / max(calls, 1)))
+
+    alg_bytes, alg_flops = algorithmic(wl, touched)
+    step_s = ms_per_step / 1e3
+    hbm_bound = alg_flops / alg_bytes < 1e3 * BF16_PEAK_TFLOPS / HBM_PEAK_GBS
+    dom = max(("expert_up", "expert_down"), key=lambda s: stage_ms[s])
+    dom_s = stage_ms[dom] / calls / 1e3
+    kb, kf = expert_kernel_units(wl, touched, dom)
+    avg_rows = wl.T * wl.top_k / wl.n_experts
+    kernel = "gemm_stream_kernel" if (wl.experts == "fp4" or avg_rows <= 48) else "gemm_tile_kernel"
+    if hbm_bound:
+        achieved, peak, unit, bound = kb / dom_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = kf / dom_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    tr = stored_traffic(kernel, wl.name)
+    traffic = None if tr is None else tr["hbm_bytes_per_launch"]
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": "%s (%s)" % (kernel, dom), "launch_ms": round(dom_s * 1e3, 5),
+                "alg_bytes_per_launch": int(kb), "alg_flops_per_launch": kf}
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal weights and tokens, N(0, 1/fan_in))",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "latent": wl.latent,
+                   "n_experts": wl.n_experts, "top_k": wl.top_k, "expert_hidden": wl.expert_hidden,
+                   "shared_hidden": wl.shared_hidden, "experts": wl.experts, "router": wl.router,
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "layer": {"alg_bytes": int(alg_bytes), "alg_flops": alg_flops, "experts_touched": touched,
+                  "eager_ms_per_step_with_events": round(eager_ms, 5),
+                  "hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(alg_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "stage_ms": {k: round(v / max(calls, 1), 5) for k, v in stage_ms.items()}},
+    }
+    layer.close()
+    del Wd, xd
+    torch.cuda.empty_cache()
+    if args.copy_probe_mib:
+        # elementwise copy that reads and writes exactly n*4 bytes per launch
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log("copy probe: 5 launches of %d MiB read + %d MiB write" % (args.copy_probe_mib, args.copy_probe_mib))
+        del a, b
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(wl, x, W)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

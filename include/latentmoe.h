@@ -109,6 +109,18 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
 int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
                       int32_t* topk_idx, float* topk_gate, hipStream_t stream);
 
+/* Same contract and results as latentmoe_forward, replayed as a HIP graph.
+ * The first call for a given (x, T, y, topk_idx, topk_gate) captures the whole
+ * forward (all its streams) into a graph and instantiates it; that call
+ * allocates graph resources.  Later calls with the same arguments only
+ * enqueue hipGraphLaunch on `stream`, which removes the per-kernel launch
+ * gaps of a serving loop; the buffers' contents may change between calls.
+ * Different arguments replace the cached graph.  Errors as latentmoe_forward,
+ * plus HIP when capture or instantiation fails.  Stage timing does not apply
+ * to graph replays. */
+int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
+                            int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
 /* Free the handle and its workspace.  Work still queued on a stream that uses
  * the handle must have completed.  NULL is accepted (returns OK). */
 int latentmoe_destroy(latentmoe_handle_t h);
@@ -133,6 +145,8 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
  *   LATENTMOE_INTER_H        [T*K, m] bf16     expert hidden activations (permuted)
  *   LATENTMOE_INTER_HS_HI    [T, m_s] bf16     shared hidden, high part
  *   LATENTMOE_INTER_HS_LO    [T, m_s] bf16     shared hidden, remainder
+ *   LATENTMOE_INTER_Z_LO     [T, l] bf16       latent tokens, remainder
+ *   LATENTMOE_INTER_H_LO     [T*K, m] bf16     expert hidden, remainder
  * Errors: INVALID_ARG for an unknown `which`, a null pointer or more bytes
  * than the intermediate holds. */
 #define LATENTMOE_INTER_Z 0
@@ -145,18 +159,21 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
 #define LATENTMOE_INTER_HS_HI 7
 #define LATENTMOE_INTER_HS_LO 8
 #define LATENTMOE_INTER_Y_LAT_LO 9
+#define LATENTMOE_INTER_Z_LO 10
+#define LATENTMOE_INTER_H_LO 11
 int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t bytes,
                          hipStream_t stream);
 
-/* Stage timing with HIP events recorded on the forward's stream.
+/* Stage timing with HIP events recorded on the stream each stage runs on.
  * latentmoe_profile_begin reserves events for up to max_calls forward calls
  * (host allocation of HIP events; call it outside any timed or captured
- * region); every later forward records one start/stop pair per stage.
+ * region); every later latentmoe_forward records one start/stop pair for each
+ * stage whose bit (1 << LATENTMOE_STAGE_*) is set in stage_mask.
  * latentmoe_profile_end synchronises those events, writes the summed
  * milliseconds of each stage to stage_ms (host, n_stages entries, order of
  * LATENTMOE_STAGE_*), the number of recorded calls to *calls (host), and
- * stops recording.  Errors: INVALID_ARG (null handle/pointers, max_calls < 1),
- * HIP. */
+ * stops recording (stages outside the mask report 0).  Errors: INVALID_ARG
+ * (null handle/pointers, max_calls < 1), HIP. */
 #define LATENTMOE_STAGE_ROUTER 0      /* router logits GEMM                       */
 #define LATENTMOE_STAGE_TOPK 1        /* top-K + softmax                          */
 #define LATENTMOE_STAGE_BUCKET 2      /* counts, offsets, permutation             */
@@ -168,7 +185,7 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
 #define LATENTMOE_STAGE_SHARED_DOWN 8 /* y = S2 h_s                               */
 #define LATENTMOE_STAGE_UP_PROJ 9     /* y += W_up (y_lat hi + lo)                */
 #define LATENTMOE_NUM_STAGES 10
-int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls);
+int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls, uint32_t stage_mask);
 int latentmoe_profile_end(latentmoe_handle_t h, float* stage_ms, int n_stages, int* calls);
 
 /* Decode n_blocks block-scaled FP4 blocks with the same in-register decoder

@@ -24,12 +24,13 @@ LATENTMOE_ERR_HIP = -4
 LATENTMOE_EXPERTS_BF16 = 0
 LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 = 1
 
-INTER = dict(z=0, y_lat=1, counts=2, offsets=3, row_src=4, inv=5, h=6, hs_hi=7, hs_lo=8, y_lat_lo=9)
+INTER = dict(z=0, y_lat=1, counts=2, offsets=3, row_src=4, inv=5, h=6, hs_hi=7, hs_lo=8, y_lat_lo=9, z_lo=10, h_lo=11)
 STAGES = ["router", "topk", "bucket", "down_proj", "expert_up", "expert_down", "combine",
           "shared_up", "shared_down", "up_proj"]
 
 EXPORTED = [
-    "latentmoe_init", "latentmoe_forward", "latentmoe_destroy", "latentmoe_status_string",
+    "latentmoe_init", "latentmoe_forward", "latentmoe_forward_graph", "latentmoe_destroy",
+    "latentmoe_status_string",
     "latentmoe_workspace_bytes", "latentmoe_debug_copy", "latentmoe_profile_begin",
     "latentmoe_profile_end", "latentmoe_fp4_decode",
 ]
@@ -70,12 +71,13 @@ def load(path: str = LIB_PATH):
     lib.latentmoe_init.argtypes = [ctypes.POINTER(latentmoe_config), ctypes.POINTER(latentmoe_weights),
                                    vp, ctypes.POINTER(vp)]
     lib.latentmoe_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp]
+    lib.latentmoe_forward_graph.argtypes = [vp, vp, i32, vp, vp, vp, vp]
     lib.latentmoe_destroy.argtypes = [vp]
     lib.latentmoe_status_string.argtypes = [ctypes.c_int]
     lib.latentmoe_status_string.restype = ctypes.c_char_p
     lib.latentmoe_workspace_bytes.argtypes = [ctypes.POINTER(latentmoe_config), ctypes.POINTER(sz)]
     lib.latentmoe_debug_copy.argtypes = [vp, ctypes.c_int, vp, sz, vp]
-    lib.latentmoe_profile_begin.argtypes = [vp, ctypes.c_int]
+    lib.latentmoe_profile_begin.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
     lib.latentmoe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int)]
     lib.latentmoe_fp4_decode.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
@@ -117,6 +119,13 @@ def latentmoe_forward(h: int, x_ptr: int, T: int, y_ptr: int, idx_ptr: int, gate
         ctypes.c_void_p(idx_ptr or None), ctypes.c_void_p(gate_ptr or None), ctypes.c_void_p(stream)))
 
 
+def latentmoe_forward_graph(h: int, x_ptr: int, T: int, y_ptr: int, idx_ptr: int, gate_ptr: int,
+                            stream: int) -> None:
+    _check("latentmoe_forward_graph", load().latentmoe_forward_graph(
+        ctypes.c_void_p(h), ctypes.c_void_p(x_ptr), int(T), ctypes.c_void_p(y_ptr),
+        ctypes.c_void_p(idx_ptr or None), ctypes.c_void_p(gate_ptr or None), ctypes.c_void_p(stream)))
+
+
 def latentmoe_destroy(h: int) -> None:
     _check("latentmoe_destroy", load().latentmoe_destroy(ctypes.c_void_p(h)))
 
@@ -126,8 +135,9 @@ def latentmoe_debug_copy(h: int, which: int, dst_ptr: int, nbytes: int, stream: 
         ctypes.c_void_p(h), int(which), ctypes.c_void_p(dst_ptr), nbytes, ctypes.c_void_p(stream)))
 
 
-def latentmoe_profile_begin(h: int, max_calls: int) -> None:
-    _check("latentmoe_profile_begin", load().latentmoe_profile_begin(ctypes.c_void_p(h), int(max_calls)))
+def latentmoe_profile_begin(h: int, max_calls: int, stage_mask: int = (1 << 10) - 1) -> None:
+    _check("latentmoe_profile_begin", load().latentmoe_profile_begin(ctypes.c_void_p(h), int(max_calls),
+                                                                     int(stage_mask)))
 
 
 def latentmoe_profile_end(h: int) -> tuple[list, int]:
@@ -193,8 +203,9 @@ class LatentMoE:
         self.h = latentmoe_init(self.cfg, w, self.stream.cuda_stream)
         self.device = next(v for v in Wd.values() if v is not None).device
 
-    def forward(self, x, y=None, idx=None, gates=None):
-        """x: [T, d] int16 (bf16 bits) device tensor.  Returns (y fp32, idx int32, gates fp32)."""
+    def forward(self, x, y=None, idx=None, gates=None, graph=False):
+        """x: [T, d] int16 (bf16 bits) device tensor.  Returns (y fp32, idx int32, gates fp32).
+        graph=True replays a captured HIP graph (latentmoe_forward_graph)."""
         torch = _torch()
         T = x.shape[0]
         K = self.dims.top_k
@@ -204,8 +215,8 @@ class LatentMoE:
             idx = torch.empty((T, K), dtype=torch.int32, device=self.device)
         if gates is None:
             gates = torch.empty((T, K), dtype=torch.float32, device=self.device)
-        latentmoe_forward(self.h, x.data_ptr(), T, y.data_ptr(), _ptr(idx), _ptr(gates),
-                          self.stream.cuda_stream)
+        fn = latentmoe_forward_graph if graph else latentmoe_forward
+        fn(self.h, x.data_ptr(), T, y.data_ptr(), _ptr(idx), _ptr(gates), self.stream.cuda_stream)
         return y, idx, gates
 
     def intermediate(self, which: str, shape, dtype):
@@ -215,8 +226,9 @@ class LatentMoE:
                              self.stream.cuda_stream)
         return out
 
-    def profile_begin(self, max_calls: int):
-        latentmoe_profile_begin(self.h, max_calls)
+    def profile_begin(self, max_calls: int, stages=None):
+        mask = (1 << len(STAGES)) - 1 if stages is None else sum(1 << STAGES.index(s) for s in stages)
+        latentmoe_profile_begin(self.h, max_calls, mask)
 
     def profile_end(self):
         ms, calls = latentmoe_profile_end(self.h)

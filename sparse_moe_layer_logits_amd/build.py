@@ -29,23 +29,27 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    objs = [os.path.join(OUT_DIR, s.replace(".hip", ".o")) for s in SOURCES]
+def build(verbose: bool = False, out_dir: str = OUT_DIR, defines=()) -> str:
+    """Compile every source and link liblatentmoe.so into out_dir.  `defines`
+    are extra -D settings for the kernels' tunables."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liblatentmoe.so")
+    objs = [os.path.join(out_dir, s.replace(".hip", ".o")) for s in SOURCES]
+    extra = ["-D" + d for d in defines]
 
     def one(i):
-        return _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
+        return _run([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         for out in ex.map(one, range(len(SOURCES))):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     for o in objs:
         os.remove(o)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":

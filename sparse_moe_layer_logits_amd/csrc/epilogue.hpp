@@ -34,13 +34,25 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int expert, int s
       break;
     }
     case EPI_SQRELU_HILO: {
+      const float ts = p.b_tscale ? p.b_tscale[expert] : 1.0f;
       float hi[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float u = fmaxf(v[i], 0.0f);
+        float u = fmaxf(v[i] * ts, 0.0f);
         float s = u * u;
         hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(s));
         lo[i] = s - hi[i];
+      }
+      store_bf16x4(p.C, off, hi[0], hi[1], hi[2], hi[3]);
+      store_bf16x4(p.C2, off, lo[0], lo[1], lo[2], lo[3]);
+      break;
+    }
+    case EPI_BF16_HILO: {
+      float hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i]));
+        lo[i] = v[i] - hi[i];
       }
       store_bf16x4(p.C, off, hi[0], hi[1], hi[2], hi[3]);
       store_bf16x4(p.C2, off, lo[0], lo[1], lo[2], lo[3]);

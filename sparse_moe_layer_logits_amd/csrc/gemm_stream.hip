@@ -1,11 +1,11 @@
 // Weight-streaming MFMA GEMM for tiles of at most ROWS activation rows.
 //
 // In decode-like shapes every expert sees a few tokens, so the cost is reading
-// the weights once from HBM (the pages' point that low-latency MoE inference is
-// bound by expert weight reads; "Nemotron 3 Super", section 2 and section 3.2
-// principle 1).  Each wave streams 16*NT weight rows straight from HBM into
-// registers (double-buffered chunks of 256 k) and multiplies them with the
-// tile's activation rows, which the block stages once per chunk in LDS.
+// the weights once from HBM (low-latency MoE inference is bound by expert
+// weight reads: "Nemotron 3 Super", section 2 and section 3.2 principle 1).
+// Each wave streams 16*NT weight rows straight from HBM into registers
+// (double-buffered chunks) and multiplies them with the tile's activation rows,
+// which the block stages once per chunk in LDS.
 //
 // The weight tile is the MFMA "A" operand (rows = output columns n) and the
 // activations are the MFMA "B" operand (columns = token rows), so each lane
@@ -15,15 +15,15 @@
 // k = 16g .. 16g+15; MFMA step j (0, 1) uses k = 16g + 8j .. 16g + 8j + 7.  The
 // same map is used for both operands, so the products pair up correctly, and a
 // block-scaled FP4 lane group covers exactly one 16-element scale block.
+//
+// DUAL: the activation comes as two bf16 parts (hi + lo); each weight
+// fragment feeds two MFMAs, so the weights are still read once.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "fp4.hpp"
 #include "kernels.hpp"
 
 namespace lmoe {
-
-constexpr int ST_PAIRS = 4;              // 64-k blocks per chunk (chunk = 256 k)
-constexpr int ST_KC = 64 * ST_PAIRS;
 
 struct SegPtr {
   const uint16_t* A;
@@ -53,17 +53,21 @@ struct BFrag<false> {
 };
 template <>
 struct BFrag<true> {
-  u32x2_t codes;  // 16 E2M1 codes
-  uint32_t scale; // E4M3 byte
+  u32x2_t codes;   // 16 E2M1 codes
+  uint32_t scale;  // E4M3 byte
 };
 
-template <int W, int NT, int ROWS, bool FP4>
+template <int W, int NT, int ROWS, int PAIRS, bool FP4, bool DUAL>
 __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
   constexpr int MTMAX = ROWS / 16;
-  constexpr int PIECES = ROWS * 8 * ST_PAIRS;          // 16-byte A pieces per chunk
+  constexpr int NPART = DUAL ? 2 : 1;
+  constexpr int KC = 64 * PAIRS;                           // k per chunk
+  constexpr int ROWB = KC * 2;                             // LDS bytes per row and part
+  constexpr int PIECES = ROWS * 8 * PAIRS * NPART;         // 16-byte A pieces per chunk
   constexpr int THREADS = W * 64;
-  constexpr int APT = (PIECES + THREADS - 1) / THREADS;  // A pieces per thread
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][ROWS * ST_KC * 2];
+  constexpr int APT = (PIECES + THREADS - 1) / THREADS;    // A pieces per thread
+  constexpr int PPR = 8 * PAIRS;                           // pieces per row and part
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][NPART * ROWS * ROWB];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -96,19 +100,19 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
   const int kend = min(Ktot, kbeg + p.k_split);
   if (kbeg >= kend) return;
   const int npairs = (kend - kbeg) >> 6;
-  const int nchunks = (npairs + ST_PAIRS - 1) / ST_PAIRS;
+  const int nchunks = (npairs + PAIRS - 1) / PAIRS;
 
-  // ---- this thread's A pieces (fixed rows across chunks) ----
+  // ---- this thread's A pieces: (part, row, piece) fixed across chunks ----
   int a_row[APT];
-  int a_piece[APT];
+  int a_piece[APT];  // part * ROWS * PPR + row * PPR + piece, or -1
 #pragma unroll
   for (int u = 0; u < APT; ++u) {
     const int i = threadIdx.x + u * THREADS;
-    const int row = i / (8 * ST_PAIRS);
-    a_piece[u] = i % (8 * ST_PAIRS);
+    const int row = (i % (ROWS * PPR)) / PPR;
     int src = -1;
     if (i < PIECES && row < rows) src = p.row_index ? p.row_index[row0 + row] : row0 + row;
     a_row[u] = src;
+    a_piece[u] = i < PIECES ? i : -1;
   }
 
   // ---- this wave's weight rows ----
@@ -123,10 +127,10 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto load_b = [&](BFrag<FP4> (&bf)[ST_PAIRS][NT], int c) {
+  auto load_b = [&](BFrag<FP4> (&bf)[PAIRS][NT], int c) {
 #pragma unroll
-    for (int pr = 0; pr < ST_PAIRS; ++pr) {
-      const int pg = c * ST_PAIRS + pr;
+    for (int pr = 0; pr < PAIRS; ++pr) {
+      const int pg = c * PAIRS + pr;
       if (pg < npairs && wave_active) {
         const SegPtr sp = seg_at(p, kbeg + pg * 64);
 #pragma unroll
@@ -152,30 +156,33 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < APT; ++u) {
       a_regs[u] = zero128();
-      const int pr = a_piece[u] >> 3, pc = a_piece[u] & 7;
-      const int pg = c * ST_PAIRS + pr;
-      if (a_row[u] >= 0 && pg < npairs) {
+      if (a_piece[u] < 0 || a_row[u] < 0) continue;
+      const int part = a_piece[u] / (ROWS * PPR);
+      const int pc = a_piece[u] % PPR;
+      const int pg = c * PAIRS + (pc >> 3);
+      if (pg < npairs) {
         const SegPtr sp = seg_at(p, kbeg + pg * 64);
-        a_regs[u] = ld128(sp.A + (long long)a_row[u] * p.lda + sp.kl + pc * 8);
+        const uint16_t* base = (DUAL && part) ? reinterpret_cast<const uint16_t*>(p.a_lo) : sp.A;
+        a_regs[u] = ld128(base + (long long)a_row[u] * p.lda + sp.kl + (pc & 7) * 8);
       }
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < APT; ++u) {
-      const int i = threadIdx.x + u * THREADS;
-      if (i < PIECES) {
-        const int row = i / (8 * ST_PAIRS);
-        const int phys = a_piece[u] ^ (row & 15);
-        *reinterpret_cast<u32x4_t*>(&As[buf][row * (ST_KC * 2) + phys * 16]) = a_regs[u];
-      }
+      if (a_piece[u] < 0) continue;
+      const int part = a_piece[u] / (ROWS * PPR);
+      const int row = (a_piece[u] % (ROWS * PPR)) / PPR;
+      const int pc = a_piece[u] % PPR;
+      const int phys = pc ^ (row & 15);
+      *reinterpret_cast<u32x4_t*>(&As[buf][(part * ROWS + row) * ROWB + phys * 16]) = a_regs[u];
     }
   };
-  auto compute = [&](const BFrag<FP4> (&bf)[ST_PAIRS][NT], int buf, int c) {
+  auto compute = [&](const BFrag<FP4> (&bf)[PAIRS][NT], int buf, int c) {
     if (!wave_active) return;
 #pragma unroll
-    for (int pr = 0; pr < ST_PAIRS; ++pr) {
-      const int pg = c * ST_PAIRS + pr;
+    for (int pr = 0; pr < PAIRS; ++pr) {
+      const int pg = c * PAIRS + pr;
       if (pg < npairs) {
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
@@ -194,10 +201,13 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
             if (mt < MT) {
               const int row = mt * 16 + r16;
               const int phys = (pr * 8 + 2 * g + js) ^ (row & 15);
-              const u32x4_t av =
-                  *reinterpret_cast<const u32x4_t*>(&As[buf][row * (ST_KC * 2) + phys * 16]);
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma_16x16x32(bw[nt], av, acc[nt][mt]);
+              for (int part = 0; part < NPART; ++part) {
+                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
+                    &As[buf][(part * ROWS + row) * ROWB + phys * 16]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma_16x16x32(bw[nt], av, acc[nt][mt]);
+              }
             }
           }
         }
@@ -205,7 +215,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
     }
   };
 
-  BFrag<FP4> b0[ST_PAIRS][NT], b1[ST_PAIRS][NT];
+  BFrag<FP4> b0[PAIRS][NT], b1[PAIRS][NT];
   load_a(0);
   load_b(b0, 0);
   store_a(0);
@@ -243,24 +253,42 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
   }
 }
 
+#ifndef LMOE_ST_W
+#define LMOE_ST_W 8
+#endif
+#ifndef LMOE_ST_PAIRS16
+#define LMOE_ST_PAIRS16 4
+#endif
+
+template <int ROWS, int PAIRS, bool FP4, bool DUAL>
+static void launch_rows(const GemmParams& p, long long blocks, hipStream_t s) {
+  constexpr int W = LMOE_ST_W, NT = 1;
+  gemm_stream_kernel<W, NT, ROWS, PAIRS, FP4, DUAL><<<(unsigned)blocks, W * 64, 0, s>>>(p);
+}
+
+template <bool FP4, bool DUAL>
+static void launch_fmt(const GemmParams& p, bool small_rows, long long blocks, hipStream_t s) {
+  if (small_rows)
+    launch_rows<16, LMOE_ST_PAIRS16, FP4, DUAL>(p, blocks, s);
+  else
+    launch_rows<64, DUAL ? 2 : 4, FP4, DUAL>(p, blocks, s);
+}
+
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s) {
-  constexpr int W = 8, NT = 1;
+  constexpr int W = LMOE_ST_W, NT = 1;
   const bool small_rows = p.tile_expert && p.rows_per_tile <= 16;
   const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
   const int rows_per_tile = small_rows ? 16 : 64;
   const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows_per_tile - 1) / rows_per_tile;
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
+  const bool dual = p.a_lo != nullptr;
   if (fp4) {
-    if (small_rows)
-      gemm_stream_kernel<W, NT, 16, true><<<(unsigned)blocks, W * 64, 0, s>>>(p);
-    else
-      gemm_stream_kernel<W, NT, 64, true><<<(unsigned)blocks, W * 64, 0, s>>>(p);
+    if (dual) launch_fmt<true, true>(p, small_rows, blocks, s);
+    else launch_fmt<true, false>(p, small_rows, blocks, s);
   } else {
-    if (small_rows)
-      gemm_stream_kernel<W, NT, 16, false><<<(unsigned)blocks, W * 64, 0, s>>>(p);
-    else
-      gemm_stream_kernel<W, NT, 64, false><<<(unsigned)blocks, W * 64, 0, s>>>(p);
+    if (dual) launch_fmt<false, true>(p, small_rows, blocks, s);
+    else launch_fmt<false, false>(p, small_rows, blocks, s);
   }
 }
 

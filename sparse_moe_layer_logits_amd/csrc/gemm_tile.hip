@@ -9,6 +9,10 @@
 //
 // The k layout inside a 64-wide k block is the one the weight-streaming kernel
 // uses: lane group g holds k = 16g .. 16g+15, MFMA step j uses 16g + 8j .. +7.
+//
+// DUAL: the activation tile is staged as two bf16 parts (hi + lo) and every
+// weight fragment feeds both, so the product carries about 16 bits of the
+// activation at twice the MFMA work and the same weight traffic.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "kernels.hpp"
@@ -32,9 +36,15 @@ __device__ __forceinline__ void seg_at_tile(const GemmParams& p, int kg, const u
   kl = k;
 }
 
+template <bool DUAL>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t Ws[2][TL_BN * TL_ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t Xs[2][TL_BM * TL_ROWB];
+  constexpr int NPART = DUAL ? 2 : 1;
+  constexpr int WBYTES = TL_BN * TL_ROWB;
+  constexpr int XBYTES = TL_BM * TL_ROWB;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // [buf][weights | activation part 0 | activation part 1]
+  auto Wbuf = [&](int buf) { return smem + buf * (WBYTES + NPART * XBYTES); };
+  auto Xbuf = [&](int buf, int part) { return Wbuf(buf) + WBYTES + part * XBYTES; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,7 +92,8 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   }
   const int pc = tid & 7;
 
-  u32x4_t wr[4], xr[4];
+  const uint16_t* Alo = reinterpret_cast<const uint16_t*>(p.a_lo);
+  u32x4_t wr[4], xr[NPART][4];
   auto load = [&](int kt) {
     const uint16_t *A, *B;
     int kl;
@@ -90,7 +101,9 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       wr[u] = w_row[u] >= 0 ? ld128(B + bexp + (long long)w_row[u] * p.ldb + kl + pc * 8) : zero128();
-      xr[u] = x_src[u] >= 0 ? ld128(A + (long long)x_src[u] * p.lda + kl + pc * 8) : zero128();
+      xr[0][u] = x_src[u] >= 0 ? ld128(A + (long long)x_src[u] * p.lda + kl + pc * 8) : zero128();
+      if constexpr (DUAL)
+        xr[1][u] = x_src[u] >= 0 ? ld128(Alo + (long long)x_src[u] * p.lda + kl + pc * 8) : zero128();
     }
   };
   auto store = [&](int buf) {
@@ -98,8 +111,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
     for (int u = 0; u < 4; ++u) {
       const int row = (tid + u * 256) >> 3;
       const int off = row * TL_ROWB + ((pc ^ (row & 7)) << 4);
-      *reinterpret_cast<u32x4_t*>(&Ws[buf][off]) = wr[u];
-      *reinterpret_cast<u32x4_t*>(&Xs[buf][off]) = xr[u];
+      *reinterpret_cast<u32x4_t*>(Wbuf(buf) + off) = wr[u];
+#pragma unroll
+      for (int part = 0; part < NPART; ++part)
+        *reinterpret_cast<u32x4_t*>(Xbuf(buf, part) + off) = xr[part][u];
     }
   };
 
@@ -113,18 +128,25 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
       const int piece = 2 * g + js;
-      u32x4_t wf[4], xf[4];
+      u32x4_t wf[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int rw = wn * 64 + t * 16 + r16;
-        const int rx = wm * 64 + t * 16 + r16;
-        wf[t] = *reinterpret_cast<const u32x4_t*>(&Ws[buf][rw * TL_ROWB + ((piece ^ (rw & 7)) << 4)]);
-        xf[t] = *reinterpret_cast<const u32x4_t*>(&Xs[buf][rx * TL_ROWB + ((piece ^ (rx & 7)) << 4)]);
+        wf[t] = *reinterpret_cast<const u32x4_t*>(Wbuf(buf) + rw * TL_ROWB + ((piece ^ (rw & 7)) << 4));
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int part = 0; part < NPART; ++part) {
+        u32x4_t xf[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[b], acc[a][b]);
+        for (int t = 0; t < 4; ++t) {
+          const int rx = wm * 64 + t * 16 + r16;
+          xf[t] = *reinterpret_cast<const u32x4_t*>(Xbuf(buf, part) + rx * TL_ROWB + ((piece ^ (rx & 7)) << 4));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[b], acc[a][b]);
+      }
     }
   };
 
@@ -151,12 +173,28 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmParams p) {
   }
 }
 
+constexpr int tile_lds_bytes(bool dual) {
+  return 2 * (TL_BN * TL_ROWB + (dual ? 2 : 1) * TL_BM * TL_ROWB);
+}
+
+int gemm_tile_setup() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tile_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, tile_lds_bytes(true));
+  if (e != hipSuccess) return (int)e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tile_kernel<false>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, tile_lds_bytes(false));
+  return (int)e;
+}
+
 void launch_gemm_tile(const GemmParams& p, hipStream_t s) {
   const int NQ = (p.N + TL_BN - 1) / TL_BN;
   const long long tiles = p.tile_expert ? p.max_tiles : (p.M + TL_BM - 1) / TL_BM;
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
-  gemm_tile_kernel<<<(unsigned)blocks, 256, 0, s>>>(p);
+  if (p.a_lo)
+    gemm_tile_kernel<true><<<(unsigned)blocks, 256, tile_lds_bytes(true), s>>>(p);
+  else
+    gemm_tile_kernel<false><<<(unsigned)blocks, 256, tile_lds_bytes(false), s>>>(p);
 }
 
 }  // namespace lmoe

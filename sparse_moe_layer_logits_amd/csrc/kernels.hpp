@@ -10,11 +10,12 @@ enum Epi : int {
   EPI_PARTIAL = 0,      // partial[split][row][n] = acc                         (split-K)
   EPI_BF16 = 1,         // C bf16 = acc
   EPI_SQRELU_BF16 = 2,  // C bf16 = relu(acc * tscale[e])^2
-  EPI_SQRELU_HILO = 3,  // v = relu(acc)^2; C bf16 = hi(v), C2 bf16 = bf16(v - hi(v))
+  EPI_SQRELU_HILO = 3,  // v = relu(acc * tscale[e])^2; C bf16 = hi(v), C2 bf16 = bf16(v - hi(v))
   EPI_F32 = 4,          // C f32 = acc (+ bias[n])
   EPI_F32_ADD = 5,      // C f32 += acc
   EPI_GATE_F32 = 6,     // C f32 = acc * tscale[e] * row_scale[row]
   EPI_GATE_BF16 = 7,    // C bf16 = acc * tscale[e] * row_scale[row]
+  EPI_BF16_HILO = 8,    // C bf16 = hi(acc), C2 bf16 = bf16(acc - hi(acc))
 };
 
 struct GemmSeg {
@@ -23,10 +24,15 @@ struct GemmSeg {
   int K;          // multiple of 64
 };
 
+// With a_lo set ("dual" mode, one segment) the kernels compute
+// (A + A_lo) * B^T: every weight fragment is loaded once and multiplied with
+// both bf16 parts of the activation, which together carry about 16 bits.
+
 // C[row, n] = sum over segments of sum_k A_seg[row, k] * B_seg[n, k]
 struct GemmParams {
   GemmSeg seg[3];
   int nseg;
+  const void* a_lo;  // [rows, lda] bf16 remainder of seg[0].A, or null
   int lda, ldb;      // row strides in elements (ldb counts FP4 elements for packed B)
   int M, N;          // dense rows, output columns
   // grouped (expert) mode: work tiles built on the device
@@ -59,15 +65,17 @@ struct GemmParams {
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
 // LDS-tiled MFMA GEMM, 128 x 128 tiles (prefill-like shapes)
 void launch_gemm_tile(const GemmParams& p, hipStream_t s);
+// one-time kernel attributes (dynamic LDS above 64 KB); returns a HIP error code
+int gemm_tile_setup();
 // sum split-K partials and apply the epilogue
 void launch_reduce(const GemmParams& p, hipStream_t s);
 
 // router weight fp32 [N, d] -> three bf16 pieces whose sum is exact
 void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStream_t s);
 
-// per-token top-K + softmax; builds per-16-token expert masks
-void launch_topk(const float* partial, int splits, long long split_stride, const float* bias,
-                 int T, int N, int K, int* idx, float* gates, uint32_t* masks, hipStream_t s);
+// per-token top-K + softmax over logits [T, N] (+ bias); builds per-16-token expert masks
+void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
+                 float* gates, uint32_t* masks, hipStream_t s);
 // counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile)
 void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
                         int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,

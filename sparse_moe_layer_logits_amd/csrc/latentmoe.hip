@@ -9,6 +9,12 @@
 //   (y = S2 relu(S1 x)^2) -> y += W_up y_lat.
 // Everything is enqueued on the caller's stream; the forward allocates nothing
 // and never waits on the host.
+//
+// Precision: products run on bf16 MFMA with fp32 accumulation.  Activations
+// that feed a later product (z, the expert hidden h, the latent sum and the
+// shared hidden) leave their producer as a bf16 pair (hi, lo = v - hi), and the
+// consumer multiplies both parts with each weight fragment, so they carry about
+// 16 significant bits; the weights are read once.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,7 +31,7 @@ using namespace lmoe;
 namespace {
 
 constexpr int STREAM_ROWS_BIG = 64;
-constexpr int STREAM_ROWS_SMALL = 16;
+constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
 constexpr int TILE_ROWS = 128;
 constexpr int TARGET_BLOCKS = 512;
 
@@ -54,7 +60,10 @@ Plan plan_dense(int M, int N, int K) {
 
 struct Buffers {
   uint16_t* pieces = nullptr;
+  float* logits = nullptr;
   float* partial = nullptr;
+  float* partial2 = nullptr;  // split-K partials of the shared expert (side stream)
+  float* partial3 = nullptr;  // split-K partials of W_down (side stream 2)
   size_t partial_cap = 0;  // floats
   int* idx = nullptr;
   float* gates = nullptr;
@@ -71,7 +80,9 @@ struct Buffers {
   float* row_gate = nullptr;
   int* inv = nullptr;
   uint16_t* z = nullptr;
+  uint16_t* z_lo = nullptr;
   uint16_t* h = nullptr;
+  uint16_t* h_lo = nullptr;
   float* og = nullptr;
   uint16_t* y_lat = nullptr;
   uint16_t* y_lat_lo = nullptr;
@@ -115,9 +126,9 @@ size_t max_partial_floats(const latentmoe_config& c) {
   for (int T : Ts) {
     if (T < 1 || T > c.max_tokens) continue;
     struct G { int N, K; bool always; };
-    const G gs[] = {{c.n_experts, 3 * c.d, true}, {c.latent, c.d, false},
-                    {c.shared_hidden, c.d, false}, {c.d, 2 * c.shared_hidden, false},
-                    {c.d, 2 * c.latent, false}};
+    const G gs[] = {{c.n_experts, 3 * c.d, false}, {c.latent, c.d, false},
+                    {c.shared_hidden, c.d, false}, {c.d, c.shared_hidden, false},
+                    {c.d, c.latent, false}};
     for (const G& g : gs) {
       Plan p = plan_dense(T, g.N, g.K);
       if (p.splits > 1 || g.always) best = std::max(best, (size_t)p.splits * T * g.N);
@@ -134,7 +145,10 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   b.partial_cap = max_partial_floats(c);
   b.max_tiles_cap = (int)(ceil_div(TK, STREAM_ROWS_SMALL) + std::min(N, TK));
   L.add((void**)&b.pieces, 3 * N * c.d * 2);
+  L.add((void**)&b.logits, Tm * N * 4);
   L.add((void**)&b.partial, b.partial_cap * 4);
+  L.add((void**)&b.partial2, b.partial_cap * 4);
+  L.add((void**)&b.partial3, b.partial_cap * 4);
   L.add((void**)&b.idx, TK * 4);
   L.add((void**)&b.gates, TK * 4);
   L.add((void**)&b.masks, nblk * N * 4);
@@ -149,7 +163,9 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.row_gate, TK * 4);
   L.add((void**)&b.inv, TK * 4);
   L.add((void**)&b.z, Tm * c.latent * 2);
+  L.add((void**)&b.z_lo, Tm * c.latent * 2);
   L.add((void**)&b.h, TK * c.expert_hidden * 2);
+  L.add((void**)&b.h_lo, TK * c.expert_hidden * 2);
   L.add((void**)&b.og, TK * c.latent * 4);
   L.add((void**)&b.y_lat, Tm * c.latent * 2);
   L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
@@ -160,6 +176,17 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
 
 }  // namespace
 
+struct GraphKey {
+  const void* x;
+  int T;
+  const void* y;
+  const void* idx;
+  const void* gate;
+  bool operator==(const GraphKey& o) const {
+    return x == o.x && T == o.T && y == o.y && idx == o.idx && gate == o.gate;
+  }
+};
+
 struct latentmoe_handle_s {
   latentmoe_config cfg;
   latentmoe_weights w;
@@ -167,6 +194,16 @@ struct latentmoe_handle_s {
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
   int last_T = 0;
+  // the shared expert runs on a side stream forked from the caller's stream
+  hipStream_t side = nullptr;
+  hipStream_t side2 = nullptr;  // W_down, concurrent with routing
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_join2 = nullptr;
+  // graph replay of the whole forward (latentmoe_forward_graph)
+  hipStream_t cap = nullptr;  // capture stream
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  GraphKey gkey{};
+  uint32_t prof_mask = 0;
   // stage timing
   std::vector<hipEvent_t> events;
   int prof_max = 0;
@@ -176,17 +213,20 @@ struct latentmoe_handle_s {
 
 namespace {
 
+void drop_graph(latentmoe_handle_s* h);
+
 struct StageTimer {
   latentmoe_handle_s* h;
   hipStream_t s;
   bool on;
   StageTimer(latentmoe_handle_s* h_, hipStream_t s_)
       : h(h_), s(s_), on(h_->profiling && h_->prof_calls < h_->prof_max) {}
-  void start(int stage) {
-    if (on) hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2], s);
+  bool want(int stage) const { return on && ((h->prof_mask >> stage) & 1u); }
+  void start(int stage, hipStream_t st = nullptr) {
+    if (want(stage)) (void)hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2], st ? st : s);
   }
-  void stop(int stage) {
-    if (on) hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2 + 1], s);
+  void stop(int stage, hipStream_t st = nullptr) {
+    if (want(stage)) (void)hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2 + 1], st ? st : s);
   }
   void done() {
     if (on) h->prof_calls++;
@@ -202,7 +242,8 @@ GemmParams base_params() {
 
 // dense GEMM C[T, N] = sum_seg A_seg[T, K_seg] B_seg[N, K_seg]^T with a final epilogue;
 // returns the number of k splits (with force_partial the caller reduces them)
-int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool force_partial) {
+int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool force_partial,
+              float* partial = nullptr) {
   int Ktot = 0;
   for (int i = 0; i < p.nseg; ++i) Ktot += p.seg[i].K;
   Plan pl = plan_dense(T, p.N, Ktot);
@@ -218,7 +259,7 @@ int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool fo
   const bool use_partial = force_partial || pl.splits > 1;
   if (use_partial) {
     p.epi = EPI_PARTIAL;
-    p.partial = h->b.partial;
+    p.partial = partial ? partial : h->b.partial;
     p.partial_stride = (long long)T * p.N;
   }
   if (pl.stream)
@@ -282,15 +323,30 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_OUT_OF_MEMORY;
   }
   h->workspace_bytes = L.total;
+  if (gemm_tile_setup() != 0) {
+    (void)hipGetLastError();
+    hipFree(h->workspace);
+    delete h;
+    return LATENTMOE_ERR_HIP;
+  }
   char* base = static_cast<char*>(h->workspace);
   for (auto& it : L.items) {
     *it.first = base;
     base += (it.second + 255) & ~size_t(255);
   }
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->side2, hipStreamNonBlocking) != hipSuccess ||
+      hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join2, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    latentmoe_destroy(h);
+    return LATENTMOE_ERR_HIP;
+  }
   launch_router_split(w->router_w, h->b.pieces, (long long)cfg->n_experts * cfg->d, stream);
   if (hipGetLastError() != hipSuccess) {
-    hipFree(h->workspace);
-    delete h;
+    latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
   }
   *out = h;
@@ -299,18 +355,26 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
 
 int latentmoe_destroy(latentmoe_handle_t h) {
   if (!h) return LATENTMOE_OK;
-  for (hipEvent_t e : h->events) hipEventDestroy(e);
-  hipError_t e = hipFree(h->workspace);
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_join2) (void)hipEventDestroy(h->ev_join2);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->side2) (void)hipStreamDestroy(h->side2);
+  drop_graph(h);
+  if (h->cap) (void)hipStreamDestroy(h->cap);
+  hipError_t e = h->workspace ? hipFree(h->workspace) : hipSuccess;
   delete h;
   return e == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }
 
-int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
-                      int32_t* topk_idx, float* topk_gate, hipStream_t s) {
-  if (!h || T < 0) return LATENTMOE_ERR_INVALID_ARG;
-  if (T == 0) return LATENTMOE_OK;
-  if (!x || !y || T > h->cfg.max_tokens) return LATENTMOE_ERR_INVALID_ARG;
-  (void)hipGetLastError();
+}  // extern "C"
+
+namespace {
+
+// enqueue one forward on stream s (eager, or into a stream capture)
+void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
+                  float* topk_gate, hipStream_t s, bool timing) {
 
   const latentmoe_config& c = h->cfg;
   const latentmoe_weights& w = h->w;
@@ -320,6 +384,61 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   const bool fp4 = c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16;
   const long long TK = (long long)T * K;
   StageTimer tm(h, s);
+  if (!timing) tm.on = false;
+
+  // The shared expert does not depend on routing: fork it onto the side
+  // stream (same priority) and join before the up-projection adds onto y.
+  hipStream_t side = h->side;
+  (void)hipEventRecord(h->ev_fork, s);
+  (void)hipStreamWaitEvent(side, h->ev_fork, 0);
+  // ---- shared expert (side stream): h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
+  tm.start(LATENTMOE_STAGE_SHARED_UP, side);
+  GemmParams ps = base_params();
+  ps.seg[0] = GemmSeg{x, w.shared_w1, d};
+  ps.nseg = 1;
+  ps.lda = d;
+  ps.ldb = d;
+  ps.N = ms;
+  ps.epi = EPI_SQRELU_HILO;
+  ps.C = b.hs_hi;
+  ps.C2 = b.hs_lo;
+  ps.ldc = ms;
+  run_dense(h, ps, T, side, false, b.partial2);
+  tm.stop(LATENTMOE_STAGE_SHARED_UP, side);
+
+  tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
+  GemmParams p2 = base_params();
+  p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
+  p2.a_lo = b.hs_lo;
+  p2.nseg = 1;
+  p2.lda = ms;
+  p2.ldb = ms;
+  p2.N = d;
+  p2.epi = EPI_F32;
+  p2.C = y;
+  p2.ldc = d;
+  run_dense(h, p2, T, side, false, b.partial2);
+  tm.stop(LATENTMOE_STAGE_SHARED_DOWN, side);
+
+  (void)hipEventRecord(h->ev_join, side);
+
+  // ---- z = W_down x (side stream 2, concurrent with routing) ----
+  hipStream_t side2 = h->side2;
+  (void)hipStreamWaitEvent(side2, h->ev_fork, 0);
+  tm.start(LATENTMOE_STAGE_DOWN_PROJ, side2);
+  GemmParams pd = base_params();
+  pd.seg[0] = GemmSeg{x, w.w_down, d};
+  pd.nseg = 1;
+  pd.lda = d;
+  pd.ldb = d;
+  pd.N = L;
+  pd.epi = EPI_BF16_HILO;
+  pd.C = b.z;
+  pd.C2 = b.z_lo;
+  pd.ldc = L;
+  run_dense(h, pd, T, side2, false, b.partial3);
+  tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
+  (void)hipEventRecord(h->ev_join2, side2);
 
   // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
   tm.start(LATENTMOE_STAGE_ROUTER);
@@ -330,13 +449,16 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   pr.ldb = d;
   pr.N = N;
   pr.ldc = N;
-  const int router_splits = run_dense(h, pr, T, s, /*force_partial=*/true);
+  pr.epi = EPI_F32;
+  pr.C = b.logits;
+  run_dense(h, pr, T, s, false);
   tm.stop(LATENTMOE_STAGE_ROUTER);
 
   // ---- 2. top-K + softmax (sums the router's split partials, adds the bias) ----
   tm.start(LATENTMOE_STAGE_TOPK);
-  launch_topk(b.partial, router_splits, (long long)T * N, w.router_bias, T, N, K, b.idx, b.gates,
-              b.masks, s);
+  int* idx_buf = topk_idx ? topk_idx : b.idx;  // written in place when the caller asks
+  float* gate_buf = topk_gate ? topk_gate : b.gates;
+  launch_topk(b.logits, w.router_bias, T, N, K, idx_buf, gate_buf, b.masks, s);
   tm.stop(LATENTMOE_STAGE_TOPK);
 
   // ---- 3. bucketing ----
@@ -348,23 +470,12 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   tm.start(LATENTMOE_STAGE_BUCKET);
   launch_bucket_scan(b.masks, T, N, rows_per_tile, b.counts, b.offsets, b.block_prefix,
                      b.tile_expert, b.tile_row0, b.tile_rows, b.n_tiles, max_tiles, s);
-  launch_place(b.idx, b.gates, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src, b.row_gate,
+  launch_place(idx_buf, gate_buf, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src, b.row_gate,
                b.inv, s);
   tm.stop(LATENTMOE_STAGE_BUCKET);
 
-  // ---- 4. z = W_down x ----
-  tm.start(LATENTMOE_STAGE_DOWN_PROJ);
-  GemmParams pd = base_params();
-  pd.seg[0] = GemmSeg{x, w.w_down, d};
-  pd.nseg = 1;
-  pd.lda = d;
-  pd.ldb = d;
-  pd.N = L;
-  pd.epi = EPI_BF16;
-  pd.C = b.z;
-  pd.ldc = L;
-  run_dense(h, pd, T, s, false);
-  tm.stop(LATENTMOE_STAGE_DOWN_PROJ);
+  // ---- 4. wait for z = W_down x (side stream 2) ----
+  (void)hipStreamWaitEvent(s, h->ev_join2, 0);
 
   // ---- 5/6. grouped expert GEMMs ----
   GemmParams pe = base_params();
@@ -381,6 +492,7 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   tm.start(LATENTMOE_STAGE_EXPERT_UP);
   GemmParams pu = pe;
   pu.seg[0] = GemmSeg{b.z, w.expert_w1, L};
+  pu.a_lo = b.z_lo;
   pu.lda = L;
   pu.ldb = L;
   pu.N = m;
@@ -389,8 +501,9 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   pu.b_stride = (long long)m * L;
   pu.b_scale = fp4 ? w.expert_w1_scale : nullptr;
   pu.b_tscale = fp4 ? w.expert_w1_tscale : nullptr;
-  pu.epi = EPI_SQRELU_BF16;
+  pu.epi = EPI_SQRELU_HILO;
   pu.C = b.h;
+  pu.C2 = b.h_lo;
   pu.ldc = m;
   if (expert_stream)
     launch_gemm_stream(pu, fp4, s);
@@ -401,6 +514,7 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
   GemmParams pw = pe;
   pw.seg[0] = GemmSeg{b.h, w.expert_w2, m};
+  pw.a_lo = b.h_lo;
   pw.lda = m;
   pw.ldb = m;
   pw.N = L;
@@ -424,41 +538,13 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   launch_combine(b.og, b.inv, T, K, L, b.y_lat, b.y_lat_lo, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
-  // ---- 8. shared expert: h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
-  tm.start(LATENTMOE_STAGE_SHARED_UP);
-  GemmParams ps = base_params();
-  ps.seg[0] = GemmSeg{x, w.shared_w1, d};
-  ps.nseg = 1;
-  ps.lda = d;
-  ps.ldb = d;
-  ps.N = ms;
-  ps.epi = EPI_SQRELU_HILO;
-  ps.C = b.hs_hi;
-  ps.C2 = b.hs_lo;
-  ps.ldc = ms;
-  run_dense(h, ps, T, s, false);
-  tm.stop(LATENTMOE_STAGE_SHARED_UP);
-
-  tm.start(LATENTMOE_STAGE_SHARED_DOWN);
-  GemmParams p2 = base_params();
-  p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
-  p2.seg[1] = GemmSeg{b.hs_lo, w.shared_w2, ms};
-  p2.nseg = 2;
-  p2.lda = ms;
-  p2.ldb = ms;
-  p2.N = d;
-  p2.epi = EPI_F32;
-  p2.C = y;
-  p2.ldc = d;
-  run_dense(h, p2, T, s, false);
-  tm.stop(LATENTMOE_STAGE_SHARED_DOWN);
-
-  // ---- 9. y += W_up y_lat ----
+  // ---- 8. y += W_up y_lat (after the shared expert wrote y) ----
+  (void)hipStreamWaitEvent(s, h->ev_join, 0);
   tm.start(LATENTMOE_STAGE_UP_PROJ);
   GemmParams pp = base_params();
   pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
-  pp.seg[1] = GemmSeg{b.y_lat_lo, w.w_up, L};
-  pp.nseg = 2;
+  pp.a_lo = b.y_lat_lo;
+  pp.nseg = 1;
   pp.lda = L;
   pp.ldb = L;
   pp.N = d;
@@ -468,9 +554,61 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   run_dense(h, pp, T, s, false);
   tm.stop(LATENTMOE_STAGE_UP_PROJ);
   tm.done();
+  h->last_T = T;
+}
 
-  if (topk_idx) hipMemcpyAsync(topk_idx, b.idx, TK * 4, hipMemcpyDeviceToDevice, s);
-  if (topk_gate) hipMemcpyAsync(topk_gate, b.gates, TK * 4, hipMemcpyDeviceToDevice, s);
+int check_forward_args(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y) {
+  if (!h || T < 0) return LATENTMOE_ERR_INVALID_ARG;
+  if (T == 0) return LATENTMOE_OK;
+  if (!x || !y || T > h->cfg.max_tokens) return LATENTMOE_ERR_INVALID_ARG;
+  return 1;  // proceed
+}
+
+void drop_graph(latentmoe_handle_s* h) {
+  if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  h->gexec = nullptr;
+  h->graph = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
+                      int32_t* topk_idx, float* topk_gate, hipStream_t s) {
+  const int st = check_forward_args(h, x, T, y);
+  if (st != 1) return st;
+  (void)hipGetLastError();
+  forward_impl(h, x, T, y, topk_idx, topk_gate, s, true);
+  return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}
+
+int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
+                            int32_t* topk_idx, float* topk_gate, hipStream_t s) {
+  const int st = check_forward_args(h, x, T, y);
+  if (st != 1) return st;
+  (void)hipGetLastError();
+  const GraphKey key{x, T, y, topk_idx, topk_gate};
+  if (!h->gexec || !(key == h->gkey)) {
+    drop_graph(h);
+    if (hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal) != hipSuccess)
+      return LATENTMOE_ERR_HIP;
+    forward_impl(h, x, T, y, topk_idx, topk_gate, h->cap, false);
+    hipGraph_t g = nullptr;
+    if (hipStreamEndCapture(h->cap, &g) != hipSuccess || !g) {
+      (void)hipGetLastError();
+      return LATENTMOE_ERR_HIP;
+    }
+    h->graph = g;
+    if (hipGraphInstantiate(&h->gexec, g, nullptr, nullptr, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      drop_graph(h);
+      return LATENTMOE_ERR_HIP;
+    }
+    h->gkey = key;
+  }
+  if (hipGraphLaunch(h->gexec, s) != hipSuccess) return LATENTMOE_ERR_HIP;
   h->last_T = T;
   return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }
@@ -493,6 +631,8 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
     case LATENTMOE_INTER_HS_HI: src = h->b.hs_hi; have = T * c.shared_hidden * 2; break;
     case LATENTMOE_INTER_HS_LO: src = h->b.hs_lo; have = T * c.shared_hidden * 2; break;
     case LATENTMOE_INTER_Y_LAT_LO: src = h->b.y_lat_lo; have = T * c.latent * 2; break;
+    case LATENTMOE_INTER_Z_LO: src = h->b.z_lo; have = T * c.latent * 2; break;
+    case LATENTMOE_INTER_H_LO: src = h->b.h_lo; have = T * K * c.expert_hidden * 2; break;
     default: return LATENTMOE_ERR_INVALID_ARG;
   }
   if (bytes > have) return LATENTMOE_ERR_INVALID_ARG;
@@ -502,9 +642,10 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
              : LATENTMOE_ERR_HIP;
 }
 
-int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls) {
+int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls, uint32_t stage_mask) {
   if (!h || max_calls < 1) return LATENTMOE_ERR_INVALID_ARG;
-  for (hipEvent_t e : h->events) hipEventDestroy(e);
+  h->prof_mask = stage_mask;
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
   h->events.assign((size_t)max_calls * LATENTMOE_NUM_STAGES * 2, nullptr);
   for (auto& e : h->events)
     if (hipEventCreate(&e) != hipSuccess) return LATENTMOE_ERR_HIP;
@@ -520,6 +661,7 @@ int latentmoe_profile_end(latentmoe_handle_t h, float* stage_ms, int n_stages, i
   std::vector<double> sum(LATENTMOE_NUM_STAGES, 0.0);
   for (int c = 0; c < h->prof_calls; ++c) {
     for (int st = 0; st < LATENTMOE_NUM_STAGES; ++st) {
+      if (!((h->prof_mask >> st) & 1u)) continue;
       hipEvent_t a = h->events[((size_t)c * LATENTMOE_NUM_STAGES + st) * 2];
       hipEvent_t z = h->events[((size_t)c * LATENTMOE_NUM_STAGES + st) * 2 + 1];
       if (hipEventSynchronize(z) != hipSuccess) return LATENTMOE_ERR_HIP;

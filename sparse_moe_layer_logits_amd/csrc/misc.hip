@@ -13,9 +13,18 @@ __global__ void reduce_kernel(GemmParams p) {
   if (i >= groups) return;
   const int row = (int)(i / (p.N / 4));
   const int n = (int)(i % (p.N / 4)) * 4;
+  const float* src = p.partial + (long long)row * p.N + n;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.splits; ++s)
-    v += *reinterpret_cast<const f32x4_t*>(p.partial + s * p.partial_stride + (long long)row * p.N + n);
+  int s = 0;
+  // eight independent loads in flight per thread; the sum order is fixed
+  for (; s + 8 <= p.splits; s += 8) {
+    f32x4_t t[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = *reinterpret_cast<const f32x4_t*>(src + (s + i) * p.partial_stride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += t[i];
+  }
+  for (; s < p.splits; ++s) v += *reinterpret_cast<const f32x4_t*>(src + s * p.partial_stride);
   epilogue4(p, 0, 0, row, n, v);
 }
 
@@ -31,31 +40,41 @@ void launch_reduce(const GemmParams& p, hipStream_t s) {
 // their gate; the sum runs k = 0 .. K-1, so the result does not depend on
 // scheduling.  The fp32 sum leaves as a bf16 pair (hi, lo = sum - hi) so the
 // up-projection sees it to about 16 significant bits.
-__global__ void combine_kernel(const float* __restrict__ og, const int* __restrict__ inv, int K,
-                               int L, uint16_t* __restrict__ y_lat, uint16_t* __restrict__ y_lat_lo) {
+__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ og,
+                                                     const int* __restrict__ inv, int K, int L,
+                                                     uint16_t* __restrict__ y_lat,
+                                                     uint16_t* __restrict__ y_lat_lo) {
+  __shared__ int pos[64];
   const int t = blockIdx.x;
-  for (int c = threadIdx.x * 4; c < L; c += blockDim.x * 4) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const int pos = inv[(long long)t * K + k];
-      acc += *reinterpret_cast<const f32x4_t*>(og + (long long)pos * L + c);
-    }
-    float hi[4], lo[4];
+  if (threadIdx.x < K) pos[threadIdx.x] = inv[(long long)t * K + threadIdx.x];
+  __syncthreads();
+  const int c = (blockIdx.y * 64 + threadIdx.x) * 4;
+  if (c >= L) return;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= K; k += 8) {  // eight loads in flight, summed in k order
+    f32x4_t v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
-      lo[i] = acc[i] - hi[i];
-    }
-    store_bf16x4(y_lat, (long long)t * L + c, hi[0], hi[1], hi[2], hi[3]);
-    store_bf16x4(y_lat_lo, (long long)t * L + c, lo[0], lo[1], lo[2], lo[3]);
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4_t*>(og + (long long)pos[k + i] * L + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += v[i];
   }
+  for (; k < K; ++k) acc += *reinterpret_cast<const f32x4_t*>(og + (long long)pos[k] * L + c);
+  float hi[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
+    lo[i] = acc[i] - hi[i];
+  }
+  store_bf16x4(y_lat, (long long)t * L + c, hi[0], hi[1], hi[2], hi[3]);
+  store_bf16x4(y_lat_lo, (long long)t * L + c, lo[0], lo[1], lo[2], lo[3]);
 }
 
 void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
                     uint16_t* y_lat_lo, hipStream_t s) {
   if (T <= 0) return;
-  const int threads = min(256, max(64, L / 4));
-  combine_kernel<<<T, threads, 0, s>>>(og, inv, K, L, y_lat, y_lat_lo);
+  dim3 grid(T, (L / 4 + 63) / 64);
+  combine_kernel<<<grid, 64, 0, s>>>(og, inv, K, L, y_lat, y_lat_lo);
 }
 
 // decode n_blocks16 FP4 blocks (8 code bytes + 1 scale byte each) to bf16

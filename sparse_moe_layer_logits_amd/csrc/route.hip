@@ -35,9 +35,11 @@ void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStrea
 }
 
 // ---------------------------------------------------------------------------
-// top-K: one wavefront per token.  Logit e lives in lane e % 64, slot e / 64.
-// Keys (orderable float bits << 32 | ~index) make "larger logit, then lower
-// index" a plain unsigned maximum.
+// top-K: one wavefront per token.  Logit e lives in lane e % 64, slot e / 64,
+// as an order-preserving unsigned key.  The K-th largest key tau is found by a
+// 32-step bisection whose counts are wave ballots; the experts above tau and
+// the lowest-index experts equal to tau (ties go to the lower index) form the
+// selection, which is then ranked by (-logit, index) for the output order.
 // ---------------------------------------------------------------------------
 constexpr int TOPK_TOKENS_PER_BLOCK = 16;  // one wave each; masks are 16 bits wide
 
@@ -48,16 +50,9 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 __device__ __forceinline__ float from_orderable(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// number of set bits of m in lanes below this one
+__device__ __forceinline__ int bits_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -67,13 +62,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <int SLOTS>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ partial, int splits,
-                                                    long long split_stride,
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int N,
                                                     int K, int* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     uint32_t* __restrict__ masks) {
   __shared__ uint32_t smask[1024];
+  __shared__ unsigned long long cand[TOPK_TOKENS_PER_BLOCK][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * TOPK_TOKENS_PER_BLOCK + w;
@@ -81,76 +76,74 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ pa
   __syncthreads();
 
   if (t < T) {
-    // this lane's logits: experts lane, lane + 64, ...
-    uint32_t okey[SLOTS];  // orderable logit bits; 0 marks an empty or removed slot
+    uint32_t ok[SLOTS];  // orderable logit; 0 marks an empty slot
 #pragma unroll
     for (int j = 0; j < SLOTS; ++j) {
       const int e = j * 64 + lane;
-      okey[j] = 0u;
-      if (e < N) {
-        const float* pp = partial + (long long)t * N + e;
-        float v = 0.0f;
-#pragma unroll 1
-        for (int s = 0; s < splits; ++s) v += pp[s * split_stride];
-        if (bias) v += bias[e];
-        okey[j] = orderable(v);
-      }
+      ok[j] = 0u;
+      if (e < N) ok[j] = orderable(logits[(long long)t * N + e] + (bias ? bias[e] : 0.0f));
     }
-    // lane-local best: largest value, then lowest slot (= lowest expert index)
-    auto local_best = [&]() -> unsigned long long {
-      uint32_t bv = 0u;
-      int bj = 0;
+    // tau = the largest key with at least K keys >= it (the K-th largest key)
+    uint32_t tau = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = tau | (1u << bit);
+      int cnt = 0;
 #pragma unroll
-      for (int j = 0; j < SLOTS; ++j) {
-        if (okey[j] > bv) {
-          bv = okey[j];
-          bj = j;
-        }
-      }
-      return bv ? (((unsigned long long)bv << 32) | (uint32_t)(~(uint32_t)(bj * 64 + lane))) : 0ull;
-    };
-    unsigned long long best = local_best();
-
-    float my_val = 0.0f;
-    int my_idx = 0;
-    for (int k = 0; k < K; ++k) {
-      const unsigned long long win = wave_max_u64(best);
-      const int e = (int)(~(uint32_t)win);
-      if (lane == k) {
-        my_idx = e;
-        my_val = from_orderable((uint32_t)(win >> 32));
-      }
-      if ((e & 63) == lane) {  // the owner removes the winner
-        const int jw = e >> 6;
-#pragma unroll
-        for (int j = 0; j < SLOTS; ++j)
-          if (j == jw) okey[j] = 0u;
-        best = local_best();
-      }
+      for (int j = 0; j < SLOTS; ++j) cnt += __popcll(__ballot(ok[j] >= c));
+      if (cnt >= K) tau = c;
     }
-    // softmax over the K selected logits; the first selected one is the maximum
-    const float vmax = __shfl(my_val, 0, 64);
-    const float ex = lane < K ? expf(my_val - vmax) : 0.0f;
+    int n_gt = 0;
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) n_gt += __popcll(__ballot(ok[j] > tau));
+    // selection in index order (slot-major, then lane): keys above tau, then
+    // the first K - n_gt keys equal to tau
+    const int need = K - n_gt;
+    int eq_before = 0, base = 0;
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) {
+      const unsigned long long eqm = __ballot(ok[j] == tau);
+      const bool take = ok[j] > tau || (ok[j] == tau && eq_before + bits_below(eqm) < need);
+      eq_before += __popcll(eqm);
+      const unsigned long long sm = __ballot(take);
+      if (take)
+        cand[w][base + bits_below(sm)] =
+            ((unsigned long long)ok[j] << 32) | (uint32_t)(~(uint32_t)(j * 64 + lane));
+      base += __popcll(sm);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // rank of each selected key: keys are unique (index in the low half)
+    unsigned long long mine = 0ull, top = 0ull;
+    int rank = 0;
+    if (lane < K) mine = cand[w][lane];
+    for (int c = 0; c < K; ++c) {
+      const unsigned long long o = cand[w][c];
+      rank += o > mine;
+      top = o > top ? o : top;
+    }
+    const float v = from_orderable((uint32_t)(mine >> 32));
+    const float vmax = from_orderable((uint32_t)(top >> 32));
+    const float ex = lane < K ? expf(v - vmax) : 0.0f;
     const float tot = wave_sum(ex);
     if (lane < K) {
-      idx_out[(long long)t * K + lane] = my_idx;
-      gate_out[(long long)t * K + lane] = ex / tot;
-      atomicOr(&smask[my_idx], 1u << w);
+      const int e = (int)(~(uint32_t)mine);
+      idx_out[(long long)t * K + rank] = e;
+      gate_out[(long long)t * K + rank] = ex / tot;
+      atomicOr(&smask[e], 1u << w);
     }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < N; e += blockDim.x) masks[(long long)blockIdx.x * N + e] = smask[e];
 }
 
-void launch_topk(const float* partial, int splits, long long split_stride, const float* bias,
-                 int T, int N, int K, int* idx, float* gates, uint32_t* masks, hipStream_t s) {
+void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
+                 float* gates, uint32_t* masks, hipStream_t s) {
   const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
   if (N <= 512)
-    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(partial, splits, split_stride,
-                                                                  bias, T, N, K, idx, gates, masks);
+    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates, masks);
   else
-    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(partial, splits, split_stride,
-                                                                   bias, T, N, K, idx, gates, masks);
+    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates, masks);
 }
 
 // ---------------------------------------------------------------------------

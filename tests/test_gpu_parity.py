@@ -165,3 +165,36 @@ def test_super_prefill_full():
 
 def test_ultra_full():
     sampled_check("ultra", 8, 1e-2)
+
+
+def test_graph_replay_matches_eager_and_oracle():
+    """latentmoe_forward_graph: replays see new buffer contents, equal the eager
+    forward bit for bit, and a new T re-captures."""
+    import torch
+    wl = small_wl(T=40, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=128, shared_hidden=256)
+    xa, W = gen(wl, 11)
+    xb, _ = gen(wl, 12)
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(xa)
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.T, wl.top_k), dtype=torch.int32, device="cuda")
+    g = torch.empty((wl.T, wl.top_k), dtype=torch.float32, device="cuda")
+    for rep, xs in enumerate([xa, xb, xa, xb, xa]):
+        xd.copy_(binding.to_device(xs))
+        layer.forward(xd, y, idx, g, graph=True)
+        torch.cuda.synchronize()
+        yg, ig, gg = y.clone(), idx.clone(), g.clone()
+        ye, ie, ge = layer.forward(xd)                 # eager, fresh outputs
+        torch.cuda.synchronize()
+        assert torch.equal(yg, ye) and torch.equal(ig, ie) and torch.equal(gg, ge), rep
+        ref = oracle.forward(xs, W, wl.top_k)
+        rms = np.sqrt(np.mean(ref["y"] ** 2))
+        assert np.max(np.abs(yg.cpu().numpy() - ref["y"])) <= 1e-2 * rms
+    # a smaller T (new arguments) re-captures; then the original again
+    for T in (17, 40):
+        y2, i2, g2 = layer.forward(xd[:T], graph=True)
+        torch.cuda.synchronize()
+        ref = oracle.forward(xa[:T], W, wl.top_k)
+        assert np.max(np.abs(y2.cpu().numpy() - ref["y"])) <= 1e-2 * np.sqrt(np.mean(ref["y"] ** 2))
+    layer.close()
