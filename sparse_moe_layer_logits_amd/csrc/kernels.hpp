@@ -67,6 +67,10 @@ void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
 void launch_gemm_tile(const GemmParams& p, hipStream_t s);
 // one-time kernel attributes (dynamic LDS above 64 KB); returns a HIP error code
 int gemm_tile_setup();
+// large-tile MFMA GEMM, 256 x 256 tiles (prefill-sized problems)
+void launch_gemm_big(const GemmParams& p, hipStream_t s);
+bool gemm_big_supports(int epi);
+int gemm_big_setup();
 // sum split-K partials and apply the epilogue
 void launch_reduce(const GemmParams& p, hipStream_t s);
 

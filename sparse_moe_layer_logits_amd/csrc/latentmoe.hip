@@ -32,8 +32,9 @@ namespace {
 
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
-constexpr int TILE_ROWS = 128;
-constexpr int TARGET_BLOCKS = 512;
+constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
+constexpr int TARGET_BLOCKS = 512;      // streaming kernel: 8-wave blocks, several per CU
+constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 4-wave block per CU
 
 struct Plan {
   bool stream;  // weight-streaming kernel (true) or LDS-tiled kernel
@@ -48,9 +49,9 @@ Plan plan_dense(int M, int N, int K) {
   Plan p;
   p.stream = M <= STREAM_ROWS_BIG;
   const int per_split = p.stream ? ceil_div(N, 128) * ceil_div(M, STREAM_ROWS_BIG)
-                                 : ceil_div(N, 128) * ceil_div(M, TILE_ROWS);
-  const int gran = p.stream ? 256 : 64;
-  int want = std::max(1, ceil_div(TARGET_BLOCKS, per_split));
+                                 : ceil_div(N, 256) * ceil_div(M, TILE_ROWS);
+  const int gran = 256;
+  int want = std::max(1, ceil_div(p.stream ? TARGET_BLOCKS : TARGET_BLOCKS_BIG, per_split));
   want = std::min(want, std::max(1, K / gran));
   int ks = ceil_div(ceil_div(K, want), gran) * gran;
   p.k_split = ks;
@@ -265,7 +266,7 @@ int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool fo
   if (pl.stream)
     launch_gemm_stream(p, false, s);
   else
-    launch_gemm_tile(p, s);
+    launch_gemm_big(p, s);
   if (use_partial && !force_partial) {
     GemmParams r = p;
     r.epi = final_epi;
@@ -323,7 +324,7 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_OUT_OF_MEMORY;
   }
   h->workspace_bytes = L.total;
-  if (gemm_tile_setup() != 0) {
+  if (gemm_tile_setup() != 0 || gemm_big_setup() != 0) {
     (void)hipGetLastError();
     hipFree(h->workspace);
     delete h;
@@ -508,7 +509,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   if (expert_stream)
     launch_gemm_stream(pu, fp4, s);
   else
-    launch_gemm_tile(pu, s);
+    launch_gemm_big(pu, s);
   tm.stop(LATENTMOE_STAGE_EXPERT_UP);
 
   tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
@@ -530,7 +531,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   if (expert_stream)
     launch_gemm_stream(pw, fp4, s);
   else
-    launch_gemm_tile(pw, s);
+    launch_gemm_big(pw, s);
   tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
 
   // ---- 7. combine ----
