@@ -63,13 +63,10 @@ struct GemmParams {
 
 // weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes)
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
-// LDS-tiled MFMA GEMM, 128 x 128 tiles (prefill-like shapes)
-void launch_gemm_tile(const GemmParams& p, hipStream_t s);
-// one-time kernel attributes (dynamic LDS above 64 KB); returns a HIP error code
-int gemm_tile_setup();
 // large-tile MFMA GEMM, 256 x 256 tiles (prefill-sized problems)
 void launch_gemm_big(const GemmParams& p, hipStream_t s);
 bool gemm_big_supports(int epi);
+// one-time kernel attributes (dynamic LDS above 64 KB); returns a HIP error code
 int gemm_big_setup();
 // sum split-K partials and apply the epilogue
 void launch_reduce(const GemmParams& p, hipStream_t s);
@@ -80,10 +77,13 @@ void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStrea
 // per-token top-K + softmax over logits [T, N] (+ bias); builds per-16-token expert masks
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
                  float* gates, uint32_t* masks, hipStream_t s);
-// counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile)
+// counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile);
+// with place_idx set it also does launch_place's work in the same workgroup (small T)
 void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
                         int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
-                        int* tile_rows, int* n_tiles, int max_tiles, hipStream_t s);
+                        int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
+                        const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
+                        hipStream_t s);
 // permuted positions: row_src[p] = token, row_gate[p] = gate, inv[t*K+k] = p
 void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
                   const int* block_prefix, int T, int N, int K, int* row_src, float* row_gate,

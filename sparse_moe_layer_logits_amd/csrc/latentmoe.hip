@@ -30,10 +30,17 @@ using namespace lmoe;
 
 namespace {
 
+#ifndef LMOE_SHARED_FORK_AT
+#define LMOE_SHARED_FORK_AT 1  // 0: at the start, 1: after the router GEMM, 2: after bucketing
+#endif
+
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
 constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
-constexpr int TARGET_BLOCKS = 512;      // streaming kernel: 8-wave blocks, several per CU
+#ifndef LMOE_TARGET_BLOCKS
+#define LMOE_TARGET_BLOCKS 256
+#endif
+constexpr int TARGET_BLOCKS = LMOE_TARGET_BLOCKS;  // streaming kernel: 8-wave blocks, several per CU
 constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 4-wave block per CU
 
 struct Plan {
@@ -198,7 +205,7 @@ struct latentmoe_handle_s {
   // the shared expert runs on a side stream forked from the caller's stream
   hipStream_t side = nullptr;
   hipStream_t side2 = nullptr;  // W_down, concurrent with routing
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_join2 = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_fork2 = nullptr, ev_join = nullptr, ev_join2 = nullptr;
   // graph replay of the whole forward (latentmoe_forward_graph)
   hipStream_t cap = nullptr;  // capture stream
   hipGraph_t graph = nullptr;
@@ -324,7 +331,7 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_OUT_OF_MEMORY;
   }
   h->workspace_bytes = L.total;
-  if (gemm_tile_setup() != 0 || gemm_big_setup() != 0) {
+  if (gemm_big_setup() != 0) {
     (void)hipGetLastError();
     hipFree(h->workspace);
     delete h;
@@ -339,6 +346,7 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
       hipStreamCreateWithFlags(&h->side2, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork2, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_join2, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
@@ -358,6 +366,7 @@ int latentmoe_destroy(latentmoe_handle_t h) {
   if (!h) return LATENTMOE_OK;
   for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_fork2) (void)hipEventDestroy(h->ev_fork2);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_join2) (void)hipEventDestroy(h->ev_join2);
   if (h->side) (void)hipStreamDestroy(h->side);
@@ -387,59 +396,72 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
 
-  // The shared expert does not depend on routing: fork it onto the side
-  // stream (same priority) and join before the up-projection adds onto y.
+  // The shared expert and W_down do not depend on routing: each runs on a side
+  // stream forked from the caller's stream (same priority) and joins before
+  // its consumer.  W_down is forked at the start; the shared expert after the
+  // router GEMM, so the router runs at full speed and the shared expert's
+  // weight stream fills the latency-bound top-K / bucketing chain.
   hipStream_t side = h->side;
-  (void)hipEventRecord(h->ev_fork, s);
-  (void)hipStreamWaitEvent(side, h->ev_fork, 0);
-  // ---- shared expert (side stream): h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
-  tm.start(LATENTMOE_STAGE_SHARED_UP, side);
-  GemmParams ps = base_params();
-  ps.seg[0] = GemmSeg{x, w.shared_w1, d};
-  ps.nseg = 1;
-  ps.lda = d;
-  ps.ldb = d;
-  ps.N = ms;
-  ps.epi = EPI_SQRELU_HILO;
-  ps.C = b.hs_hi;
-  ps.C2 = b.hs_lo;
-  ps.ldc = ms;
-  run_dense(h, ps, T, side, false, b.partial2);
-  tm.stop(LATENTMOE_STAGE_SHARED_UP, side);
-
-  tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
-  GemmParams p2 = base_params();
-  p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
-  p2.a_lo = b.hs_lo;
-  p2.nseg = 1;
-  p2.lda = ms;
-  p2.ldb = ms;
-  p2.N = d;
-  p2.epi = EPI_F32;
-  p2.C = y;
-  p2.ldc = d;
-  run_dense(h, p2, T, side, false, b.partial2);
-  tm.stop(LATENTMOE_STAGE_SHARED_DOWN, side);
-
-  (void)hipEventRecord(h->ev_join, side);
-
-  // ---- z = W_down x (side stream 2, concurrent with routing) ----
   hipStream_t side2 = h->side2;
-  (void)hipStreamWaitEvent(side2, h->ev_fork, 0);
-  tm.start(LATENTMOE_STAGE_DOWN_PROJ, side2);
-  GemmParams pd = base_params();
-  pd.seg[0] = GemmSeg{x, w.w_down, d};
-  pd.nseg = 1;
-  pd.lda = d;
-  pd.ldb = d;
-  pd.N = L;
-  pd.epi = EPI_BF16_HILO;
-  pd.C = b.z;
-  pd.C2 = b.z_lo;
-  pd.ldc = L;
-  run_dense(h, pd, T, side2, false, b.partial3);
-  tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
-  (void)hipEventRecord(h->ev_join2, side2);
+  auto fork_to = [&](hipStream_t to, hipEvent_t ev) {
+    (void)hipEventRecord(ev, s);
+    (void)hipStreamWaitEvent(to, ev, 0);
+  };
+  auto shared_expert = [&]() {
+    // ---- shared expert (side stream): h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
+    tm.start(LATENTMOE_STAGE_SHARED_UP, side);
+    GemmParams ps = base_params();
+    ps.seg[0] = GemmSeg{x, w.shared_w1, d};
+    ps.nseg = 1;
+    ps.lda = d;
+    ps.ldb = d;
+    ps.N = ms;
+    ps.epi = EPI_SQRELU_HILO;
+    ps.C = b.hs_hi;
+    ps.C2 = b.hs_lo;
+    ps.ldc = ms;
+    run_dense(h, ps, T, side, false, b.partial2);
+    tm.stop(LATENTMOE_STAGE_SHARED_UP, side);
+
+    tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
+    GemmParams p2 = base_params();
+    p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
+    p2.a_lo = b.hs_lo;
+    p2.nseg = 1;
+    p2.lda = ms;
+    p2.ldb = ms;
+    p2.N = d;
+    p2.epi = EPI_F32;
+    p2.C = y;
+    p2.ldc = d;
+    run_dense(h, p2, T, side, false, b.partial2);
+    tm.stop(LATENTMOE_STAGE_SHARED_DOWN, side);
+
+    (void)hipEventRecord(h->ev_join, side);
+  };
+  auto down_proj = [&]() {
+    // ---- z = W_down x (side stream 2, concurrent with routing) ----
+    tm.start(LATENTMOE_STAGE_DOWN_PROJ, side2);
+    GemmParams pd = base_params();
+    pd.seg[0] = GemmSeg{x, w.w_down, d};
+    pd.nseg = 1;
+    pd.lda = d;
+    pd.ldb = d;
+    pd.N = L;
+    pd.epi = EPI_BF16_HILO;
+    pd.C = b.z;
+    pd.C2 = b.z_lo;
+    pd.ldc = L;
+    run_dense(h, pd, T, side2, false, b.partial3);
+    tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
+    (void)hipEventRecord(h->ev_join2, side2);
+  };
+  fork_to(side2, h->ev_fork);
+  down_proj();
+#if LMOE_SHARED_FORK_AT == 0
+  fork_to(side, h->ev_fork2);
+  shared_expert();
+#endif
 
   // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
   tm.start(LATENTMOE_STAGE_ROUTER);
@@ -454,6 +476,10 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pr.C = b.logits;
   run_dense(h, pr, T, s, false);
   tm.stop(LATENTMOE_STAGE_ROUTER);
+#if LMOE_SHARED_FORK_AT == 1
+  fork_to(side, h->ev_fork2);
+  shared_expert();
+#endif
 
   // ---- 2. top-K + softmax (sums the router's split partials, adds the bias) ----
   tm.start(LATENTMOE_STAGE_TOPK);
@@ -469,11 +495,18 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       expert_stream ? (avg_rows <= 8.0 ? STREAM_ROWS_SMALL : STREAM_ROWS_BIG) : TILE_ROWS;
   const int max_tiles = ceil_div(TK, rows_per_tile) + (int)std::min<long long>(N, TK);
   tm.start(LATENTMOE_STAGE_BUCKET);
+  const bool fuse_place = TK <= 8192;  // one workgroup places a few thousand rows quickly
   launch_bucket_scan(b.masks, T, N, rows_per_tile, b.counts, b.offsets, b.block_prefix,
-                     b.tile_expert, b.tile_row0, b.tile_rows, b.n_tiles, max_tiles, s);
-  launch_place(idx_buf, gate_buf, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src, b.row_gate,
-               b.inv, s);
+                     b.tile_expert, b.tile_row0, b.tile_rows, b.n_tiles, max_tiles,
+                     fuse_place ? idx_buf : nullptr, gate_buf, K, b.row_src, b.row_gate, b.inv, s);
+  if (!fuse_place)
+    launch_place(idx_buf, gate_buf, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src,
+                 b.row_gate, b.inv, s);
   tm.stop(LATENTMOE_STAGE_BUCKET);
+#if LMOE_SHARED_FORK_AT == 2
+  fork_to(side, h->ev_fork2);
+  shared_expert();
+#endif
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
   (void)hipStreamWaitEvent(s, h->ev_join2, 0);

@@ -152,11 +152,38 @@ void launch_topk(const float* logits, const float* bias, int T, int N, int K, in
 // expert e is a prefix over 16-token blocks plus a popcount inside the block,
 // so the order is deterministic.  One workgroup, thread e owns expert e.
 // ---------------------------------------------------------------------------
+struct PlaceArgs {  // fused placement (small T): see place_kernel
+  const int* idx;
+  const float* gates;
+  int T, K;
+  int* row_src;
+  float* row_gate;
+  int* inv;
+};
+
+__device__ __forceinline__ void place_one(long long i, const int* __restrict__ idx,
+                                          const float* __restrict__ gates,
+                                          const uint32_t* __restrict__ masks,
+                                          const int* __restrict__ offsets,
+                                          const int* __restrict__ block_prefix, int N, int K,
+                                          int* __restrict__ row_src, float* __restrict__ row_gate,
+                                          int* __restrict__ inv) {
+  const int t = (int)(i / K);
+  const int e = idx[i];
+  const int b = t / TOPK_TOKENS_PER_BLOCK;
+  const int tl = t % TOPK_TOKENS_PER_BLOCK;
+  const uint32_t m = masks[(long long)b * N + e];
+  const int pos = offsets[e] + block_prefix[(long long)b * N + e] + __popc(m & ((1u << tl) - 1u));
+  row_src[pos] = t;
+  row_gate[pos] = gates[i];
+  inv[i] = pos;
+}
+
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     const uint32_t* __restrict__ masks, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ block_prefix, int* __restrict__ tile_expert,
     int* __restrict__ tile_row0, int* __restrict__ tile_rows, int* __restrict__ n_tiles,
-    int max_tiles) {
+    int max_tiles, PlaceArgs pa) {
   __shared__ int scan_a[1024];
   __shared__ int scan_b[1024];
   const int e = threadIdx.x;
@@ -210,15 +237,25 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     offsets[N] = scan_a[1023];
     n_tiles[0] = min(scan_b[1023], max_tiles);
   }
+  if (pa.idx) {  // small T: the same workgroup places every (token, k)
+    __syncthreads();
+    const long long n = (long long)pa.T * pa.K;
+    for (long long i = threadIdx.x; i < n; i += blockDim.x)
+      place_one(i, pa.idx, pa.gates, masks, offsets, block_prefix, N, pa.K, pa.row_src, pa.row_gate,
+                pa.inv);
+  }
 }
 
 void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
                         int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
-                        int* tile_rows, int* n_tiles, int max_tiles, hipStream_t s) {
+                        int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
+                        const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
+                        hipStream_t s) {
   const int nblk = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  PlaceArgs pa{place_idx, place_gates, T, K, row_src, row_gate, inv};
   bucket_scan_kernel<<<1, 1024, 0, s>>>(masks, nblk, N, tile_rows_max, counts, offsets,
                                         block_prefix, tile_expert, tile_row0, tile_rows, n_tiles,
-                                        max_tiles);
+                                        max_tiles, pa);
 }
 
 __global__ void place_kernel(const int* __restrict__ idx, const float* __restrict__ gates,
@@ -228,15 +265,7 @@ __global__ void place_kernel(const int* __restrict__ idx, const float* __restric
                              int* __restrict__ inv) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)T * K) return;
-  const int t = (int)(i / K);
-  const int e = idx[i];
-  const int b = t / TOPK_TOKENS_PER_BLOCK;
-  const int tl = t % TOPK_TOKENS_PER_BLOCK;
-  const uint32_t m = masks[(long long)b * N + e];
-  const int pos = offsets[e] + block_prefix[(long long)b * N + e] + __popc(m & ((1u << tl) - 1u));
-  row_src[pos] = t;
-  row_gate[pos] = gates[i];
-  inv[i] = pos;
+  place_one(i, idx, gates, masks, offsets, block_prefix, N, K, row_src, row_gate, inv);
 }
 
 void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
