@@ -63,6 +63,10 @@ struct GemmParams {
 
 // weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes)
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
+// grouped MFMA GEMM for 64-row expert tiles with dual activations (tens of rows
+// per expert): activations through an LDS ring, weights read once per tile
+void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s);
+bool gemm_mid_supports(const GemmParams& p, bool fp4);
 // large-tile MFMA GEMM, 256 x 256 tiles (prefill-sized problems)
 void launch_gemm_big(const GemmParams& p, hipStream_t s);
 bool gemm_big_supports(int epi);

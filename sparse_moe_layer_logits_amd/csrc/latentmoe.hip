@@ -37,6 +37,12 @@ namespace {
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
 constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
+#ifndef LMOE_MID_FP4
+#define LMOE_MID_FP4 1  // FP4 experts with 64-row tiles use the mid kernel
+#endif
+#ifndef LMOE_MID_BF16
+#define LMOE_MID_BF16 1  // bf16 experts with 64-row tiles use the mid kernel
+#endif
 #ifndef LMOE_TARGET_BLOCKS
 #define LMOE_TARGET_BLOCKS 256
 #endif
@@ -523,6 +529,15 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pe.M = rows_per_tile;
   pe.splits = 1;
 
+  auto launch_expert = [&](const GemmParams& g) {
+    if (!expert_stream)
+      launch_gemm_big(g, s);
+    else if (rows_per_tile == STREAM_ROWS_BIG && (fp4 ? LMOE_MID_FP4 : LMOE_MID_BF16) && gemm_mid_supports(g, fp4))
+      launch_gemm_mid(g, fp4, s);
+    else
+      launch_gemm_stream(g, fp4, s);
+  };
+
   tm.start(LATENTMOE_STAGE_EXPERT_UP);
   GemmParams pu = pe;
   pu.seg[0] = GemmSeg{b.z, w.expert_w1, L};
@@ -539,10 +554,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pu.C = b.h;
   pu.C2 = b.h_lo;
   pu.ldc = m;
-  if (expert_stream)
-    launch_gemm_stream(pu, fp4, s);
-  else
-    launch_gemm_big(pu, s);
+  launch_expert(pu);
   tm.stop(LATENTMOE_STAGE_EXPERT_UP);
 
   tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
@@ -561,10 +573,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pw.row_scale = b.row_gate;
   pw.C = b.og;
   pw.ldc = L;
-  if (expert_stream)
-    launch_gemm_stream(pw, fp4, s);
-  else
-    launch_gemm_big(pw, s);
+  launch_expert(pw);
   tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
 
   // ---- 7. combine ----
