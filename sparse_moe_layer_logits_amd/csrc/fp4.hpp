@@ -9,23 +9,26 @@
 
 namespace lmoe {
 
-// FP4 E2M1 nibble -> fp32 bits (sign, 2-bit exponent with bias 1, 1-bit mantissa)
-__device__ __forceinline__ uint32_t e2m1_f32_bits(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-  return mag | ((c & 8u) << 28);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// the two E2M1 codes of byte I of `codes` (low nibble first) times a block scale
+// -> two bf16 in one word.  The conversion with a unit scale gives the exact
+// E2M1 values in fp32; the products are bf16 numbers, so keeping the upper
+// halves is exact.
+template <int I>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16(uint32_t codes, float scale) {
+  const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, I);
+  const float a = v.x * scale, b = v.y * scale;
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // eight E2M1 codes (low nibble first) times a block scale -> eight bf16 (exact)
 __device__ __forceinline__ u32x4_t fp4x8_to_bf16(uint32_t codes, float scale) {
   u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = __uint_as_float(e2m1_f32_bits((codes >> (8 * i)) & 15u)) * scale;
-    const float b = __uint_as_float(e2m1_f32_bits((codes >> (8 * i + 4)) & 15u)) * scale;
-    // the products are bf16 numbers, so dropping the low half is exact
-    r[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-  }
+  r[0] = fp4x2_to_bf16<0>(codes, scale);
+  r[1] = fp4x2_to_bf16<1>(codes, scale);
+  r[2] = fp4x2_to_bf16<2>(codes, scale);
+  r[3] = fp4x2_to_bf16<3>(codes, scale);
   return r;
 }
 

@@ -1,43 +1,51 @@
-// Grouped MFMA GEMM for tiles of up to 64 activation rows with weights read
-// once per tile (experts that see tens of tokens; the FP4 workload).
+// Grouped MFMA GEMM for block-scaled FP4 expert weights and tiles of up to 64
+// activation rows (experts that see tens of tokens), dual (hi + lo bf16)
+// activations.
 //
-// Block: four waves; wave w owns NT 16-row MFMA tiles of weight rows
-// (n0 + 16*NT*w ..) against the tile's activation rows in 16-row groups (a
-// tile of r rows runs ceil(r/16) groups, no more).  The activation tile (bf16
-// hi + lo, 64 k per stage) is staged once per block in LDS and read by all
-// four waves; each wave loads its own weight fragments straight into
-// registers, two 64-wide k blocks ahead, so every weight byte crosses HBM once
-// and is decoded once.
+// Block: W waves (W = 8, 7 or 4, the largest that divides N into 64-row wave
+// slabs); wave w owns four 16-row MFMA tiles of weight rows (n0 + 64w ..)
+// against the tile's activation rows in 16-row groups (a tile of r rows runs
+// ceil(r/16) groups, no more).  The k loop runs in stages of 128.  Stage s is
+// loaded into register set s % NS, NS - 1 stages ahead: the activation stage
+// (64 rows x 128 k, hi and lo, shared by all W waves) and the stage's E4M3
+// block scales go through one of two LDS slots; each wave keeps its FP4 codes
+// (64 contiguous bytes per weight row and stage) in registers.  The block
+// scales are read from a stage-major copy made at initialisation, so one
+// stage's scales for the block are one contiguous range.  Every weight byte
+// crosses HBM once and is decoded once.
 //
-// Block-scaled FP4 weights ("Nemotron 3 Super", section 3.6; E2M1 elements
-// and E4M3 block scales per "Nemotron 3 Ultra") are decoded in registers: the
-// packed FP4 -> bf16 conversion with a unit scale gives the exact E2M1 values,
-// and an fp32 multiply by the E4M3 block scale is exact as well (every such
-// product is a bf16 number).  The per-matrix fp32 scale multiplies the
-// accumulator in the epilogue.
+// Block-scaled FP4 ("Nemotron 3 Super", section 3.6; E2M1 elements and E4M3
+// block scales per "Nemotron 3 Ultra") is decoded in registers with the exact
+// decoder of fp4.hpp; the per-matrix fp32 scale multiplies the accumulator in
+// the epilogue.
 //
-// MFMA roles and the k layout follow the other kernels: weight tile = MFMA A
-// operand (rows = output columns n), activations = B operand; inside each
-// 64-wide k block lane group g holds k = 16g .. 16g+15 (one FP4 scale block)
-// and MFMA step j uses 16g + 8j .. +7.
+// MFMA roles follow the other kernels: weight tile = MFMA A operand (rows =
+// output columns n), activations = B operand.  k order inside a 128-wide stage:
+// lane group g holds k = 32g .. 32g+31 (16 code bytes, two scale blocks) and
+// MFMA step j (0..3) uses k = 32g + 8j .. +7 from every lane group.
 #include "common.hpp"
 #include "epilogue.hpp"
+#include "fp4.hpp"
 #include "kernels.hpp"
 
 #include <type_traits>
 
-#ifndef LMOE_MID_NT_FP4
-#define LMOE_MID_NT_FP4 4
+#ifndef LMOE_MID_SETS
+#define LMOE_MID_SETS 3  // register sets: loads run LMOE_MID_SETS - 1 stages ahead
 #endif
 
 namespace lmoe {
 
-constexpr int MD_ROWS = 64;                  // activation rows per tile
-constexpr int MD_PARTB = MD_ROWS * 128;      // one part of one stage: 64 rows x 64 k bf16 = 8 KB
-constexpr int MD_STAGEB = 2 * MD_PARTB;      // hi + lo
+constexpr int MD_ROWS = 64;                 // activation rows per tile
+constexpr int MD_NT = 4;                    // 16-row weight tiles per wave
+constexpr int MD_KS = 128;                  // k per stage
+constexpr int MD_ROWB = MD_KS * 2;          // bytes of one activation row per stage and part
+constexpr int MD_PARTB = MD_ROWS * MD_ROWB; // 16 KB
+constexpr int MD_PIECES = MD_PARTB / 16;    // 16-byte pieces per part and stage
 
+// activation byte offset in a slot: 16 pieces of 16 bytes per row, XOR-swizzled
 __device__ __forceinline__ int md_off(int part, int row, int piece) {
-  return part * MD_PARTB + row * 128 + ((piece ^ (row & 7)) << 4);
+  return part * MD_PARTB + row * MD_ROWB + ((piece ^ (row & 15)) << 4);
 }
 
 // wait for this wave's LDS operations (its stores) before a barrier; vector
@@ -46,199 +54,157 @@ __device__ __forceinline__ void md_wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
-// one wave's activation slice of one stage: two 16-byte pieces of hi and lo
-struct MdX {
-  u32x4_t v[2][2];  // [chunk][part]
+// one thread's share of one stage: XP 16-byte pieces of each activation part,
+// the 8 scale bytes of one weight row, 16 code bytes per weight tile
+template <int XP>
+struct MdStage {
+  u32x4_t x[2][XP];      // [part][piece]
+  u32x2_t sc;            // E4M3 scales of weight row n0 + thread
+  u32x4_t codes[MD_NT];  // 32 E2M1 codes per weight tile
 };
 
-// one wave's weight fragments for one 64-wide k block
-template <bool FP4, int NT>
-struct MdW;
-template <int NT>
-struct MdW<false, NT> {
-  u32x4_t v[NT][2];  // [n tile][step]
-};
-template <int NT>
-struct MdW<true, NT> {
-  u32x2_t codes[NT];   // 16 E2M1 codes per n tile
-  uint32_t scale[NT];  // E4M3 byte per n tile
-};
-
-// two E2M1 codes (byte I of `codes`) times an E4M3 block scale -> two bf16
-template <int I>
-__device__ __forceinline__ uint32_t md_fp4x2(uint32_t codes, float s) {
-  const bf16x2_t q = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, I);  // exact E2M1
-  const uint32_t qb = __builtin_bit_cast(uint32_t, q);
-  const float lo = __uint_as_float(qb << 16) * s;
-  const float hi = __uint_as_float(qb & 0xFFFF0000u) * s;
-  // the products are bf16 numbers: keep the upper halves
-  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// eight E2M1 codes times an E4M3 block scale (already as float) -> eight bf16
-__device__ __forceinline__ u32x4_t md_fp4x8(uint32_t codes, float s) {
-  u32x4_t r;
-  r[0] = md_fp4x2<0>(codes, s);
-  r[1] = md_fp4x2<1>(codes, s);
-  r[2] = md_fp4x2<2>(codes, s);
-  r[3] = md_fp4x2<3>(codes, s);
-  return r;
-}
-
-// The pipelined main loop for a tile whose rows fill MT 16-row groups.
-// Stage s (one 64-wide k block) is loaded into register set s % 3 two steps
-// ahead: the activation part is written to LDS slot s % 2 at step s, the
-// weight part is used from registers.  Every step issues the same loads (past
-// the last k block it re-reads the last one), so the compiler's in-order wait
-// counts are exact on every path and the loads of two later stages stay in
-// flight while a stage is multiplied.
-template <bool FP4, int NT, int EPI, int MT>
+template <int W, int EPI, int MT>
 __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int expert, int row0,
-                                         int rows, int nbase, bool active) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+                                         int rows, int n0, int nbase, bool active) {
+  constexpr int NTH = 64 * W;
+  constexpr int BN = 64 * W;
+  constexpr int XP = (MD_PIECES + NTH - 1) / NTH;
+  // register sets: three fit next to two activation pieces per thread
+  constexpr int NS = XP <= 2 ? LMOE_MID_SETS : 2;
+  constexpr int SLOTB = 2 * MD_PARTB + BN * 8;  // hi + lo + scales
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
-  const int P = p.seg[0].K >> 6;  // 64-wide k blocks
+  const int K = p.seg[0].K;
+  const int P = K / MD_KS;
 
-  // activations: this wave moves chunks wave and wave + 4 (1 KB = 8 rows x
-  // 128 B each) of both parts.  Lane l handles row 8c + l/8, logical piece l%8,
-  // stored at piece (l%8) ^ (row & 7).
-  uint32_t x_off[2], x_lds[2];
+  // ---- activations: piece id = i * NTH + tid -> row id / 16, piece id % 16
+  // (ids past the stage are clamped for the load and not stored) ----
+  uint32_t x_off[XP], x_lds[XP];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+  for (int i = 0; i < XP; ++i) {
+    const int id = min(i * NTH + tid, MD_PIECES - 1);
+    const int row = id >> 4, piece = id & 15;
     const int xr = min(row, rows - 1);
     const int src = p.row_index ? p.row_index[row0 + xr] : row0 + xr;
-    x_off[i] = ((uint32_t)src * (uint32_t)p.lda + (lane & 7) * 8) * 2u;  // bytes
-    x_lds[i] = md_off(0, row, lane & 7);
+    x_off[i] = ((uint32_t)src * (uint32_t)p.lda + piece * 8) * 2u;  // bytes
+    x_lds[i] = md_off(0, row, piece);
   }
   const uint8_t* Xhi = reinterpret_cast<const uint8_t*>(p.seg[0].A);
   const uint8_t* Xlo = reinterpret_cast<const uint8_t*>(p.a_lo);
 
-  // weights: uniform expert base + 32-bit per-lane offsets (row n, k = 16g ..);
-  // waves past the end read a valid slab they never use (p.N is a multiple of 16 * NT)
-  const int wrow0 = min(nbase, p.N - 16 * NT);
-  const uint8_t* Wb;
-  const uint8_t* Sb = nullptr;
-  uint32_t w_off[NT], s_off[NT];
-  if constexpr (FP4) {
-    Wb = reinterpret_cast<const uint8_t*>(p.seg[0].B) + (size_t)expert * (size_t)(p.b_stride / 2);
-    Sb = p.b_scale + (size_t)expert * (size_t)p.N * (size_t)(p.ldb / 16);
+  // ---- codes: uniform expert base + 32-bit per-lane offsets (row n, bytes 16g ..);
+  // waves past the end read a valid slab they never use (p.N is a multiple of 64)
+  const int wrow0 = min(nbase, p.N - 16 * MD_NT);
+  const uint8_t* Wb = reinterpret_cast<const uint8_t*>(p.seg[0].B) + (size_t)expert * (size_t)(p.b_stride / 2);
+  uint32_t w_off[MD_NT];
+  uint32_t s_lds[MD_NT];  // this lane's two scale bytes in a slot's scale part
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t n = wrow0 + nt * 16 + r16;
-      w_off[nt] = n * (uint32_t)(p.ldb / 2) + 8u * g;
-      s_off[nt] = n * (uint32_t)(p.ldb / 16) + g;
-    }
-  } else {
-    Wb = reinterpret_cast<const uint8_t*>(p.seg[0].B) + (size_t)expert * (size_t)p.b_stride * 2;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t n = wrow0 + nt * 16 + r16;
-      w_off[nt] = (n * (uint32_t)p.ldb + 16u * g) * 2u;
-      s_off[nt] = 0;
-    }
+  for (int nt = 0; nt < MD_NT; ++nt) {
+    const uint32_t n = wrow0 + nt * 16 + r16;
+    w_off[nt] = n * (uint32_t)(p.ldb / 2) + 16u * g;
+    s_lds[nt] = 2 * MD_PARTB + (n - n0) * 8 + 2 * g;
   }
+  // scales, stage-major [expert][stage][N][8]: thread tid moves row n0 + tid
+  // (the last row below N past the end)
+  const uint8_t* Sb = p.b_scale_sm + ((size_t)expert * P * p.N + min(n0 + tid, p.N - 1)) * 8;
+  const size_t s_stage = (size_t)p.N * 8;
 
-  auto issue = [&](MdX& xv, MdW<FP4, NT>& wv, int ps) {
-    const uint8_t* xh = Xhi + ps * 128;
-    const uint8_t* xl = Xlo + ps * 128;
+  auto issue = [&](MdStage<XP>& st, int ps) {
+    const uint8_t* xh = Xhi + ps * (MD_KS * 2);
+    const uint8_t* xl = Xlo + ps * (MD_KS * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      xv.v[i][0] = *reinterpret_cast<const u32x4_t*>(xh + x_off[i]);
-      xv.v[i][1] = *reinterpret_cast<const u32x4_t*>(xl + x_off[i]);
+    for (int i = 0; i < XP; ++i) {
+      st.x[0][i] = *reinterpret_cast<const u32x4_t*>(xh + x_off[i]);
+      st.x[1][i] = *reinterpret_cast<const u32x4_t*>(xl + x_off[i]);
     }
-    if constexpr (FP4) {
-      const uint8_t* wb = Wb + ps * 32;
-      const uint8_t* sb = Sb + ps * 4;
+    st.sc = *reinterpret_cast<const u32x2_t*>(Sb + ps * s_stage);
+    const uint8_t* wb = Wb + ps * (MD_KS / 2);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        wv.codes[nt] = *reinterpret_cast<const u32x2_t*>(wb + w_off[nt]);
-        wv.scale[nt] = sb[s_off[nt]];
-      }
-    } else {
-      const uint8_t* wb = Wb + ps * 128;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        wv.v[nt][0] = *reinterpret_cast<const u32x4_t*>(wb + w_off[nt]);
-        wv.v[nt][1] = *reinterpret_cast<const u32x4_t*>(wb + w_off[nt] + 16);
-      }
-    }
+    for (int nt = 0; nt < MD_NT; ++nt) st.codes[nt] = *reinterpret_cast<const u32x4_t*>(wb + w_off[nt]);
   };
-  auto stash = [&](const MdX& xv, int s) {
-    uint8_t* st = smem + (s & 1) * MD_STAGEB;
+  auto stash = [&](const MdStage<XP>& st, int s) {
+    uint8_t* slot = smem + (s & 1) * SLOTB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4_t*>(st + x_lds[i]) = xv.v[i][0];
-      *reinterpret_cast<u32x4_t*>(st + MD_PARTB + x_lds[i]) = xv.v[i][1];
+    for (int i = 0; i < XP; ++i) {
+      if (XP * NTH == MD_PIECES || i * NTH + tid < MD_PIECES) {
+        *reinterpret_cast<u32x4_t*>(slot + x_lds[i]) = st.x[0][i];
+        *reinterpret_cast<u32x4_t*>(slot + MD_PARTB + x_lds[i]) = st.x[1][i];
+      }
     }
+    *reinterpret_cast<u32x2_t*>(slot + 2 * MD_PARTB + tid * 8) = st.sc;
   };
 
-  f32x4_t acc[NT][MT];
+  f32x4_t acc[MD_NT][MT];
 #pragma unroll
-  for (int a = 0; a < NT; ++a)
+  for (int a = 0; a < MD_NT; ++a)
 #pragma unroll
     for (int b = 0; b < MT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const MdW<FP4, NT>& wv, int s) {
-    const uint8_t* st = smem + (s & 1) * MD_STAGEB;
-    float sc[NT];
-    if constexpr (FP4) {
+  auto compute = [&](const MdStage<XP>& st, int s) {
+    const uint8_t* slot = smem + (s & 1) * SLOTB;
+    float sc[MD_NT][2];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sc[nt] = e4m3_to_f32(wv.scale[nt]);
+    for (int nt = 0; nt < MD_NT; ++nt) {
+      const uint32_t two = *reinterpret_cast<const uint16_t*>(slot + s_lds[nt]);
+      sc[nt][0] = e4m3_to_f32(two & 0xFFu);
+      sc[nt][1] = e4m3_to_f32(two >> 8);
     }
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
+    for (int j = 0; j < 4; ++j) {
       u32x4_t xf[2][MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int part = 0; part < 2; ++part)
-          xf[part][mt] = *reinterpret_cast<const u32x4_t*>(st + md_off(part, mt * 16 + r16, 2 * g + js));
+          xf[part][mt] = *reinterpret_cast<const u32x4_t*>(slot + md_off(part, mt * 16 + r16, 4 * g + j));
+      u32x4_t wf[MD_NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        u32x4_t wf;
-        if constexpr (FP4)
-          wf = md_fp4x8(wv.codes[nt][js], sc[nt]);
-        else
-          wf = wv.v[nt][js];
+      for (int nt = 0; nt < MD_NT; ++nt) wf[nt] = fp4x8_to_bf16(st.codes[nt][j], sc[nt][j >> 1]);
+#pragma unroll
+      for (int nt = 0; nt < MD_NT; ++nt) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[nt][mt] = mfma_16x16x32(wf, xf[0][mt], acc[nt][mt]);
-          acc[nt][mt] = mfma_16x16x32(wf, xf[1][mt], acc[nt][mt]);
+          acc[nt][mt] = mfma_16x16x32(wf[nt], xf[0][mt], acc[nt][mt]);
+          acc[nt][mt] = mfma_16x16x32(wf[nt], xf[1][mt], acc[nt][mt]);
         }
       }
     }
   };
 
-  MdX x0, x1, x2;
-  MdW<FP4, NT> w0, w1, w2;
-  // sched_barrier keeps each stage's loads together and in stage order, so a
-  // stage's loads are never behind the next stage's in the in-order counter
-  issue(x0, w0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(x1, w1, min(1, P - 1));
-  __builtin_amdgcn_sched_barrier(0);
-  auto step = [&](MdX& xc, MdW<FP4, NT>& wc, MdX& xn, MdW<FP4, NT>& wn, int s) {
-    stash(xc, s);  // slot s % 2 was last read at step s - 2, before the previous barrier
-    md_wait_lgkm0();
-    asm volatile("s_barrier" ::: "memory");
-    issue(xn, wn, min(s + 2, P - 1));
+  // Stage s lives in register set s % NS; at step s, set (s - 1) % NS (emptied
+  // at step s - 1) is refilled with stage s + NS - 1 first, then stage s's
+  // activations and scales go to LDS slot s % 2 (last read at step s - 2,
+  // before the previous barrier), then stage s is multiplied.  Every step
+  // issues the same loads (past the last stage it re-reads the last one), so
+  // the compiler's in-order wait counts are exact on every path;
+  // sched_barrier keeps each stage's loads together and in stage order.  The
+  // trip count is padded to a multiple of NS (one loop exit; a padding step
+  // only moves data) so the register sets stay static.
+  MdStage<XP> st[NS];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    issue(st[i], min(i, P - 1));
     __builtin_amdgcn_sched_barrier(0);
-    if (active && s < P) compute(wc, s);
-  };
-  // the trip count is padded to a multiple of three (one loop exit; the
-  // padding steps only move data) so the register sets stay static
-  const int P3 = (P + 2) / 3 * 3;
-  for (int s = 0; s < P3; s += 3) {
-    step(x0, w0, x2, w2, s);
-    step(x1, w1, x0, w0, s + 1);
-    step(x2, w2, x1, w1, s + 2);
+  }
+  const int PN = (P + NS - 1) / NS * NS;
+  for (int s0 = 0; s0 < PN; s0 += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int s = s0 + i;
+      issue(st[(i + NS - 1) % NS], min(s + NS - 1, P - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      stash(st[i], s);
+      md_wait_lgkm0();
+      asm volatile("s_barrier" ::: "memory");
+      if (active && s < P) compute(st[i], s);
+    }
   }
 
   if (!active) return;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < MD_NT; ++nt) {
     const int n = nbase + nt * 16 + 4 * g;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -248,53 +214,103 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   }
 }
 
-template <bool FP4, int NT, int EPI>
-__global__ __launch_bounds__(256) void gemm_mid_kernel(GemmParams p) {
+template <int W>
+constexpr int mid_lds_bytes() {
+  return 2 * (2 * MD_PARTB + 64 * W * 8);
+}
+
+template <int W, int EPI>
+__global__ __launch_bounds__(64 * W) void gemm_mid_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int BN = 4 * 16 * NT;  // weight rows per block
+  constexpr int BN = 64 * W;
   const int NQ = (p.N + BN - 1) / BN;
-  const int j = blockIdx.x / NQ;
-  const int q = blockIdx.x % NQ;
-  if (j >= p.n_tiles[0]) return;
+  const int b = blockIdx.x;
+  if (b >= p.n_tiles[0] * NQ) return;
+  const int j = b / NQ;
+  const int q = b % NQ;
   const int expert = p.tile_expert[j];
   const int row0 = p.tile_row0[j];
   const int rows = p.tile_rows[j];
-  const int nbase = q * BN + (threadIdx.x >> 6) * 16 * NT;
+  const int n0 = q * BN;
+  const int nbase = n0 + (threadIdx.x >> 6) * 16 * MD_NT;
   const bool active = nbase < p.N;  // wave-uniform; inactive waves still stage activations
   switch ((rows + 15) >> 4) {
-    case 1: mid_body<FP4, NT, EPI, 1>(p, smem, expert, row0, rows, nbase, active); break;
-    case 2: mid_body<FP4, NT, EPI, 2>(p, smem, expert, row0, rows, nbase, active); break;
-    case 3: mid_body<FP4, NT, EPI, 3>(p, smem, expert, row0, rows, nbase, active); break;
-    default: mid_body<FP4, NT, EPI, 4>(p, smem, expert, row0, rows, nbase, active); break;
+    case 1: mid_body<W, EPI, 1>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    case 2: mid_body<W, EPI, 2>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    case 3: mid_body<W, EPI, 3>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    default: mid_body<W, EPI, 4>(p, smem, expert, row0, rows, n0, nbase, active); break;
   }
 }
 
-template <bool FP4, int NT, int EPI>
+template <int W, int EPI>
 static void mid_launch(const GemmParams& p, hipStream_t s) {
-  constexpr int BN = 4 * 16 * NT;
-  const long long blocks = (long long)p.max_tiles * ((p.N + BN - 1) / BN);
+  const long long blocks = (long long)p.max_tiles * ((p.N + 64 * W - 1) / (64 * W));
   if (blocks <= 0) return;
-  gemm_mid_kernel<FP4, NT, EPI><<<(unsigned)blocks, 256, 2 * MD_STAGEB, s>>>(p);
+  gemm_mid_kernel<W, EPI><<<(unsigned)blocks, 64 * W, mid_lds_bytes<W>(), s>>>(p);
 }
 
-constexpr int MD_NT_FP4 = LMOE_MID_NT_FP4;
-constexpr int MD_NT_BF16 = 4;
+// waves per block: the largest of 8, 7 that splits N into whole blocks, else 4
+static int mid_waves(int N) { return N % 512 == 0 ? 8 : N % 448 == 0 ? 7 : 4; }
+
+template <int EPI>
+static void mid_launch_w(const GemmParams& p, hipStream_t s) {
+  switch (mid_waves(p.N)) {
+    case 8: mid_launch<8, EPI>(p, s); break;
+    case 7: mid_launch<7, EPI>(p, s); break;
+    default: mid_launch<4, EPI>(p, s); break;
+  }
+}
 
 bool gemm_mid_supports(const GemmParams& p, bool fp4) {
-  const int nt = fp4 ? MD_NT_FP4 : MD_NT_BF16;
-  return p.tile_expert && p.rows_per_tile <= MD_ROWS && p.a_lo && p.nseg == 1 &&
-         p.N % (16 * nt) == 0 && p.seg[0].K % 64 == 0 && p.seg[0].K >= 64 &&
+  return fp4 && p.tile_expert && p.rows_per_tile <= MD_ROWS && p.a_lo && p.nseg == 1 &&
+         p.b_scale_sm && p.N % 64 == 0 && p.seg[0].K % MD_KS == 0 && p.seg[0].K >= MD_KS &&
          (p.epi == EPI_SQRELU_HILO || p.epi == EPI_GATE_F32);
 }
 
+template <int W, int EPI>
+static hipError_t mid_attr() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mid_kernel<W, EPI>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, mid_lds_bytes<W>());
+}
+
+int gemm_mid_setup() {
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = mid_attr<8, EPI_SQRELU_HILO>();
+  if (e == hipSuccess) e = mid_attr<8, EPI_GATE_F32>();
+  if (e == hipSuccess) e = mid_attr<7, EPI_SQRELU_HILO>();
+  if (e == hipSuccess) e = mid_attr<7, EPI_GATE_F32>();
+  if (e == hipSuccess) e = mid_attr<4, EPI_SQRELU_HILO>();
+  if (e == hipSuccess) e = mid_attr<4, EPI_GATE_F32>();
+  return (int)e;
+}
+
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s) {
-  if (fp4) {
-    if (p.epi == EPI_SQRELU_HILO) mid_launch<true, MD_NT_FP4, EPI_SQRELU_HILO>(p, s);
-    else mid_launch<true, MD_NT_FP4, EPI_GATE_F32>(p, s);
-  } else {
-    if (p.epi == EPI_SQRELU_HILO) mid_launch<false, MD_NT_BF16, EPI_SQRELU_HILO>(p, s);
-    else mid_launch<false, MD_NT_BF16, EPI_GATE_F32>(p, s);
-  }
+  (void)fp4;
+  if (p.epi == EPI_SQRELU_HILO)
+    mid_launch_w<EPI_SQRELU_HILO>(p, s);
+  else
+    mid_launch_w<EPI_GATE_F32>(p, s);
+}
+
+// [E][N][K/16] -> [E][K/128][N][8]: one thread per 8-byte group
+__global__ void scale_stage_major_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                         long long groups, int N, int P) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // (e, n, s) row-major
+  if (i >= groups) return;
+  const int s = (int)(i % P);
+  const long long en = i / P;
+  const int n = (int)(en % N);
+  const long long e = en / N;
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src + 8 * i);
+  *reinterpret_cast<u32x2_t*>(dst + (((e * P + s) * N) + n) * 8) = v;
+}
+
+void launch_scale_stage_major(const uint8_t* src, uint8_t* dst, long long E, int N, int K,
+                              hipStream_t s) {
+  const int P = K / MD_KS;
+  const long long groups = E * N * P;
+  if (groups <= 0) return;
+  scale_stage_major_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(src, dst, groups, N, P);
 }
 
 }  // namespace lmoe

@@ -46,6 +46,7 @@ struct GemmParams {
   long long b_stride;       // elements between consecutive experts' B (FP4: elements, i.e. 2 per byte)
   // block-scaled FP4 B operand
   const uint8_t* b_scale;   // [E, N, ldb/16] E4M3FN
+  const uint8_t* b_scale_sm; // the same scales stage-major, [E, ldb/128, N, 8] (or null)
   const float* b_tscale;    // [E] fp32 applied to the accumulator (null => 1)
   // split-K
   int splits;
@@ -63,10 +64,15 @@ struct GemmParams {
 
 // weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes)
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
-// grouped MFMA GEMM for 64-row expert tiles with dual activations (tens of rows
-// per expert): activations through an LDS ring, weights read once per tile
+// grouped MFMA GEMM for 64-row expert tiles of block-scaled FP4 weights with dual
+// activations (tens of rows per expert): activations staged in LDS, weights read once
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s);
 bool gemm_mid_supports(const GemmParams& p, bool fp4);
+// one-time kernel attributes (dynamic LDS above 64 KB); returns a HIP error code
+int gemm_mid_setup();
+// FP4 block scales [E, N, K/16] -> stage-major [E, K/128, N, 8] (the mid kernel's order)
+void launch_scale_stage_major(const uint8_t* src, uint8_t* dst, long long E, int N, int K,
+                              hipStream_t s);
 // large-tile MFMA GEMM, 256 x 256 tiles (prefill-sized problems)
 void launch_gemm_big(const GemmParams& p, hipStream_t s);
 bool gemm_big_supports(int epi);

@@ -37,11 +37,11 @@ namespace {
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
 constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
+#ifndef LMOE_SERIAL
+#define LMOE_SERIAL 0  // 1: no side streams
+#endif
 #ifndef LMOE_MID_FP4
 #define LMOE_MID_FP4 1  // FP4 experts with 64-row tiles use the mid kernel
-#endif
-#ifndef LMOE_MID_BF16
-#define LMOE_MID_BF16 1  // bf16 experts with 64-row tiles use the mid kernel
 #endif
 #ifndef LMOE_TARGET_BLOCKS
 #define LMOE_TARGET_BLOCKS 256
@@ -102,6 +102,8 @@ struct Buffers {
   uint16_t* y_lat_lo = nullptr;
   uint16_t* hs_hi = nullptr;
   uint16_t* hs_lo = nullptr;
+  uint8_t* w1_scale_sm = nullptr;  // FP4: expert block scales in the mid kernel's stage-major order
+  uint8_t* w2_scale_sm = nullptr;
 };
 
 struct Layout {
@@ -185,6 +187,12 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
   L.add((void**)&b.hs_hi, Tm * c.shared_hidden * 2);
   L.add((void**)&b.hs_lo, Tm * c.shared_hidden * 2);
+  if (c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 && c.latent % 128 == 0 &&
+      c.expert_hidden % 128 == 0) {
+    const size_t sc_bytes = N * (size_t)c.expert_hidden * (c.latent / 16);  // same for both
+    L.add((void**)&b.w1_scale_sm, sc_bytes);
+    L.add((void**)&b.w2_scale_sm, sc_bytes);
+  }
   return L;
 }
 
@@ -337,9 +345,10 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_OUT_OF_MEMORY;
   }
   h->workspace_bytes = L.total;
-  if (gemm_big_setup() != 0) {
+  if (gemm_big_setup() != 0 ||
+      (cfg->expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 && gemm_mid_setup() != 0)) {
     (void)hipGetLastError();
-    hipFree(h->workspace);
+    (void)hipFree(h->workspace);
     delete h;
     return LATENTMOE_ERR_HIP;
   }
@@ -360,6 +369,12 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_HIP;
   }
   launch_router_split(w->router_w, h->b.pieces, (long long)cfg->n_experts * cfg->d, stream);
+  if (h->b.w1_scale_sm) {
+    launch_scale_stage_major(w->expert_w1_scale, h->b.w1_scale_sm, cfg->n_experts,
+                             cfg->expert_hidden, cfg->latent, stream);
+    launch_scale_stage_major(w->expert_w2_scale, h->b.w2_scale_sm, cfg->n_experts, cfg->latent,
+                             cfg->expert_hidden, stream);
+  }
   if (hipGetLastError() != hipSuccess) {
     latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
@@ -409,6 +424,9 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // weight stream fills the latency-bound top-K / bucketing chain.
   hipStream_t side = h->side;
   hipStream_t side2 = h->side2;
+#if LMOE_SERIAL
+  side = side2 = s;  // everything in one stream, in program order (per-stage profiling)
+#endif
   auto fork_to = [&](hipStream_t to, hipEvent_t ev) {
     (void)hipEventRecord(ev, s);
     (void)hipStreamWaitEvent(to, ev, 0);
@@ -532,7 +550,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   auto launch_expert = [&](const GemmParams& g) {
     if (!expert_stream)
       launch_gemm_big(g, s);
-    else if (rows_per_tile == STREAM_ROWS_BIG && (fp4 ? LMOE_MID_FP4 : LMOE_MID_BF16) && gemm_mid_supports(g, fp4))
+    else if (rows_per_tile == STREAM_ROWS_BIG && LMOE_MID_FP4 && gemm_mid_supports(g, fp4))
       launch_gemm_mid(g, fp4, s);
     else
       launch_gemm_stream(g, fp4, s);
@@ -549,6 +567,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pu.row_index = b.row_src;
   pu.b_stride = (long long)m * L;
   pu.b_scale = fp4 ? w.expert_w1_scale : nullptr;
+  pu.b_scale_sm = b.w1_scale_sm;
   pu.b_tscale = fp4 ? w.expert_w1_tscale : nullptr;
   pu.epi = EPI_SQRELU_HILO;
   pu.C = b.h;
@@ -568,6 +587,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pw.row_index = nullptr;
   pw.b_stride = (long long)L * m;
   pw.b_scale = fp4 ? w.expert_w2_scale : nullptr;
+  pw.b_scale_sm = b.w2_scale_sm;
   pw.b_tscale = fp4 ? w.expert_w2_tscale : nullptr;
   pw.epi = EPI_GATE_F32;
   pw.row_scale = b.row_gate;
