@@ -1,0 +1,113 @@
+"""Short text summaries of rocprofv3 CSV output (kernel traces and counter runs).
+
+    python -m sparse_moe_layer_logits_amd.rocprof_summary kt DIR [--top N]
+        per (kernel, grid size) group: calls, average / min / max duration
+
+    python -m sparse_moe_layer_logits_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \\
+            --kernel SUBSTR --grid G --probe-mib M --source-sha SHA --out FILE.json
+        HBM bytes per launch of one kernel group from a FETCH_SIZE run and a
+        WRITE_SIZE run.  Each counter is scaled by what it reads for the plain
+        copy launches of the same run (bench.py --copy-probe-mib M: M MiB read
+        and M MiB written per launch).
+
+DIR is the rocprofv3 output directory (-d) of a run with --output-format csv.
+"""
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import sys
+
+
+def _one(dir_, pattern):
+    files = sorted(glob.glob(os.path.join(dir_, "**", pattern), recursive=True))
+    if not files:
+        raise SystemExit("no %s under %s" % (pattern, dir_))
+    return files[0]
+
+
+def kernel_groups(dir_):
+    """(kernel name, grid size) -> list of durations in ns, from *kernel_trace.csv."""
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(_one(dir_, "*kernel_trace.csv"))):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups[(r["Kernel_Name"], grid)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return groups
+
+
+def cmd_kt(a):
+    groups = kernel_groups(a.dir)
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[: a.top]
+    print("| kernel | grid (threads) | calls | avg us | min us | max us | % time |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for (name, grid), v in rows:
+        print("| `%s` | %d | %d | %.1f | %.1f | %.1f | %.1f |" % (
+            name[:90], grid, len(v), sum(v) / len(v) / 1e3, min(v) / 1e3, max(v) / 1e3,
+            100.0 * sum(v) / total))
+
+
+def counter_per_dispatch(dir_, counter):
+    """(kernel name, grid size) -> list of per-dispatch values of one counter."""
+    out = collections.defaultdict(list)
+    for r in csv.DictReader(open(_one(dir_, "*counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            out[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(groups, kernel, grid):
+    hits = [(k, v) for k, v in groups.items() if kernel in k[0] and (grid is None or k[1] == grid)]
+    if len(hits) != 1:
+        raise SystemExit("kernel %r grid %s matches %d groups: %s" % (
+            kernel, grid, len(hits), [k for k, _ in hits][:8]))
+    return hits[0]
+
+
+def cmd_traffic(a):
+    probe_bytes = a.probe_mib * (1 << 20)
+    res = {}
+    for counter, dir_ in (("FETCH_SIZE", a.fetch_dir), ("WRITE_SIZE", a.write_dir)):
+        groups = counter_per_dispatch(dir_, counter)
+        (name, grid), vals = _pick(groups, a.kernel, a.grid)
+        # the copy probe: elementwise launches that move about probe_bytes each
+        probe = [v for (k, g), vs in groups.items() if "elementwise" in k
+                 for v in vs if probe_bytes / 4 < v * 1024 < probe_bytes * 4]
+        if not probe:
+            raise SystemExit("no copy-probe launches in %s" % dir_)
+        probe_kib = sorted(probe)[len(probe) // 2]
+        factor = probe_bytes / (probe_kib * 1024)
+        kib = sum(vals) / len(vals)
+        res[counter] = {"kib_per_launch": kib, "launches": len(vals), "probe_kib": probe_kib,
+                        "factor": factor, "bytes_per_launch": kib * 1024 * factor}
+        res["kernel_name"], res["grid"] = name, grid
+    res["hbm_bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
+    res["source_sha"] = a.source_sha
+    res["command"] = a.command
+    json.dump(res, open(a.out, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kt")
+    k.add_argument("dir")
+    k.add_argument("--top", type=int, default=20)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--grid", type=int, default=None)
+    t.add_argument("--probe-mib", type=int, required=True)
+    t.add_argument("--source-sha", required=True)
+    t.add_argument("--command", default="")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    {"kt": cmd_kt, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
