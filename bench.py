@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="super_decode")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch size T instead of the workload's (e.g. speculative-verify sweeps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain fp32 copy kernel of this size (counter calibration)")
@@ -137,8 +139,20 @@ def main():
     from sparse_moe_layer_logits_amd import binding, synth
 
     wl = synth.WORKLOADS[args.workload]
+    redraw_from = wl.name
+    if args.tokens:
+        # the same layer at another batch size: token rows are drawn per row, so
+        # a smaller T is a prefix of the batch; super_verify's redraw table
+        # covers the decode router up to 512 rows
+        import dataclasses
+        if args.tokens > wl.T and wl.name == "super_decode":
+            redraw_from = "super_verify"
+        elif args.tokens > wl.T:
+            raise SystemExit("--tokens above %d needs a workload whose batch has that many rows" % wl.T)
+        wl = dataclasses.replace(wl, T=args.tokens)
     t0 = time.time()
-    x, W = synth.make(wl, args.seed, redraws=synth.load_redraws(wl.name, args.seed))
+    redraws = {t: a for t, a in synth.load_redraws(redraw_from, args.seed).items() if t < wl.T}
+    x, W = synth.make(wl, args.seed, redraws=redraws)
     log("generated %s inputs in %.1fs" % (wl.name, time.time() - t0))
     torch.cuda.set_device(0)
     Wd = binding.upload_weights(W)
@@ -194,7 +208,8 @@ def main():
         achieved, peak, unit, bound = kb / dom_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
     else:
         achieved, peak, unit, bound = kf / dom_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
-    tr = stored_traffic(kernel, wl.name)
+    # counter data is stored for the workloads' own batch sizes only
+    tr = None if args.tokens else stored_traffic(kernel, wl.name)
     traffic = None if tr is None else tr["hbm_bytes_per_launch"]
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,

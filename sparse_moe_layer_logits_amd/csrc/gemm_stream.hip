@@ -267,28 +267,30 @@ static void launch_rows(const GemmParams& p, long long blocks, hipStream_t s) {
 }
 
 template <bool FP4, bool DUAL>
-static void launch_fmt(const GemmParams& p, bool small_rows, long long blocks, hipStream_t s) {
-  if (small_rows)
+static void launch_fmt(const GemmParams& p, int rows, long long blocks, hipStream_t s) {
+  if (rows == 16)
     launch_rows<16, LMOE_ST_PAIRS16, FP4, DUAL>(p, blocks, s);
+  else if (rows == 32)
+    launch_rows<32, DUAL ? 2 : 4, FP4, DUAL>(p, blocks, s);
   else
     launch_rows<64, DUAL ? 2 : 4, FP4, DUAL>(p, blocks, s);
 }
 
 void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s) {
   constexpr int W = LMOE_ST_W, NT = 1;
-  const bool small_rows = p.tile_expert && p.rows_per_tile <= 16;
+  // tile height: the grouped tile list's (16, 32 or 64 rows), 64 for dense GEMMs
+  const int rows = !p.tile_expert ? 64 : p.rows_per_tile <= 16 ? 16 : p.rows_per_tile <= 32 ? 32 : 64;
   const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
-  const int rows_per_tile = small_rows ? 16 : 64;
-  const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows_per_tile - 1) / rows_per_tile;
+  const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows - 1) / rows;
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
   const bool dual = p.a_lo != nullptr;
   if (fp4) {
-    if (dual) launch_fmt<true, true>(p, small_rows, blocks, s);
-    else launch_fmt<true, false>(p, small_rows, blocks, s);
+    if (dual) launch_fmt<true, true>(p, rows, blocks, s);
+    else launch_fmt<true, false>(p, rows, blocks, s);
   } else {
-    if (dual) launch_fmt<false, true>(p, small_rows, blocks, s);
-    else launch_fmt<false, false>(p, small_rows, blocks, s);
+    if (dual) launch_fmt<false, true>(p, rows, blocks, s);
+    else launch_fmt<false, false>(p, rows, blocks, s);
   }
 }
 

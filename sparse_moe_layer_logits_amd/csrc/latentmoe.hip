@@ -36,6 +36,13 @@ namespace {
 
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
+constexpr int STREAM_ROWS_MID = 32;
+#ifndef LMOE_ROWS16_MAX_AVG
+#define LMOE_ROWS16_MAX_AVG 12.0  // up to this many rows per expert on average: 16-row tiles
+#endif
+#ifndef LMOE_ROWS32_MAX_AVG
+#define LMOE_ROWS32_MAX_AVG 24.0  // then up to this many: 32-row tiles, above: 64
+#endif
 constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
 #ifndef LMOE_SERIAL
 #define LMOE_SERIAL 0  // 1: no side streams
@@ -516,7 +523,10 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const double avg_rows = (double)TK / N;
   const bool expert_stream = fp4 || avg_rows <= 48.0;
   const int rows_per_tile =
-      expert_stream ? (avg_rows <= 8.0 ? STREAM_ROWS_SMALL : STREAM_ROWS_BIG) : TILE_ROWS;
+      !expert_stream                   ? TILE_ROWS
+      : avg_rows <= LMOE_ROWS16_MAX_AVG ? STREAM_ROWS_SMALL
+      : avg_rows <= LMOE_ROWS32_MAX_AVG ? STREAM_ROWS_MID
+                                        : STREAM_ROWS_BIG;
   const int max_tiles = ceil_div(TK, rows_per_tile) + (int)std::min<long long>(N, TK);
   tm.start(LATENTMOE_STAGE_BUCKET);
   const bool fuse_place = TK <= 8192;  // one workgroup places a few thousand rows quickly

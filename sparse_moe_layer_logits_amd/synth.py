@@ -69,6 +69,10 @@ WORKLOADS = {
     # Ultra expert shapes (Nemotron 3 Ultra, method section); d and ell chosen here
     "ultra": Workload("ultra", T=256, d=8192, latent=2048, n_experts=512, top_k=22,
                       expert_hidden=5120, shared_hidden=10240),
+    # Super decode shapes at the speculative-verify batch sizes: T = users x 8
+    # (a draft of 7 plus the verified token); smaller T are prefixes of this batch
+    "super_verify": Workload("super_verify", T=512, d=4096, latent=1024, n_experts=512,
+                             top_k=22, expert_hidden=2688, shared_hidden=5376),
     # Super shapes with block-scaled FP4 expert weights
     "super_fp4": Workload("super_fp4", T=1024, d=4096, latent=1024, n_experts=512,
                           top_k=22, expert_hidden=2688, shared_hidden=5376,

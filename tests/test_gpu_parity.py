@@ -10,7 +10,7 @@ import pytest
 import oracle
 from sparse_moe_layer_logits_amd import binding, synth
 
-from gpu_common import full_check, log, run_layer, sampled_check
+from gpu_common import check_bucketing, check_topk, check_y, full_check, log, run_layer, sampled_check
 
 pytestmark = pytest.mark.gpu
 
@@ -88,11 +88,34 @@ def test_tiled_path():
 
 
 def test_mid_rows_stream_path():
-    # 8 < rows per expert <= 48: 64-row streaming tiles, some experts span two tiles
-    wl = small_wl(T=200, d=256, latent=64, n_experts=32, top_k=4, expert_hidden=128, shared_hidden=256)
+    # 24 < rows per expert <= 48: 64-row streaming tiles, some experts span two tiles
+    wl = small_wl(T=240, d=256, latent=64, n_experts=32, top_k=4, expert_hidden=128, shared_hidden=256)
     x, W = gen(wl, 5)
     log("64-row stream tiles", wl)
     full_check(wl, x, W)
+
+
+def test_rows32_stream_path():
+    # 12 < rows per expert <= 24: 32-row streaming tiles, bf16 and FP4 experts
+    wl = small_wl(T=160, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=192, shared_hidden=256)
+    x, W = gen(wl, 13)
+    log("32-row stream tiles", wl)
+    full_check(wl, x, W)
+    wl4 = small_wl(T=160, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=192,
+                   shared_hidden=256, experts="fp4")
+    x4, W4 = gen(wl4, 14)
+    full_check(wl4, x4, W4, tol=3e-2)
+
+
+def test_fp4_mid_kernel_small():
+    # FP4 experts, 24 < rows per expert <= 48: the LDS-staged FP4 kernel; up-proj
+    # N = 512 runs 8-wave blocks, down-proj N = 128 4-wave blocks with two waves
+    # past N; K = 128 is a single stage
+    wl = small_wl(T=240, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=512,
+                  shared_hidden=256, experts="fp4")
+    x, W = gen(wl, 15)
+    log("FP4 mid kernel", wl)
+    full_check(wl, x, W, tol=3e-2)
 
 
 def test_k_equals_n():
@@ -197,4 +220,45 @@ def test_graph_replay_matches_eager_and_oracle():
         torch.cuda.synchronize()
         ref = oracle.forward(xa[:T], W, wl.top_k)
         assert np.max(np.abs(y2.cpu().numpy() - ref["y"])) <= 1e-2 * np.sqrt(np.mean(ref["y"] ** 2))
+    layer.close()
+
+
+def test_super_verify_sweep():
+    """Speculative-verify decode batches at Super shapes, T = users x 8 from 8 to
+    512 (prefixes of one 512-token batch; the 16- and 64-row expert tiles):
+    every token's top-K, exact bucketing, sampled outputs, eager and graph."""
+    import torch
+    wl = synth.WORKLOADS["super_verify"]
+    x, W = synth.make(wl, 0, redraws=synth.load_redraws("super_verify", 0))
+    logits = oracle.router_logits(x, W["router_w"], W["router_bias"])
+    assert np.all(oracle.topk_gap(logits, wl.top_k) >= 1e-4)
+    ref_idx = oracle.select_topk(logits, wl.top_k)
+    ref_g = oracle.softmax_selected(logits, ref_idx)
+    Ts = (8, 16, 24, 40, 64, 128, 256, 512)
+    # a token's output does not depend on the batch it is in: one oracle pass
+    samples = {T: np.unique(np.linspace(0, T - 1, 5).astype(int)) for T in Ts}
+    toks = np.unique(np.concatenate(list(samples.values())))
+    ref = oracle.forward(x, W, wl.top_k, tokens=toks)
+    ref_y = dict(zip(toks.tolist(), ref["y"]))
+    log("verify sweep: oracle on %d tokens done" % len(toks))
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    K, L = wl.top_k, wl.latent
+    for T in Ts:
+        for graph in (False, True):
+            y, idx, g = layer.forward(xd[:T], graph=graph)
+            counts = layer.intermediate("counts", (wl.n_experts,), torch.int32)
+            offsets = layer.intermediate("offsets", (wl.n_experts + 1,), torch.int32)
+            row_src = layer.intermediate("row_src", (T * K,), torch.int32)
+            inv = layer.intermediate("inv", (T * K,), torch.int32)
+            torch.cuda.synchronize()
+            idx_h = idx.cpu().numpy()
+            check_topk(idx_h, g.cpu().numpy(), ref_idx[:T], ref_g[:T])
+            check_bucketing(dict(counts=counts.cpu().numpy(), offsets=offsets.cpu().numpy(),
+                                 row_src=row_src.cpu().numpy(), inv=inv.cpu().numpy()),
+                            idx_h, wl.n_experts, K)
+            s = samples[T]
+            check_y(y.cpu().numpy().astype(np.float64)[s], np.stack([ref_y[t] for t in s.tolist()]), 1e-2)
+            log("verify sweep: T=%d graph=%s ok" % (T, graph))
     layer.close()
