@@ -147,6 +147,12 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
  *   LATENTMOE_INTER_HS_LO    [T, m_s] bf16     shared hidden, remainder
  *   LATENTMOE_INTER_Z_LO     [T, l] bf16       latent tokens, remainder
  *   LATENTMOE_INTER_H_LO     [T*K, m] bf16     expert hidden, remainder
+ * Permuted order: the rows of expert e are [OFFSETS[e], OFFSETS[e+1]), sorted
+ * by token.  When the layer runs its large-tile path (bf16 experts and more
+ * than 48 routed rows per expert on average, T*K/N > 48), the rows of each
+ * expert whose gate is at least 0.1 come first (sorted by token), then the
+ * others (sorted by token): only the first group carries z and h as hi + lo
+ * pairs, the others as bf16 (H_LO is not written for them).
  * Errors: INVALID_ARG for an unknown `which`, a null pointer or more bytes
  * than the intermediate holds. */
 #define LATENTMOE_INTER_Z 0

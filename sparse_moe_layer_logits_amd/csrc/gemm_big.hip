@@ -76,10 +76,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
   const int split = item % p.splits;
   item /= p.splits;
   const int q = item % NQ;
-  const int j = item / NQ;
+  int j = item / NQ;
   int expert = 0, row0, rows;
   if (p.tile_expert) {
     if (j >= p.n_tiles[0]) return;
+    if (p.tile_first) j += p.tile_first[0];
     expert = p.tile_expert[j];
     row0 = p.tile_row0[j];
     rows = p.tile_rows[j];
@@ -217,6 +218,7 @@ static void big_for_each_epi(int epi, F&& f) {
     case EPI_PARTIAL: f(std::integral_constant<int, EPI_PARTIAL>{}); break;
     case EPI_BF16_HILO: f(std::integral_constant<int, EPI_BF16_HILO>{}); break;
     case EPI_SQRELU_HILO: f(std::integral_constant<int, EPI_SQRELU_HILO>{}); break;
+    case EPI_SQRELU_BF16: f(std::integral_constant<int, EPI_SQRELU_BF16>{}); break;
     case EPI_F32: f(std::integral_constant<int, EPI_F32>{}); break;
     case EPI_F32_ADD: f(std::integral_constant<int, EPI_F32_ADD>{}); break;
     case EPI_GATE_F32: f(std::integral_constant<int, EPI_GATE_F32>{}); break;
@@ -225,7 +227,8 @@ static void big_for_each_epi(int epi, F&& f) {
 }
 
 int gemm_big_setup() {
-  const int kinds[] = {EPI_PARTIAL, EPI_BF16_HILO, EPI_SQRELU_HILO, EPI_F32, EPI_F32_ADD, EPI_GATE_F32};
+  const int kinds[] = {EPI_PARTIAL, EPI_BF16_HILO, EPI_SQRELU_HILO, EPI_SQRELU_BF16,
+                       EPI_F32, EPI_F32_ADD, EPI_GATE_F32};
   hipError_t e = hipSuccess;
   for (int k : kinds) {
     big_for_each_epi(k, [&](auto E) {
@@ -237,8 +240,8 @@ int gemm_big_setup() {
 }
 
 bool gemm_big_supports(int epi) {
-  return epi == EPI_PARTIAL || epi == EPI_BF16_HILO || epi == EPI_SQRELU_HILO || epi == EPI_F32 ||
-         epi == EPI_F32_ADD || epi == EPI_GATE_F32;
+  return epi == EPI_PARTIAL || epi == EPI_BF16_HILO || epi == EPI_SQRELU_HILO ||
+         epi == EPI_SQRELU_BF16 || epi == EPI_F32 || epi == EPI_F32_ADD || epi == EPI_GATE_F32;
 }
 
 void launch_gemm_big(const GemmParams& p, hipStream_t s) {

@@ -40,6 +40,7 @@ struct GemmParams {
   const int* tile_row0;     // first (permuted) row of the tile
   const int* tile_rows;     // rows in the tile
   const int* n_tiles;       // number of valid tiles (device scalar)
+  const int* tile_first;    // first tile of this launch in the tile list (device scalar) or null
   int max_tiles;            // launch bound on tiles
   int rows_per_tile;        // tile height the tile list was built for (grouped mode)
   const int* row_index;     // A row of permuted row p (null => A row = p)
@@ -85,19 +86,24 @@ void launch_reduce(const GemmParams& p, hipStream_t s);
 void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStream_t s);
 
 // per-token top-K + softmax over logits [T, N] (+ bias); builds per-16-token expert masks
+// (masks_hi, if not null: the routed rows whose gate is at least hi_tau)
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
-                 float* gates, uint32_t* masks, hipStream_t s);
+                 float* gates, uint32_t* masks, float hi_tau, uint32_t* masks_hi, hipStream_t s);
 // counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile);
-// with place_idx set it also does launch_place's work in the same workgroup (small T)
-void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
-                        int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
+// with masks_hi the rows of each expert are split into the hi class (first) and the rest,
+// hi tiles first in the list: n_tiles[0] hi tiles, then n_tiles[1] others.  With place_idx
+// set it also does launch_place's work in the same workgroup (small T)
+void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, int N,
+                        int tile_rows_max, int* counts, int* counts_hi, int* offsets,
+                        int* prefix_hi, int* prefix_lo, int* tile_expert, int* tile_row0,
                         int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
                         const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
                         hipStream_t s);
 // permuted positions: row_src[p] = token, row_gate[p] = gate, inv[t*K+k] = p
-void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
-                  const int* block_prefix, int T, int N, int K, int* row_src, float* row_gate,
-                  int* inv, hipStream_t s);
+void launch_place(const int* idx, const float* gates, const uint32_t* masks,
+                  const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
+                  const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
+                  float* row_gate, int* inv, hipStream_t s);
 // y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo
 void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
                     uint16_t* y_lat_lo, hipStream_t s);

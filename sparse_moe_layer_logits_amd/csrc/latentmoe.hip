@@ -44,6 +44,14 @@ constexpr int STREAM_ROWS_MID = 32;
 #define LMOE_ROWS32_MAX_AVG 24.0  // then up to this many: 32-row tiles, above: 64
 #endif
 constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
+#ifndef LMOE_HI_TAU
+// Large-tile path (prefill): routed rows whose gate is at least this carry
+// their activations as bf16 hi + lo; the others as bf16.  A row's rounding
+// reaches the output multiplied by its gate, so the small-gate rows add little
+// error (fp64 emulation of the rounding points: max |y - y_exact| rises from
+// 1e-5 to 2.6e-3 rms with a uniform router, stays 1e-5 with the skewed one).
+#define LMOE_HI_TAU 0.1
+#endif
 #ifndef LMOE_SERIAL
 #define LMOE_SERIAL 0  // 1: no side streams
 #endif
@@ -89,7 +97,10 @@ struct Buffers {
   int* idx = nullptr;
   float* gates = nullptr;
   uint32_t* masks = nullptr;
-  int* block_prefix = nullptr;
+  uint32_t* masks_hi = nullptr;  // rows whose gate reaches LMOE_HI_TAU (large-tile path)
+  int* block_prefix = nullptr;   // per (block, expert) prefix of the (hi-class) rows
+  int* prefix_lo = nullptr;      // the same for the other rows
+  int* counts_hi = nullptr;
   int* counts = nullptr;
   int* offsets = nullptr;
   int* tile_expert = nullptr;
@@ -166,7 +177,8 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   const size_t TK = Tm * K;
   const size_t nblk = (Tm + 15) / 16;
   b.partial_cap = max_partial_floats(c);
-  b.max_tiles_cap = (int)(ceil_div(TK, STREAM_ROWS_SMALL) + std::min(N, TK));
+  // every expert may end in one partial tile per row class
+  b.max_tiles_cap = (int)(ceil_div(TK, STREAM_ROWS_SMALL) + 2 * std::min(N, TK));
   L.add((void**)&b.pieces, 3 * N * c.d * 2);
   L.add((void**)&b.logits, Tm * N * 4);
   L.add((void**)&b.partial, b.partial_cap * 4);
@@ -175,13 +187,16 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.idx, TK * 4);
   L.add((void**)&b.gates, TK * 4);
   L.add((void**)&b.masks, nblk * N * 4);
+  L.add((void**)&b.masks_hi, nblk * N * 4);
   L.add((void**)&b.block_prefix, nblk * N * 4);
+  L.add((void**)&b.prefix_lo, nblk * N * 4);
+  L.add((void**)&b.counts_hi, N * 4);
   L.add((void**)&b.counts, N * 4);
   L.add((void**)&b.offsets, (N + 1) * 4);
   L.add((void**)&b.tile_expert, (size_t)b.max_tiles_cap * 4);
   L.add((void**)&b.tile_row0, (size_t)b.max_tiles_cap * 4);
   L.add((void**)&b.tile_rows, (size_t)b.max_tiles_cap * 4);
-  L.add((void**)&b.n_tiles, 4);
+  L.add((void**)&b.n_tiles, 2 * 4);
   L.add((void**)&b.row_src, TK * 4);
   L.add((void**)&b.row_gate, TK * 4);
   L.add((void**)&b.inv, TK * 4);
@@ -516,26 +531,32 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_TOPK);
   int* idx_buf = topk_idx ? topk_idx : b.idx;  // written in place when the caller asks
   float* gate_buf = topk_gate ? topk_gate : b.gates;
-  launch_topk(b.logits, w.router_bias, T, N, K, idx_buf, gate_buf, b.masks, s);
+  const double avg_rows = (double)TK / N;
+  const bool expert_stream = fp4 || avg_rows <= 48.0;
+  // large-tile path: rows split by gate into a hi + lo class and a bf16 class
+  const bool split_rows = !expert_stream && LMOE_HI_TAU > 0;
+  uint32_t* masks_hi = split_rows ? b.masks_hi : nullptr;
+  launch_topk(b.logits, w.router_bias, T, N, K, idx_buf, gate_buf, b.masks, (float)LMOE_HI_TAU,
+              masks_hi, s);
   tm.stop(LATENTMOE_STAGE_TOPK);
 
   // ---- 3. bucketing ----
-  const double avg_rows = (double)TK / N;
-  const bool expert_stream = fp4 || avg_rows <= 48.0;
   const int rows_per_tile =
       !expert_stream                   ? TILE_ROWS
       : avg_rows <= LMOE_ROWS16_MAX_AVG ? STREAM_ROWS_SMALL
       : avg_rows <= LMOE_ROWS32_MAX_AVG ? STREAM_ROWS_MID
                                         : STREAM_ROWS_BIG;
-  const int max_tiles = ceil_div(TK, rows_per_tile) + (int)std::min<long long>(N, TK);
+  const int max_tiles =
+      ceil_div(TK, rows_per_tile) + (split_rows ? 2 : 1) * (int)std::min<long long>(N, TK);
   tm.start(LATENTMOE_STAGE_BUCKET);
   const bool fuse_place = TK <= 8192;  // one workgroup places a few thousand rows quickly
-  launch_bucket_scan(b.masks, T, N, rows_per_tile, b.counts, b.offsets, b.block_prefix,
-                     b.tile_expert, b.tile_row0, b.tile_rows, b.n_tiles, max_tiles,
-                     fuse_place ? idx_buf : nullptr, gate_buf, K, b.row_src, b.row_gate, b.inv, s);
+  launch_bucket_scan(b.masks, masks_hi, T, N, rows_per_tile, b.counts, b.counts_hi, b.offsets,
+                     b.block_prefix, b.prefix_lo, b.tile_expert, b.tile_row0, b.tile_rows,
+                     b.n_tiles, max_tiles, fuse_place ? idx_buf : nullptr, gate_buf, K, b.row_src,
+                     b.row_gate, b.inv, s);
   if (!fuse_place)
-    launch_place(idx_buf, gate_buf, b.masks, b.offsets, b.block_prefix, T, N, K, b.row_src,
-                 b.row_gate, b.inv, s);
+    launch_place(idx_buf, gate_buf, b.masks, masks_hi, b.offsets, b.counts_hi, b.block_prefix,
+                 b.prefix_lo, T, N, K, b.row_src, b.row_gate, b.inv, s);
   tm.stop(LATENTMOE_STAGE_BUCKET);
 #if LMOE_SHARED_FORK_AT == 2
   fork_to(side, h->ev_fork2);
@@ -557,8 +578,18 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pe.M = rows_per_tile;
   pe.splits = 1;
 
-  auto launch_expert = [&](const GemmParams& g) {
-    if (!expert_stream)
+  // epi_lo: the epilogue of the bf16-class launch (split rows)
+  auto launch_expert = [&](const GemmParams& g, int epi_lo) {
+    if (split_rows) {
+      launch_gemm_big(g, s);  // hi tiles: tiles [0, n_tiles[0])
+      GemmParams gl = g;      // then tiles [n_tiles[0], n_tiles[0] + n_tiles[1]), one part
+      gl.n_tiles = b.n_tiles + 1;
+      gl.tile_first = b.n_tiles;
+      gl.a_lo = nullptr;
+      gl.epi = epi_lo;
+      gl.C2 = nullptr;
+      launch_gemm_big(gl, s);
+    } else if (!expert_stream)
       launch_gemm_big(g, s);
     else if (rows_per_tile == STREAM_ROWS_BIG && LMOE_MID_FP4 && gemm_mid_supports(g, fp4))
       launch_gemm_mid(g, fp4, s);
@@ -583,7 +614,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pu.C = b.h;
   pu.C2 = b.h_lo;
   pu.ldc = m;
-  launch_expert(pu);
+  launch_expert(pu, EPI_SQRELU_BF16);
   tm.stop(LATENTMOE_STAGE_EXPERT_UP);
 
   tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
@@ -603,7 +634,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pw.row_scale = b.row_gate;
   pw.C = b.og;
   pw.ldc = L;
-  launch_expert(pw);
+  launch_expert(pw, EPI_GATE_F32);
   tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
 
   // ---- 7. combine ----

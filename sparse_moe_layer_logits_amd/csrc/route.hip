@@ -8,6 +8,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace lmoe {
 
 // ---------------------------------------------------------------------------
@@ -66,13 +68,15 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
                                                     const float* __restrict__ bias, int T, int N,
                                                     int K, int* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
-                                                    uint32_t* __restrict__ masks) {
+                                                    uint32_t* __restrict__ masks, float hi_tau,
+                                                    uint32_t* __restrict__ masks_hi) {
   __shared__ uint32_t smask[1024];
+  __shared__ uint32_t smask_hi[1024];
   __shared__ unsigned long long cand[TOPK_TOKENS_PER_BLOCK][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * TOPK_TOKENS_PER_BLOCK + w;
-  for (int e = threadIdx.x; e < N; e += blockDim.x) smask[e] = 0u;
+  for (int e = threadIdx.x; e < N; e += blockDim.x) smask[e] = smask_hi[e] = 0u;
   __syncthreads();
 
   if (t < T) {
@@ -129,28 +133,40 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
     if (lane < K) {
       const int e = (int)(~(uint32_t)mine);
       idx_out[(long long)t * K + rank] = e;
-      gate_out[(long long)t * K + rank] = ex / tot;
+      const float gate = ex / tot;
+      gate_out[(long long)t * K + rank] = gate;
       atomicOr(&smask[e], 1u << w);
+      if (gate >= hi_tau) atomicOr(&smask_hi[e], 1u << w);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += blockDim.x) masks[(long long)blockIdx.x * N + e] = smask[e];
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    masks[(long long)blockIdx.x * N + e] = smask[e];
+    if (masks_hi) masks_hi[(long long)blockIdx.x * N + e] = smask_hi[e];
+  }
 }
 
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
-                 float* gates, uint32_t* masks, hipStream_t s) {
+                 float* gates, uint32_t* masks, float hi_tau, uint32_t* masks_hi, hipStream_t s) {
   const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
   if (N <= 512)
-    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates, masks);
+    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates,
+                                                                masks, hi_tau, masks_hi);
   else
-    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates, masks);
+    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates,
+                                                                 masks, hi_tau, masks_hi);
 }
 
 // ---------------------------------------------------------------------------
-// bucketing.  Permuted order is (expert, token): rows of expert e occupy
-// [offsets[e], offsets[e+1]) sorted by token.  The rank of token t inside
-// expert e is a prefix over 16-token blocks plus a popcount inside the block,
-// so the order is deterministic.  One workgroup, thread e owns expert e.
+// bucketing.  Permuted order is (expert, class, token): rows of expert e occupy
+// [offsets[e], offsets[e+1]); with a second mask (rows whose gate reaches a
+// threshold: the "hi" class) those rows come first, each class sorted by
+// token, and every tile holds rows of one class; hi tiles of all experts come
+// first in the tile list (n_tiles[0] of them), then the other tiles
+// (n_tiles[1]).  Without the second mask every row is in the hi class.  The
+// rank of token t inside its class is a prefix over 16-token blocks plus a
+// popcount inside the block, so the order is deterministic.  One workgroup,
+// thread e owns expert e.
 // ---------------------------------------------------------------------------
 struct PlaceArgs {  // fused placement (small T): see place_kernel
   const int* idx;
@@ -161,120 +177,180 @@ struct PlaceArgs {  // fused placement (small T): see place_kernel
   int* inv;
 };
 
+struct BucketMasks {
+  const uint32_t* all;      // [nblk, N] rows of each expert per 16-token block
+  const uint32_t* hi;       // [nblk, N] the hi-class subset, or null (all rows are hi)
+  int* prefix_hi;           // [nblk, N] hi rows of expert e in blocks before b
+  int* prefix_lo;           // [nblk, N] the other rows likewise (used with hi)
+  int* counts_hi;           // [N]
+};
+
 __device__ __forceinline__ void place_one(long long i, const int* __restrict__ idx,
-                                          const float* __restrict__ gates,
-                                          const uint32_t* __restrict__ masks,
-                                          const int* __restrict__ offsets,
-                                          const int* __restrict__ block_prefix, int N, int K,
+                                          const float* __restrict__ gates, const BucketMasks& bm,
+                                          const int* __restrict__ offsets, int N, int K,
                                           int* __restrict__ row_src, float* __restrict__ row_gate,
                                           int* __restrict__ inv) {
   const int t = (int)(i / K);
   const int e = idx[i];
   const int b = t / TOPK_TOKENS_PER_BLOCK;
   const int tl = t % TOPK_TOKENS_PER_BLOCK;
-  const uint32_t m = masks[(long long)b * N + e];
-  const int pos = offsets[e] + block_prefix[(long long)b * N + e] + __popc(m & ((1u << tl) - 1u));
+  const long long be = (long long)b * N + e;
+  const uint32_t below = (1u << tl) - 1u;
+  const uint32_t m = bm.all[be];
+  int pos;
+  if (!bm.hi) {
+    pos = offsets[e] + bm.prefix_hi[be] + __popc(m & below);
+  } else {
+    const uint32_t mh = bm.hi[be];
+    if ((mh >> tl) & 1u)
+      pos = offsets[e] + bm.prefix_hi[be] + __popc(mh & below);
+    else
+      pos = offsets[e] + bm.counts_hi[e] + bm.prefix_lo[be] + __popc(m & ~mh & below);
+  }
   row_src[pos] = t;
   row_gate[pos] = gates[i];
   inv[i] = pos;
 }
 
+template <bool HI>
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(
-    const uint32_t* __restrict__ masks, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
-    int* __restrict__ offsets, int* __restrict__ block_prefix, int* __restrict__ tile_expert,
-    int* __restrict__ tile_row0, int* __restrict__ tile_rows, int* __restrict__ n_tiles,
-    int max_tiles, PlaceArgs pa) {
+    BucketMasks bm, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ tile_expert, int* __restrict__ tile_row0,
+    int* __restrict__ tile_rows, int* __restrict__ n_tiles, int max_tiles, PlaceArgs pa) {
   __shared__ int scan_a[1024];
   __shared__ int scan_b[1024];
+  __shared__ int scan_c[1024];
   const int e = threadIdx.x;
-  int run = 0;
+  int run_hi = 0, run_lo = 0;
   if (e < N) {
+    // U blocks of masks in flight per step (16, then 4, then 1): the loads do
+    // not wait on the prefix
     int b = 0;
-    for (; b + 4 <= nblk; b += 4) {
-      uint32_t m0 = masks[(long long)(b + 0) * N + e];
-      uint32_t m1 = masks[(long long)(b + 1) * N + e];
-      uint32_t m2 = masks[(long long)(b + 2) * N + e];
-      uint32_t m3 = masks[(long long)(b + 3) * N + e];
-      block_prefix[(long long)(b + 0) * N + e] = run; run += __popc(m0);
-      block_prefix[(long long)(b + 1) * N + e] = run; run += __popc(m1);
-      block_prefix[(long long)(b + 2) * N + e] = run; run += __popc(m2);
-      block_prefix[(long long)(b + 3) * N + e] = run; run += __popc(m3);
-    }
-    for (; b < nblk; ++b) {
-      uint32_t m = masks[(long long)b * N + e];
-      block_prefix[(long long)b * N + e] = run;
-      run += __popc(m);
-    }
-    counts[e] = run;
+    auto steps = [&](auto UC, int b_end) {
+      constexpr int U = decltype(UC)::value;
+      for (; b + U <= b_end; b += U) {
+        uint32_t m[U], mh[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          m[u] = bm.all[(long long)(b + u) * N + e];
+          if constexpr (HI) mh[u] = bm.hi[(long long)(b + u) * N + e];
+          else mh[u] = m[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const long long be = (long long)(b + u) * N + e;
+          bm.prefix_hi[be] = run_hi;
+          run_hi += __popc(mh[u]);
+          if constexpr (HI) {
+            bm.prefix_lo[be] = run_lo;
+            run_lo += __popc(m[u] & ~mh[u]);
+          }
+        }
+      }
+    };
+    steps(std::integral_constant<int, 16>{}, nblk);
+    steps(std::integral_constant<int, 4>{}, nblk);
+    steps(std::integral_constant<int, 1>{}, nblk);
+    if constexpr (HI) bm.counts_hi[e] = run_hi;
+    counts[e] = run_hi + run_lo;
   }
-  const int ntile_e = (e < N) ? (run + tile_rows_max - 1) / tile_rows_max : 0;
-  // two inclusive scans at once (rows and tiles), Hillis-Steele over the block
-  scan_a[e] = (e < N) ? run : 0;
-  scan_b[e] = ntile_e;
+  const int run = run_hi + run_lo;
+  const int nt_hi = (e < N) ? (run_hi + tile_rows_max - 1) / tile_rows_max : 0;
+  const int nt_lo = (e < N) ? (run_lo + tile_rows_max - 1) / tile_rows_max : 0;
+  // inclusive scans at once (rows, hi tiles, other tiles), Hillis-Steele
+  scan_a[e] = run;
+  scan_b[e] = nt_hi;
+  if constexpr (HI) scan_c[e] = nt_lo;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int a = scan_a[e], bb = scan_b[e];
-    if (e >= off) { a += scan_a[e - off]; bb += scan_b[e - off]; }
+    int a = scan_a[e], bb = scan_b[e], c = 0;
+    if constexpr (HI) c = scan_c[e];
+    if (e >= off) {
+      a += scan_a[e - off];
+      bb += scan_b[e - off];
+      if constexpr (HI) c += scan_c[e - off];
+    }
     __syncthreads();
     scan_a[e] = a;
     scan_b[e] = bb;
+    if constexpr (HI) scan_c[e] = c;
     __syncthreads();
   }
-  const int row_start = scan_a[e] - ((e < N) ? run : 0);
-  const int tile_start = scan_b[e] - ntile_e;
+  const int row_start = scan_a[e] - run;
+  const int total_hi = scan_b[1023];
+  const int hi_start = scan_b[e] - nt_hi;
+  const int lo_start = HI ? total_hi + scan_c[e] - nt_lo : 0;
+  const int total_lo = HI ? scan_c[1023] : 0;
   if (e < N) {
     offsets[e] = row_start;
-    for (int i = 0; i < ntile_e; ++i) {
-      const int j = tile_start + i;
+    for (int i = 0; i < nt_hi; ++i) {
+      const int j = hi_start + i;
       if (j < max_tiles) {
         tile_expert[j] = e;
         tile_row0[j] = row_start + i * tile_rows_max;
-        tile_rows[j] = min(tile_rows_max, run - i * tile_rows_max);
+        tile_rows[j] = min(tile_rows_max, run_hi - i * tile_rows_max);
+      }
+    }
+    for (int i = 0; HI && i < nt_lo; ++i) {
+      const int j = lo_start + i;
+      if (j < max_tiles) {
+        tile_expert[j] = e;
+        tile_row0[j] = row_start + run_hi + i * tile_rows_max;
+        tile_rows[j] = min(tile_rows_max, run_lo - i * tile_rows_max);
       }
     }
   }
   if (e == 0) {
     offsets[N] = scan_a[1023];
-    n_tiles[0] = min(scan_b[1023], max_tiles);
+    const int nh = min(total_hi, max_tiles);
+    n_tiles[0] = nh;                                        // hi tiles: [0, n_tiles[0])
+    n_tiles[1] = min(total_hi + total_lo, max_tiles) - nh;  // then n_tiles[1] others
   }
   if (pa.idx) {  // small T: the same workgroup places every (token, k)
     __syncthreads();
     const long long n = (long long)pa.T * pa.K;
     for (long long i = threadIdx.x; i < n; i += blockDim.x)
-      place_one(i, pa.idx, pa.gates, masks, offsets, block_prefix, N, pa.K, pa.row_src, pa.row_gate,
-                pa.inv);
+      place_one(i, pa.idx, pa.gates, bm, offsets, N, pa.K, pa.row_src, pa.row_gate, pa.inv);
   }
 }
 
-void launch_bucket_scan(const uint32_t* masks, int T, int N, int tile_rows_max, int* counts,
-                        int* offsets, int* block_prefix, int* tile_expert, int* tile_row0,
+void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, int N,
+                        int tile_rows_max, int* counts, int* counts_hi, int* offsets,
+                        int* prefix_hi, int* prefix_lo, int* tile_expert, int* tile_row0,
                         int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
                         const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
                         hipStream_t s) {
   const int nblk = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
   PlaceArgs pa{place_idx, place_gates, T, K, row_src, row_gate, inv};
-  bucket_scan_kernel<<<1, 1024, 0, s>>>(masks, nblk, N, tile_rows_max, counts, offsets,
-                                        block_prefix, tile_expert, tile_row0, tile_rows, n_tiles,
-                                        max_tiles, pa);
+  BucketMasks bm{masks, masks_hi, prefix_hi, prefix_lo, counts_hi};
+  if (masks_hi)
+    bucket_scan_kernel<true><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
+                                                tile_expert, tile_row0, tile_rows, n_tiles,
+                                                max_tiles, pa);
+  else
+    bucket_scan_kernel<false><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
+                                                 tile_expert, tile_row0, tile_rows, n_tiles,
+                                                 max_tiles, pa);
 }
 
 __global__ void place_kernel(const int* __restrict__ idx, const float* __restrict__ gates,
-                             const uint32_t* __restrict__ masks, const int* __restrict__ offsets,
-                             const int* __restrict__ block_prefix, int T, int N, int K,
+                             BucketMasks bm, const int* __restrict__ offsets, int T, int N, int K,
                              int* __restrict__ row_src, float* __restrict__ row_gate,
                              int* __restrict__ inv) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)T * K) return;
-  place_one(i, idx, gates, masks, offsets, block_prefix, N, K, row_src, row_gate, inv);
+  place_one(i, idx, gates, bm, offsets, N, K, row_src, row_gate, inv);
 }
 
-void launch_place(const int* idx, const float* gates, const uint32_t* masks, const int* offsets,
-                  const int* block_prefix, int T, int N, int K, int* row_src, float* row_gate,
-                  int* inv, hipStream_t s) {
+void launch_place(const int* idx, const float* gates, const uint32_t* masks,
+                  const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
+                  const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
+                  float* row_gate, int* inv, hipStream_t s) {
   const long long n = (long long)T * K;
-  place_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, gates, masks, offsets,
-                                                           block_prefix, T, N, K, row_src,
-                                                           row_gate, inv);
+  BucketMasks bm{masks, masks_hi, const_cast<int*>(prefix_hi), const_cast<int*>(prefix_lo),
+                 const_cast<int*>(counts_hi)};
+  place_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, gates, bm, offsets, T, N, K,
+                                                           row_src, row_gate, inv);
 }
 
 }  // namespace lmoe

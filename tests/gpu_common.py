@@ -62,8 +62,21 @@ def check_y(y_gpu, y_ref, tol):
     return err / rms
 
 
-def check_bucketing(out, idx, N, K):
-    """counts, offsets, stable (expert, token) permutation and its inverse."""
+# the library's large-tile path (include/latentmoe.h, LATENTMOE_INTER_ROW_SRC):
+# bf16 experts with more than 48 routed rows per expert on average split each
+# expert's rows into gate >= 0.1 first, then the rest
+SPLIT_MIN_AVG_ROWS = 48.0
+HI_TAU = 0.1
+
+
+def splits_rows(wl):
+    return wl.experts == "bf16" and wl.T * wl.top_k / wl.n_experts > SPLIT_MIN_AVG_ROWS
+
+
+def check_bucketing(out, idx, N, K, gates=None):
+    """counts, offsets, stable (expert, token) permutation and its inverse.
+    With gates: each expert's rows are its gate >= HI_TAU tokens, then the
+    others, each group sorted by token."""
     T = idx.shape[0]
     counts = np.bincount(idx.ravel(), minlength=N)
     assert np.array_equal(out["counts"], counts)
@@ -73,7 +86,12 @@ def check_bucketing(out, idx, N, K):
     assert sorted(inv.tolist()) == list(range(T * K))          # a permutation
     for e in range(N):
         seg = row_src[offs[e]:offs[e + 1]]
-        toks = np.nonzero((idx == e).any(1))[0]
+        sel = idx == e
+        if gates is None:
+            toks = np.nonzero(sel.any(1))[0]
+        else:
+            hi = (sel & (gates >= HI_TAU)).any(1)
+            toks = np.concatenate([np.nonzero(hi)[0], np.nonzero(sel.any(1) & ~hi)[0]])
         assert np.array_equal(seg, toks), e                    # sorted by token: stable
     flat_t = np.repeat(np.arange(T), K)
     assert np.array_equal(row_src[inv], flat_t)                # inverse
@@ -94,13 +112,15 @@ def full_check(wl, x, W, tol=1e-2, extra=("z", "z_lo", "y_lat", "y_lat_lo", "cou
         # hi + lo: the fp32 accumulation, well inside 1e-5 relative
         z2 = z + oracle.bf16_to_f64(out["z_lo"])
         assert np.all(np.abs(z2 - rz) <= 1e-5 * np.sqrt(np.mean(rz ** 2)) + 2.0 ** -16 * np.abs(rz))
+    split = splits_rows(wl)
     if "y_lat" in out:
-        # every stage carries ~16 bits: the latent sum matches closely
+        # every stage carries ~16 bits: the latent sum matches closely (rows
+        # carried at bf16 on the large-tile path add up to ~3e-3 of it)
         yl = oracle.bf16_to_f64(out["y_lat"]) + oracle.bf16_to_f64(out["y_lat_lo"])
         ry = ref["y_lat"]
-        assert np.max(np.abs(yl - ry)) <= 1e-3 * np.sqrt(np.mean(ry ** 2))
+        assert np.max(np.abs(yl - ry)) <= (1e-2 if split else 1e-3) * np.sqrt(np.mean(ry ** 2))
     if "counts" in out:
-        check_bucketing(out, out["idx"], wl.n_experts, wl.top_k)
+        check_bucketing(out, out["idx"], wl.n_experts, wl.top_k, out["gates"] if split else None)
     return out, ref, ratio
 
 
@@ -118,7 +138,7 @@ def sampled_check(name, n_sample, tol, seed=0):
     ref_idx = oracle.select_topk(logits, wl.top_k)
     ref_g = oracle.softmax_selected(logits, ref_idx)
     check_topk(out["idx"], out["gates"], ref_idx, ref_g)
-    check_bucketing(out, out["idx"], wl.n_experts, wl.top_k)
+    check_bucketing(out, out["idx"], wl.n_experts, wl.top_k, out["gates"] if splits_rows(wl) else None)
     log("%s: top-K and bucketing match on all %d tokens" % (name, wl.T))
     toks = np.unique(np.linspace(0, wl.T - 1, n_sample).astype(int))
     ref = oracle.forward(x, W, wl.top_k, tokens=toks)

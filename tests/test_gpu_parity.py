@@ -133,6 +133,16 @@ def test_zero_router_tie_break():
     assert np.all(np.abs(out["gates"] - 1.0 / wl.top_k) <= 1e-7)
 
 
+def test_split_rows_large_tiles_zipf():
+    # > 48 rows per expert with a skewed router: the large-tile path with rows
+    # split by gate (hi + lo rows first), ragged tiles of both classes
+    wl = small_wl(T=400, d=256, latent=128, n_experts=32, top_k=5, expert_hidden=192,
+                  shared_hidden=256, router="zipf")
+    x, W = gen(wl, 16)
+    log("split rows, large tiles, zipf", wl)
+    full_check(wl, x, W)
+
+
 def test_zipf_bias_router():
     wl = small_wl(T=40, n_experts=32, top_k=5, router="zipf")
     x, W = gen(wl, 7)
