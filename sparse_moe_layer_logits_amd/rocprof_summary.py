@@ -4,9 +4,9 @@
         per (kernel, grid size) group: calls, average / min / max duration
 
     python -m sparse_moe_layer_logits_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \\
-            --kernel SUBSTR --grid G --probe-mib M --source-sha SHA --out FILE.json
-        HBM bytes per launch of one kernel group from a FETCH_SIZE run and a
-        WRITE_SIZE run.  Each counter is scaled by what it reads for the plain
+            --group SUBSTR@GRID [--group ...] --probe-mib M --source-sha SHA --out FILE.json
+        HBM bytes per launch of a stage (the sum over its kernel groups, one
+        launch each) from a FETCH_SIZE run and a WRITE_SIZE run.  Each counter is scaled by what it reads for the plain
         copy launches of the same run (bench.py --copy-probe-mib M: M MiB read
         and M MiB written per launch).
 
@@ -68,10 +68,10 @@ def _pick(groups, kernel, grid):
 
 def cmd_traffic(a):
     probe_bytes = a.probe_mib * (1 << 20)
-    res = {}
+    groups_spec = [(g.rsplit("@", 1)[0], int(g.rsplit("@", 1)[1])) for g in a.group]
+    res = {"groups": []}
     for counter, dir_ in (("FETCH_SIZE", a.fetch_dir), ("WRITE_SIZE", a.write_dir)):
         groups = counter_per_dispatch(dir_, counter)
-        (name, grid), vals = _pick(groups, a.kernel, a.grid)
         # the copy probe: elementwise launches that move about probe_bytes each
         probe = [v for (k, g), vs in groups.items() if "elementwise" in k
                  for v in vs if probe_bytes / 4 < v * 1024 < probe_bytes * 4]
@@ -79,10 +79,15 @@ def cmd_traffic(a):
             raise SystemExit("no copy-probe launches in %s" % dir_)
         probe_kib = sorted(probe)[len(probe) // 2]
         factor = probe_bytes / (probe_kib * 1024)
-        kib = sum(vals) / len(vals)
-        res[counter] = {"kib_per_launch": kib, "launches": len(vals), "probe_kib": probe_kib,
+        kib, launches, names = 0.0, [], []
+        for kernel, grid in groups_spec:
+            (name, g), vals = _pick(groups, kernel, grid)
+            kib += sum(vals) / len(vals)
+            launches.append(len(vals))
+            names.append("%s @%d" % (name, g))
+        res[counter] = {"kib_per_launch": kib, "launches": launches, "probe_kib": probe_kib,
                         "factor": factor, "bytes_per_launch": kib * 1024 * factor}
-        res["kernel_name"], res["grid"] = name, grid
+        res["groups"] = names
     res["hbm_bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
     res["source_sha"] = a.source_sha
     res["command"] = a.command
@@ -99,8 +104,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
-    t.add_argument("--kernel", required=True)
-    t.add_argument("--grid", type=int, default=None)
+    t.add_argument("--group", action="append", required=True,
+                   help="kernel name substring @ grid size (threads); repeat for a stage of several launches")
     t.add_argument("--probe-mib", type=int, required=True)
     t.add_argument("--source-sha", required=True)
     t.add_argument("--command", default="")
