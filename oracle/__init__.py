@@ -9,20 +9,25 @@ every stored byte (bf16, E4M3, E2M1) with its own code.
 Method: "Nemotron 3 Super: Open, Efficient Mixture-of-Experts Hybrid
 Mamba-Transformer Model for Agentic Reasoning", section 3.2 (LatentMoE) and the
 section 3.1 shape table; FP4 storage per the same page's section 3.6 (dual
-scale) and "Nemotron 3 Ultra" (E2M1 values, E4M3 block scales).
+scale) and "Nemotron 3 Ultra" (E2M1 values, E4M3 block scales); the shared
+expert in the same FP4 format and W_down / W_up as per-tensor FP8 per the
+released precision mix ("Nemotron 3.5 Super and Lightning", 4-bit
+quantisation section).
 
 Every function here is pinned by the CPU tests (closed forms, special cases
 that reduce to a textbook mixture, brute force on tiny inputs, exhaustive
 format tables).  Nothing here is pinned against values printed on the pages:
 the pages print no numeric LatentMoE example.
 """
-from .formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant  # noqa: F401
+from .formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant, fp8_dequant  # noqa: F401
 from .latentmoe import (  # noqa: F401
     expert_ffn,
     forward,
+    projection_weights,
     router_logits,
     select_topk,
     shared_expert,
+    shared_weights,
     softmax_selected,
     topk_gap,
 )

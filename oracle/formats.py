@@ -14,6 +14,14 @@ exponent 0 is subnormal; S.1111.111 is NaN, there is no infinity.  The Nemotron
 Block-scaled FP4 weight ("dual scale", Nemotron 3 Super section 3.6):
 w = e2m1(code) * e4m3(block scale) * tensor scale, one block scale per 16
 consecutive input-dim elements, one float32 tensor scale per expert matrix.
+The same format serves the shared expert's two matrices: the released recipe
+puts the GEMMs of the MoE experts and of the shared expert in NVFP4 and other
+projection layers in FP8 ("Nemotron 3.5 Super and Lightning", section on
+keeping accuracy under 4-bit quantisation).
+
+Per-tensor FP8 weight (that recipe's FP8 layers; here optionally W_down and
+W_up, a reading: the pages do not name the latent projections' precision):
+w = e4m3(code) * tensor scale, one float32 scale per matrix.
 """
 import numpy as np
 
@@ -62,3 +70,12 @@ def fp4_dequant(packed: np.ndarray, block_scale: np.ndarray, tensor_scale) -> np
     q[:, :, 1] = np.take(q_table, packed >> 4)
     s = np.take(s_table, np.asarray(block_scale, dtype=np.uint8)) * float(np.float32(tensor_scale))
     return (q.reshape(rows, -1, 16) * s[:, :, None]).reshape(rows, 2 * half)
+
+
+def fp8_dequant(codes: np.ndarray, tensor_scale) -> np.ndarray:
+    """Decode one per-tensor-scaled E4M3FN matrix.
+
+    codes: [rows, cols] uint8 E4M3FN.  tensor_scale: float32 scalar.
+    Returns float64 [rows, cols].
+    """
+    return e4m3fn_to_f64(codes) * float(np.float32(tensor_scale))

@@ -16,8 +16,10 @@ Per token t (readings of what the page leaves open are marked *):
   6. combine  y_lat = sum_k g_k o_k, in k order
   7. output   y = W_up y_lat + S2 relu(S1 x)^2           (shared expert, ungated*)
 
-All inputs are the stored bytes (bf16 bit patterns, float32, or block-scaled
-FP4 codes), decoded to float64 by ``formats``; every operation is float64.
+All inputs are the stored bytes (bf16 bit patterns, float32, block-scaled FP4
+codes for the experts and optionally the shared expert, per-tensor FP8 codes
+optionally for W_down and W_up), decoded to float64 by ``formats``; every
+operation is float64.
 Experts are evaluated one expert at a time over the tokens routed to it, which
 is the same per-token sum; nothing is fused or blocked.
 """
@@ -25,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import bf16_to_f64, fp4_dequant
+from .formats import bf16_to_f64, fp4_dequant, fp8_dequant
 
 
 def router_logits(x_bits, router_w, router_bias=None):
@@ -94,6 +96,25 @@ def expert_weights(W, e):
     return w1, w2
 
 
+def shared_weights(W):
+    """Float64 (S1 [m_s, d], S2 [d, m_s]) of the shared expert from the stored bytes."""
+    if W.get("shared_w1_scale") is not None:
+        s1 = fp4_dequant(W["shared_w1"], W["shared_w1_scale"], np.ravel(W["shared_w1_tscale"])[0])
+        s2 = fp4_dequant(W["shared_w2"], W["shared_w2_scale"], np.ravel(W["shared_w2_tscale"])[0])
+    else:
+        s1 = bf16_to_f64(W["shared_w1"])
+        s2 = bf16_to_f64(W["shared_w2"])
+    return s1, s2
+
+
+def projection_weights(W):
+    """Float64 (W_down [l, d], W_up [d, l]) from the stored bytes."""
+    if W.get("w_down_tscale") is not None:
+        return (fp8_dequant(W["w_down"], np.ravel(W["w_down_tscale"])[0]),
+                fp8_dequant(W["w_up"], np.ravel(W["w_up_tscale"])[0]))
+    return bf16_to_f64(W["w_down"]), bf16_to_f64(W["w_up"])
+
+
 def forward(x_bits, W, top_k, tokens=None, intermediates=False):
     """LatentMoE forward for the rows ``tokens`` of x (all rows if None).
 
@@ -110,7 +131,8 @@ def forward(x_bits, W, top_k, tokens=None, intermediates=False):
     idx = select_topk(logits, top_k)                                      # step 2
     gates = softmax_selected(logits, idx)                                 # step 3
 
-    z = x @ bf16_to_f64(W["w_down"]).T                                    # step 4
+    w_down, w_up = projection_weights(W)
+    z = x @ w_down.T                                                      # step 4
     latent = z.shape[1]
 
     out = np.zeros((Ts, top_k, latent))                                   # step 5
@@ -123,8 +145,8 @@ def forward(x_bits, W, top_k, tokens=None, intermediates=False):
     for k in range(top_k):
         y_lat += gates[:, k:k + 1] * out[:, k]
 
-    y_shared = shared_expert(x, bf16_to_f64(W["shared_w1"]), bf16_to_f64(W["shared_w2"]))
-    y = y_lat @ bf16_to_f64(W["w_up"]).T + y_shared                       # step 7
+    y_shared = shared_expert(x, *shared_weights(W))
+    y = y_lat @ w_up.T + y_shared                                         # step 7
 
     res = dict(y=y, idx=idx, gates=gates, logits=logits)
     if intermediates:

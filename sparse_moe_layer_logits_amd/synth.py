@@ -50,6 +50,8 @@ class Workload:
     shared_hidden: int    # m_s
     router: str = "normal"   # "normal" | "zipf" (adds a Zipf(1.1) per-expert bias)
     experts: str = "bf16"    # "bf16" | "fp4"
+    shared: str = "bf16"     # "bf16" | "fp4" (the shared expert's two matrices)
+    proj: str = "bf16"       # "bf16" | "fp8" (W_down and W_up, per-tensor scale)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -77,6 +79,11 @@ WORKLOADS = {
     "super_fp4": Workload("super_fp4", T=1024, d=4096, latent=1024, n_experts=512,
                           top_k=22, expert_hidden=2688, shared_hidden=5376,
                           experts="fp4"),
+    # Super shapes in the released precision mix: FP4 experts and shared expert,
+    # FP8 W_down / W_up (x and router as in super_fp4)
+    "super_recipe": Workload("super_recipe", T=1024, d=4096, latent=1024, n_experts=512,
+                             top_k=22, expert_hidden=2688, shared_hidden=5376,
+                             experts="fp4", shared="fp4", proj="fp8"),
 }
 
 # stream identifiers (one PCG64 stream per tensor / expert / row)
@@ -187,6 +194,21 @@ def encode_fp4(w_bf16: np.ndarray):
     return packed, sb_code, ts
 
 
+def encode_fp8(w_bf16: np.ndarray):
+    """Encode one matrix [rows, cols] (bf16 bits) as E4M3FN codes with one float32
+    tensor scale: scale = amax / 448, code = RNE(w / scale) with the sign in bit 7.
+    Returns (codes [rows, cols] u8, tensor scale (float32))."""
+    w = bf16_bits_to_f32(w_bf16)
+    amax = np.float32(np.max(np.abs(w))) if w.size else np.float32(0)
+    ts = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    if ts == 0:
+        ts = np.float32(1.0)
+    q = (w / ts).astype(np.float32)
+    mag = encode_e4m3(np.abs(q))
+    sign = ((q < 0) & (mag != 0)).astype(np.uint8) << 7
+    return (mag | sign).astype(np.uint8), ts
+
+
 # --------------------------------------------------------------------------
 # draws
 # --------------------------------------------------------------------------
@@ -250,6 +272,18 @@ def make_weights(wl: Workload, seed: int = 0, threads: int | None = None) -> dic
     W["w_up"] = _normal_bf16(seed, (TID_W_UP,), (d, l), 1.0 / np.sqrt(l))
     W["shared_w1"] = _normal_bf16(seed, (TID_SHARED_W1,), (ms, d), 1.0 / np.sqrt(d))
     W["shared_w2"] = _normal_bf16(seed, (TID_SHARED_W2,), (d, ms), 1.0 / np.sqrt(ms))
+    if wl.proj == "fp8":   # quantised from the same bf16 masters
+        for k in ("w_down", "w_up"):
+            W[k], ts = encode_fp8(W[k])
+            W[k + "_tscale"] = np.array([ts], np.float32)
+    elif wl.proj != "bf16":
+        raise ValueError(wl.proj)
+    if wl.shared == "fp4":
+        for k in ("shared_w1", "shared_w2"):
+            W[k], W[k + "_scale"], ts = encode_fp4(W[k])
+            W[k + "_tscale"] = np.array([ts], np.float32)
+    elif wl.shared != "bf16":
+        raise ValueError(wl.shared)
 
     if wl.experts == "bf16":
         w1 = np.empty((n, m, l), dtype=np.uint16)

@@ -3,7 +3,7 @@ format definitions (IEEE binary32 upper half for bf16; OCP Microscaling v1.0
 E2M1 and OCP FP8 E4M3FN), and the FP4 encoder used to prepare inputs."""
 import numpy as np
 
-from oracle.formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant
+from oracle.formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant, fp8_dequant
 from sparse_moe_layer_logits_amd import synth
 
 
@@ -136,3 +136,39 @@ def test_fp4_roundtrip_on_grid_and_error_bound():
     assert np.all(np.abs(back - wf) <= unit + clip + 1e-12)
     # the block maximum maps to about 6 units (within E4M3 rounding of the scale)
     assert np.all(np.abs(bmax / (6 * unit) - 1) <= 2 ** -4 + 1e-9)
+
+
+def test_fp8_dequant_known_values_and_scale():
+    codes = np.array([[0x38, 0xB8, 0x7E, 0x01, 0x00, 0x80, 0x3C, 0xC4]], np.uint8)
+    got = fp8_dequant(codes, np.float32(0.25))
+    assert got.tolist() == [[0.25, -0.25, 112.0, 2.0 ** -11, 0.0, -0.0, 0.375, -0.75]]
+    # the tensor scale is applied as its float32 value
+    assert fp8_dequant(np.array([[0x38]], np.uint8), 0.1)[0, 0] == float(np.float32(0.1))
+
+
+def test_fp8_encoder_on_grid_and_error_bound():
+    rng = np.random.default_rng(11)
+    # values already on the grid e4m3 * 2^-8 (amax at code 0x7E so amax / 448 gives the
+    # scale back) quantise back to themselves, signs included
+    c = rng.integers(0, 127, size=(12, 40)).astype(np.uint8)
+    c[0, 0] = 0x7E
+    sgn = rng.integers(0, 2, size=c.shape).astype(np.uint8) << 7
+    c = np.where(c == 0, c, c | sgn).astype(np.uint8)
+    w = fp8_dequant(c, np.float32(2.0 ** -8))
+    wb = synth.f32_to_bf16_bits(w.astype(np.float32))
+    assert np.array_equal(bf16_to_f64(wb), w)
+    codes, ts = synth.encode_fp8(wb)
+    assert ts == np.float32(2.0 ** -8)
+    assert np.array_equal(fp8_dequant(codes, ts), w)
+    # random weights: relative error at most 2^-4 (half an E4M3 step) in the normal
+    # range, absolute at most 2^-10 * scale among the subnormals; amax maps to 448
+    wr = synth.f32_to_bf16_bits((rng.standard_normal((64, 96)) * 0.03).astype(np.float32))
+    codes, ts = synth.encode_fp8(wr)
+    wf = bf16_to_f64(wr)
+    back = fp8_dequant(codes, ts)
+    err = np.abs(back - wf)
+    normal = np.abs(wf) >= 2.0 ** -6 * float(ts)
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(wf[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * float(ts) * (1 + 1e-6))
+    assert np.all(np.sign(back[back != 0]) == np.sign(wf[back != 0]))
+    assert abs(np.max(np.abs(back)) - np.max(np.abs(wf))) <= 2.0 ** -4 * np.max(np.abs(wf))

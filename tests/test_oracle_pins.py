@@ -270,3 +270,69 @@ def test_only_selected_experts_matter():
     y3 = oracle.forward(x, W3, 2)["y"]
     changed = np.any(np.abs(y3 - r["y"]) > 0, axis=1)
     assert changed.tolist() == [bool((r["idx"][t] == e).any()) for t in range(4)]
+
+
+# ---------------------------------------------------------------------------
+# the released precision mix: FP4 shared expert, FP8 W_down / W_up
+# ---------------------------------------------------------------------------
+
+def _pow2_tscale(W, key):
+    """Replace a stored tensor scale by a power of two, so that every decoded
+    weight is a bf16 number."""
+    W[key + "_tscale"] = np.array([2.0 ** -9], np.float32)
+
+
+def test_fp4_shared_expert_matches_bf16_storage_of_the_same_values():
+    """The FP4-stored shared expert gives exactly the result of bf16 storage of
+    its decoded values (exact in bf16 with a power-of-two tensor scale): the
+    format path feeds S1 and S2 to the same places as the bf16 path."""
+    wl = synth.Workload("t", T=5, d=32, latent=16, n_experts=8, top_k=3, expert_hidden=24,
+                        shared_hidden=48, shared="fp4")
+    x, W = synth.make(wl, 0, threads=2)
+    for k in ("shared_w1", "shared_w2"):
+        _pow2_tscale(W, k)
+    Wb = {k: v for k, v in W.items() if not k.startswith("shared_w")}
+    for k in ("shared_w1", "shared_w2"):
+        Wb[k] = bits(oracle.fp4_dequant(W[k], W[k + "_scale"], W[k + "_tscale"][0]))
+    assert Wb["shared_w1"].shape == (48, 32) and Wb["shared_w2"].shape == (32, 48)
+    a = oracle.forward(x, W, wl.top_k, intermediates=True)
+    b = oracle.forward(x, Wb, wl.top_k, intermediates=True)
+    np.testing.assert_array_equal(a["y_shared"], b["y_shared"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    assert np.abs(a["y_shared"]).max() > 0
+
+
+def test_fp8_projections_match_bf16_storage_of_the_same_values():
+    wl = synth.Workload("t", T=5, d=32, latent=16, n_experts=8, top_k=3, expert_hidden=24,
+                        shared_hidden=48, proj="fp8")
+    x, W = synth.make(wl, 1, threads=2)
+    assert W["w_down"].dtype == np.uint8 and W["w_down"].shape == (16, 32)
+    for k in ("w_down", "w_up"):
+        _pow2_tscale(W, k)
+    Wb = {k: v for k, v in W.items() if not k.endswith("_tscale")}
+    for k in ("w_down", "w_up"):
+        Wb[k] = bits(oracle.fp8_dequant(W[k], W[k + "_tscale"][0]))
+    a = oracle.forward(x, W, wl.top_k, intermediates=True)
+    b = oracle.forward(x, Wb, wl.top_k, intermediates=True)
+    for key in ("z", "y_lat", "y"):
+        np.testing.assert_array_equal(a[key], b[key])
+    assert np.abs(a["z"]).max() > 0
+
+
+def test_released_mix_stays_near_the_bf16_masters():
+    """Quantising from the same bf16 masters keeps the top-K (routing is untouched)
+    and moves y by about what the formats' precision allows: E4M3 (3 mantissa
+    bits) a few percent of rms(y), E2M1 (1 mantissa bit) a few tens of percent.
+    This pins that the quantised tensors encode the masters, not other draws."""
+    base = synth.Workload("t", T=6, d=64, latent=32, n_experts=8, top_k=3, expert_hidden=32,
+                          shared_hidden=64)
+    x, W0 = synth.make(base, 2, threads=2)
+    a = oracle.forward(x, W0, base.top_k)
+    rms = np.sqrt(np.mean(a["y"] ** 2))
+    for kw, lo, hi in ((dict(proj="fp8"), 3e-3, 0.06),
+                       (dict(experts="fp4", shared="fp4", proj="fp8"), 0.03, 0.3)):
+        _, W1 = synth.make(base.replace(**kw), 2, threads=2)
+        b = oracle.forward(x, W1, base.top_k)
+        np.testing.assert_array_equal(a["idx"], b["idx"])
+        rel = np.sqrt(np.mean((a["y"] - b["y"]) ** 2)) / rms
+        assert lo < rel < hi, (kw, rel)
