@@ -39,7 +39,8 @@ def log(*a):
 def source_sha(path):
     h = hashlib.sha256()
     for p in (path, "sparse_moe_layer_logits_amd/csrc/epilogue.hpp",
-              "sparse_moe_layer_logits_amd/csrc/common.hpp", "sparse_moe_layer_logits_amd/csrc/fp4.hpp"):
+              "sparse_moe_layer_logits_amd/csrc/common.hpp", "sparse_moe_layer_logits_amd/csrc/fp4.hpp",
+              "sparse_moe_layer_logits_amd/csrc/fp8.hpp"):
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()[:16]
 
@@ -48,10 +49,13 @@ def algorithmic(wl, touched):
     """Whole-layer algorithmic bytes and flops (what the method must move and
     compute; intermediates excluded, multiply-add = 2 flops)."""
     d, l, n, k, m, ms, T = wl.d, wl.latent, wl.n_experts, wl.top_k, wl.expert_hidden, wl.shared_hidden, wl.T
-    beta = 2.0 if wl.experts == "bf16" else 0.5 + 1.0 / 16
-    per_expert_extra = 0 if wl.experts == "bf16" else 8
-    bytes_ = (n * d * 4 + 2 * l * d * 2 + touched * (2 * l * m * beta + per_expert_extra)
-              + 2 * d * ms * 2 + T * d * 2 + T * d * 4)
+    fp4 = 0.5 + 1.0 / 16                                   # code nibble + E4M3 per 16
+    beta = 2.0 if wl.experts == "bf16" else fp4
+    per_expert_extra = 0 if wl.experts == "bf16" else 8    # two fp32 tensor scales
+    proj = 2 * l * d * 2 if wl.proj == "bf16" else 2 * l * d + 8
+    shared = 2 * d * ms * 2 if wl.shared == "bf16" else 2 * d * ms * fp4 + 8
+    bytes_ = (n * d * 4 + proj + touched * (2 * l * m * beta + per_expert_extra)
+              + shared + T * d * 2 + T * d * 4)
     flops = 2.0 * T * (d * n + 2 * d * l + 2 * k * l * m + 2 * d * ms)
     return bytes_, flops
 
@@ -223,7 +227,8 @@ def main():
         "data": "synthetic (seeded normal weights and tokens, N(0, 1/fan_in))",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "latent": wl.latent,
                    "n_experts": wl.n_experts, "top_k": wl.top_k, "expert_hidden": wl.expert_hidden,
-                   "shared_hidden": wl.shared_hidden, "experts": wl.experts, "router": wl.router,
+                   "shared_hidden": wl.shared_hidden, "experts": wl.experts, "shared": wl.shared,
+                   "projections": wl.proj, "router": wl.router,
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": roofline,
         "layer": {"alg_bytes": int(alg_bytes), "alg_flops": alg_flops, "experts_touched": touched,

@@ -18,8 +18,9 @@
  *   - experts: two matrices per expert with a squared-ReLU activation,
  *     o = W2 relu(W1 z)^2; the shared expert has the same form at width d and
  *     is added without a gate; no biases or norms inside the layer;
- *   - FP4 experts: one E4M3FN scale per 16 consecutive input-dim elements and
- *     one fp32 scale per expert matrix; element 2j in the low nibble of byte j.
+ *   - FP4 weights: one E4M3FN scale per 16 consecutive input-dim elements and
+ *     one fp32 scale per matrix; element 2j in the low nibble of byte j;
+ *   - FP8 weights: E4M3FN elements and one fp32 scale per matrix.
  *
  * Conventions: all matrices are row-major; a weight [out, in] computes
  * y = x * W^T.  bf16 tensors are passed as raw 16-bit patterns.  Every pointer
@@ -46,9 +47,24 @@ extern "C" {
 #define LATENTMOE_ERR_OUT_OF_MEMORY (-3) /* workspace allocation failed               */
 #define LATENTMOE_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
 
-/* ---- expert weight formats ---- */
-#define LATENTMOE_EXPERTS_BF16 0
-#define LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 1
+/* ---- weight storage formats ----
+ * BF16: raw bf16 patterns.
+ * FP4_E2M1_E4M3_B16: block-scaled 4-bit ("Nemotron 3 Super", section 3.6: a
+ *   per-tensor and a per-block scale; "Nemotron 3 Ultra": E2M1 elements, E4M3
+ *   block scales): w = e2m1(code) * e4m3fn(block scale) * tensor scale, one
+ *   block scale per 16 consecutive input-dim elements, element 2j in the low
+ *   nibble of byte j.
+ * FP8_E4M3: one E4M3FN byte per element times one fp32 tensor scale.
+ * Which matrices may use which format follows the released precision mix
+ * ("Nemotron 3.5 Super and Lightning", section on keeping accuracy under
+ * 4-bit quantisation: experts and shared expert in NVFP4, other projections in
+ * FP8); FP8 for the latent projections W_down / W_up is this library's reading,
+ * the pages do not name their precision. */
+#define LATENTMOE_FORMAT_BF16 0
+#define LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 1
+#define LATENTMOE_FORMAT_FP8_E4M3 2
+#define LATENTMOE_EXPERTS_BF16 LATENTMOE_FORMAT_BF16
+#define LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16
 
 typedef struct latentmoe_handle_s* latentmoe_handle_t;
 
@@ -64,7 +80,9 @@ typedef struct {
   int32_t expert_hidden; /* m (each expert l -> m -> l)                   */
   int32_t shared_hidden; /* m_s (shared expert d -> m_s -> d)             */
   int32_t max_tokens;    /* largest T a forward call may pass             */
-  int32_t expert_format; /* LATENTMOE_EXPERTS_*                           */
+  int32_t expert_format; /* experts W1, W2: FORMAT_BF16 | FORMAT_FP4_...  */
+  int32_t shared_format; /* shared S1, S2: FORMAT_BF16 | FORMAT_FP4_...   */
+  int32_t proj_format;   /* W_down, W_up: FORMAT_BF16 | FORMAT_FP8_E4M3   */
 } latentmoe_config;
 
 /* Weights (host struct holding device pointers).  The library BORROWS every
@@ -73,25 +91,37 @@ typedef struct {
 typedef struct {
   const float* router_w;          /* [N, d] fp32                                  */
   const float* router_bias;       /* [N] fp32, or NULL for no bias                */
-  const uint16_t* w_down;         /* [l, d] bf16   (W_down)                       */
-  const uint16_t* w_up;           /* [d, l] bf16   (W_up)                         */
+  const void* w_down;             /* bf16 [l, d]     | FP8 codes u8 [l, d]        */
+  const void* w_up;               /* bf16 [d, l]     | FP8 codes u8 [d, l]        */
   const void* expert_w1;          /* bf16 [N, m, l]  | FP4 codes u8 [N, m, l/2]   */
   const void* expert_w2;          /* bf16 [N, l, m]  | FP4 codes u8 [N, l, m/2]   */
   const uint8_t* expert_w1_scale; /* FP4 only: E4M3FN [N, m, l/16], else NULL     */
   const uint8_t* expert_w2_scale; /* FP4 only: E4M3FN [N, l, m/16], else NULL     */
   const float* expert_w1_tscale;  /* FP4 only: fp32 [N], else NULL                */
   const float* expert_w2_tscale;  /* FP4 only: fp32 [N], else NULL                */
-  const uint16_t* shared_w1;      /* [m_s, d] bf16                                */
-  const uint16_t* shared_w2;      /* [d, m_s] bf16                                */
+  const void* shared_w1;          /* bf16 [m_s, d]   | FP4 codes u8 [m_s, d/2]    */
+  const void* shared_w2;          /* bf16 [d, m_s]   | FP4 codes u8 [d, m_s/2]    */
+  const uint8_t* shared_w1_scale; /* FP4 shared only: E4M3FN [m_s, d/16]          */
+  const uint8_t* shared_w2_scale; /* FP4 shared only: E4M3FN [d, m_s/16]          */
+  const float* shared_w1_tscale;  /* FP4 shared only: fp32 [1]                    */
+  const float* shared_w2_tscale;  /* FP4 shared only: fp32 [1]                    */
+  const float* w_down_tscale;     /* FP8 projections only: fp32 [1]               */
+  const float* w_up_tscale;       /* FP8 projections only: fp32 [1]               */
 } latentmoe_weights;
 
 /* Create a layer handle.  Validates the shape and pointers, allocates the
  * workspace for cfg->max_tokens tokens (device memory owned by the handle) and
- * derives the router's split weights on `stream` (the only work enqueued).
+ * derives the router's split weights on `stream`.  With max_tokens above 64
+ * and an FP4 shared expert or FP8 projections, it also writes the exact bf16
+ * values of those matrices (block scale applied, tensor scale not) into the
+ * workspace on `stream`: dense GEMMs of more than 64 tokens run on the
+ * LDS-tiled kernel, which reads bf16 weights; up to 64 tokens the stored
+ * format is streamed and decoded in registers.  No other work is enqueued.
  * cfg, w: host pointers, read during the call only.  out: host pointer that
  * receives the handle (set to NULL on failure).
- * Errors: INVALID_ARG (null pointer, format/pointer mismatch), UNSUPPORTED
- * (shape requirements above), OUT_OF_MEMORY, HIP. */
+ * Errors: INVALID_ARG (null pointer, including a scale pointer that the
+ * chosen format needs), UNSUPPORTED (shape requirements above, a format not
+ * offered for that matrix), OUT_OF_MEMORY, HIP. */
 int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
                    latentmoe_handle_t* out);
 
@@ -201,6 +231,14 @@ int latentmoe_profile_end(latentmoe_handle_t h, float* stage_ms, int n_stages, i
  * `stream`.  Errors: INVALID_ARG (null pointers, n_blocks < 0), HIP. */
 int latentmoe_fp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
                          uint16_t* out, hipStream_t stream);
+
+/* Decode n_groups groups of 16 E4M3FN bytes (device, n_groups * 16 bytes) to
+ * bf16 (device, n_groups * 16 values, every finite E4M3 value is a bf16 number)
+ * with the in-register decoder of the FP8 weight path; the tensor scale is not
+ * applied.  Asynchronous on `stream`.  Errors: INVALID_ARG (null pointers,
+ * n_groups < 0), HIP. */
+int latentmoe_fp8_decode(const uint8_t* codes, int64_t n_groups, uint16_t* out,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -21,8 +21,11 @@ LATENTMOE_ERR_UNSUPPORTED = -2
 LATENTMOE_ERR_OUT_OF_MEMORY = -3
 LATENTMOE_ERR_HIP = -4
 
-LATENTMOE_EXPERTS_BF16 = 0
-LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 = 1
+LATENTMOE_FORMAT_BF16 = 0
+LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 = 1
+LATENTMOE_FORMAT_FP8_E4M3 = 2
+LATENTMOE_EXPERTS_BF16 = LATENTMOE_FORMAT_BF16
+LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 = LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16
 
 INTER = dict(z=0, y_lat=1, counts=2, offsets=3, row_src=4, inv=5, h=6, hs_hi=7, hs_lo=8, y_lat_lo=9, z_lo=10, h_lo=11)
 STAGES = ["router", "topk", "bucket", "down_proj", "expert_up", "expert_down", "combine",
@@ -32,21 +35,22 @@ EXPORTED = [
     "latentmoe_init", "latentmoe_forward", "latentmoe_forward_graph", "latentmoe_destroy",
     "latentmoe_status_string",
     "latentmoe_workspace_bytes", "latentmoe_debug_copy", "latentmoe_profile_begin",
-    "latentmoe_profile_end", "latentmoe_fp4_decode",
+    "latentmoe_profile_end", "latentmoe_fp4_decode", "latentmoe_fp8_decode",
 ]
 
 
 class latentmoe_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d", "latent", "n_experts", "top_k", "expert_hidden", "shared_hidden", "max_tokens",
-        "expert_format")]
+        "expert_format", "shared_format", "proj_format")]
 
 
 class latentmoe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "router_w", "router_bias", "w_down", "w_up", "expert_w1", "expert_w2",
         "expert_w1_scale", "expert_w2_scale", "expert_w1_tscale", "expert_w2_tscale",
-        "shared_w1", "shared_w2")]
+        "shared_w1", "shared_w2", "shared_w1_scale", "shared_w2_scale", "shared_w1_tscale",
+        "shared_w2_tscale", "w_down_tscale", "w_up_tscale")]
 
 
 class LatentMoEError(RuntimeError):
@@ -81,6 +85,7 @@ def load(path: str = LIB_PATH):
     lib.latentmoe_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.c_int,
                                           ctypes.POINTER(ctypes.c_int)]
     lib.latentmoe_fp4_decode.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
+    lib.latentmoe_fp8_decode.argtypes = [vp, ctypes.c_int64, vp, vp]
     for name in EXPORTED:
         if name != "latentmoe_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -154,6 +159,11 @@ def latentmoe_fp4_decode(codes_ptr: int, scales_ptr: int, n_blocks: int, out_ptr
         ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
 
 
+def latentmoe_fp8_decode(codes_ptr: int, n_groups: int, out_ptr: int, stream: int) -> None:
+    _check("latentmoe_fp8_decode", load().latentmoe_fp8_decode(
+        ctypes.c_void_p(codes_ptr), int(n_groups), ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+
 # ---- torch-facing convenience layer ----
 
 def _torch():
@@ -191,10 +201,16 @@ class LatentMoE:
         torch = _torch()
         self.dims = dims
         self.Wd = Wd
-        fp4 = "expert_w1_scale" in Wd and Wd["expert_w1_scale"] is not None
-        self.cfg = latentmoe_config(dims.d, dims.latent, dims.n_experts, dims.top_k,
-                                    dims.expert_hidden, dims.shared_hidden, int(max_tokens),
-                                    LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 if fp4 else LATENTMOE_EXPERTS_BF16)
+        def has(k):
+            return Wd.get(k) is not None
+
+        # the stored formats follow from which scale tensors are present
+        self.cfg = latentmoe_config(
+            dims.d, dims.latent, dims.n_experts, dims.top_k, dims.expert_hidden,
+            dims.shared_hidden, int(max_tokens),
+            LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 if has("expert_w1_scale") else LATENTMOE_FORMAT_BF16,
+            LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 if has("shared_w1_scale") else LATENTMOE_FORMAT_BF16,
+            LATENTMOE_FORMAT_FP8_E4M3 if has("w_down_tscale") else LATENTMOE_FORMAT_BF16)
         w = latentmoe_weights()
         for name, _ in latentmoe_weights._fields_:
             setattr(w, name, _ptr(Wd.get(name)) or None)

@@ -34,16 +34,18 @@ __device__ __forceinline__ void epi4(const GemmParams& p, int expert, int split,
     store_bf16x4(p.C, off, hi[0], hi[1], hi[2], hi[3]);
     if constexpr (EPI == EPI_SQRELU_HILO) store_bf16x4(p.C2, off, lo[0], lo[1], lo[2], lo[3]);
   } else if constexpr (EPI == EPI_BF16_HILO) {
+    const float ts = p.b_tscale ? p.b_tscale[expert] : 1.0f;
     float hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i]));
-      lo[i] = v[i] - hi[i];
+      const float u = v[i] * ts;
+      hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(u));
+      lo[i] = u - hi[i];
     }
     store_bf16x4(p.C, off, hi[0], hi[1], hi[2], hi[3]);
     store_bf16x4(p.C2, off, lo[0], lo[1], lo[2], lo[3]);
   } else if constexpr (EPI == EPI_F32) {
-    f32x4_t w = v;
+    f32x4_t w = v * (p.b_tscale ? p.b_tscale[expert] : 1.0f);
     if (p.bias) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] += p.bias[n + i];
@@ -51,7 +53,7 @@ __device__ __forceinline__ void epi4(const GemmParams& p, int expert, int split,
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + off) = w;
   } else if constexpr (EPI == EPI_F32_ADD) {
     f32x4_t* dst = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + off);
-    *dst = *dst + v;
+    *dst = *dst + v * (p.b_tscale ? p.b_tscale[expert] : 1.0f);
   } else if constexpr (EPI == EPI_GATE_F32 || EPI == EPI_GATE_BF16) {
     const float ts = p.b_tscale ? p.b_tscale[expert] : 1.0f;
     const float gg = (p.row_scale ? p.row_scale[row] : 1.0f) * ts;

@@ -18,9 +18,13 @@
 //
 // DUAL: the activation comes as two bf16 parts (hi + lo); each weight
 // fragment feeds two MFMAs, so the weights are still read once.
+//
+// FMT: the stored weight format (bf16, block-scaled FP4, per-tensor FP8); FP4
+// and FP8 weights are decoded to exact bf16 in registers after the load.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "fp4.hpp"
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace lmoe {
@@ -45,19 +49,23 @@ __device__ __forceinline__ SegPtr seg_at(const GemmParams& p, int kg) {
   return r;
 }
 
-template <bool FP4>
+template <int FMT>
 struct BFrag;
 template <>
-struct BFrag<false> {
+struct BFrag<WF_BF16> {
   u32x4_t v[2];  // steps 0 and 1
 };
 template <>
-struct BFrag<true> {
+struct BFrag<WF_FP4> {
   u32x2_t codes;   // 16 E2M1 codes
   uint32_t scale;  // E4M3 byte
 };
+template <>
+struct BFrag<WF_FP8> {
+  u32x4_t codes;   // 16 E4M3 bytes: step 0 in words 0-1, step 1 in words 2-3
+};
 
-template <int W, int NT, int ROWS, int PAIRS, bool FP4, bool DUAL>
+template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL>
 __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
   constexpr int MTMAX = ROWS / 16;
   constexpr int NPART = DUAL ? 2 : 1;
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto load_b = [&](BFrag<FP4> (&bf)[PAIRS][NT], int c) {
+  auto load_b = [&](BFrag<FMT> (&bf)[PAIRS][NT], int c) {
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
       const int pg = c * PAIRS + pr;
@@ -137,10 +145,12 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
         for (int nt = 0; nt < NT; ++nt) {
           const int n = nbase + nt * 16 + r16;
           const long long kk = sp.kl + 16 * g;
-          if constexpr (FP4) {
+          if constexpr (FMT == WF_FP4) {
             const uint8_t* bp = sp.B + (bexp + (long long)n * p.ldb + kk) / 2;
             bf[pr][nt].codes = *reinterpret_cast<const u32x2_t*>(bp);
             bf[pr][nt].scale = p.b_scale[sexp + (long long)n * (p.ldb / 16) + kk / 16];
+          } else if constexpr (FMT == WF_FP8) {
+            bf[pr][nt].codes = ld128(sp.B + bexp + (long long)n * p.ldb + kk);
           } else {
             const uint8_t* bp = sp.B + 2 * (bexp + (long long)n * p.ldb + kk);
             bf[pr][nt].v[0] = ld128(bp);
@@ -178,7 +188,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
       *reinterpret_cast<u32x4_t*>(&As[buf][(part * ROWS + row) * ROWB + phys * 16]) = a_regs[u];
     }
   };
-  auto compute = [&](const BFrag<FP4> (&bf)[PAIRS][NT], int buf, int c) {
+  auto compute = [&](const BFrag<FMT> (&bf)[PAIRS][NT], int buf, int c) {
     if (!wave_active) return;
 #pragma unroll
     for (int pr = 0; pr < PAIRS; ++pr) {
@@ -189,9 +199,11 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
           u32x4_t bw[NT];
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            if constexpr (FP4) {
+            if constexpr (FMT == WF_FP4) {
               const float sc = e4m3_to_f32(bf[pr][nt].scale);
               bw[nt] = fp4x8_to_bf16(bf[pr][nt].codes[js], sc);
+            } else if constexpr (FMT == WF_FP8) {
+              bw[nt] = fp8x8_to_bf16(bf[pr][nt].codes[2 * js], bf[pr][nt].codes[2 * js + 1]);
             } else {
               bw[nt] = bf[pr][nt].v[js];
             }
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
     }
   };
 
-  BFrag<FP4> b0[PAIRS][NT], b1[PAIRS][NT];
+  BFrag<FMT> b0[PAIRS][NT], b1[PAIRS][NT];
   load_a(0);
   load_b(b0, 0);
   store_a(0);
@@ -260,38 +272,50 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #define LMOE_ST_PAIRS16 4
 #endif
 
-template <int ROWS, int PAIRS, bool FP4, bool DUAL>
+template <int ROWS, int PAIRS, int FMT, bool DUAL>
 static void launch_rows(const GemmParams& p, long long blocks, hipStream_t s) {
   constexpr int W = LMOE_ST_W, NT = 1;
-  gemm_stream_kernel<W, NT, ROWS, PAIRS, FP4, DUAL><<<(unsigned)blocks, W * 64, 0, s>>>(p);
+  gemm_stream_kernel<W, NT, ROWS, PAIRS, FMT, DUAL><<<(unsigned)blocks, W * 64, 0, s>>>(p);
 }
 
-template <bool FP4, bool DUAL>
+template <int FMT, bool DUAL>
 static void launch_fmt(const GemmParams& p, int rows, long long blocks, hipStream_t s) {
-  if (rows == 16)
-    launch_rows<16, LMOE_ST_PAIRS16, FP4, DUAL>(p, blocks, s);
-  else if (rows == 32)
-    launch_rows<32, DUAL ? 2 : 4, FP4, DUAL>(p, blocks, s);
-  else
-    launch_rows<64, DUAL ? 2 : 4, FP4, DUAL>(p, blocks, s);
+  if constexpr (FMT == WF_FP8) {
+    // FP8 weights are the dense projections only: 64-row tiles
+    launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+  } else {
+    if (rows == 16)
+      launch_rows<16, LMOE_ST_PAIRS16, FMT, DUAL>(p, blocks, s);
+    else if (rows == 32)
+      launch_rows<32, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+    else
+      launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+  }
 }
 
-void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s) {
+template <int FMT>
+static void launch_dual(const GemmParams& p, int rows, long long blocks, hipStream_t s) {
+  if (p.a_lo != nullptr)
+    launch_fmt<FMT, true>(p, rows, blocks, s);
+  else
+    launch_fmt<FMT, false>(p, rows, blocks, s);
+}
+
+void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s) {
   constexpr int W = LMOE_ST_W, NT = 1;
   // tile height: the grouped tile list's (16, 32 or 64 rows), 64 for dense GEMMs
   const int rows = !p.tile_expert ? 64 : p.rows_per_tile <= 16 ? 16 : p.rows_per_tile <= 32 ? 32 : 64;
+  if (fmt == WF_FP8 && rows != 64) return;  // not offered (callers check gemm_stream_supports)
   const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
   const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows - 1) / rows;
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
-  const bool dual = p.a_lo != nullptr;
-  if (fp4) {
-    if (dual) launch_fmt<true, true>(p, rows, blocks, s);
-    else launch_fmt<true, false>(p, rows, blocks, s);
-  } else {
-    if (dual) launch_fmt<false, true>(p, rows, blocks, s);
-    else launch_fmt<false, false>(p, rows, blocks, s);
-  }
+  if (fmt == WF_FP4)
+    launch_dual<WF_FP4>(p, rows, blocks, s);
+  else if (fmt == WF_FP8)
+    launch_dual<WF_FP8>(p, rows, blocks, s);
+  else
+    launch_dual<WF_BF16>(p, rows, blocks, s);
 }
 
 }  // namespace lmoe

@@ -6,21 +6,29 @@
 namespace lmoe {
 
 // epilogue kinds; each applies to four consecutive output columns of one row
+// (tscale = b_tscale, 1 when null; e = the tile's expert, 0 for dense GEMMs)
 enum Epi : int {
   EPI_PARTIAL = 0,      // partial[split][row][n] = acc                         (split-K)
   EPI_BF16 = 1,         // C bf16 = acc
   EPI_SQRELU_BF16 = 2,  // C bf16 = relu(acc * tscale[e])^2
   EPI_SQRELU_HILO = 3,  // v = relu(acc * tscale[e])^2; C bf16 = hi(v), C2 bf16 = bf16(v - hi(v))
-  EPI_F32 = 4,          // C f32 = acc (+ bias[n])
-  EPI_F32_ADD = 5,      // C f32 += acc
+  EPI_F32 = 4,          // C f32 = acc * tscale[e] (+ bias[n])
+  EPI_F32_ADD = 5,      // C f32 += acc * tscale[e]
   EPI_GATE_F32 = 6,     // C f32 = acc * tscale[e] * row_scale[row]
   EPI_GATE_BF16 = 7,    // C bf16 = acc * tscale[e] * row_scale[row]
-  EPI_BF16_HILO = 8,    // C bf16 = hi(acc), C2 bf16 = bf16(acc - hi(acc))
+  EPI_BF16_HILO = 8,    // v = acc * tscale[e]; C bf16 = hi(v), C2 bf16 = bf16(v - hi(v))
+};
+
+// stored weight formats of the B operand (same values as the C ABI's formats)
+enum WFmt : int {
+  WF_BF16 = 0,  // bf16
+  WF_FP4 = 1,   // E2M1 codes, E4M3 scale per 16 k, fp32 scale per matrix
+  WF_FP8 = 2,   // E4M3 bytes, fp32 scale per matrix
 };
 
 struct GemmSeg {
   const void* A;  // [rows, lda] bf16
-  const void* B;  // [N, ldb] bf16, or packed FP4 codes [N, ldb/2] bytes
+  const void* B;  // [N, ldb] bf16, packed FP4 codes [N, ldb/2] bytes, or FP8 [N, ldb] bytes
   int K;          // multiple of 64
 };
 
@@ -48,7 +56,7 @@ struct GemmParams {
   // block-scaled FP4 B operand
   const uint8_t* b_scale;   // [E, N, ldb/16] E4M3FN
   const uint8_t* b_scale_sm; // the same scales stage-major, [E, ldb/128, N, 8] (or null)
-  const float* b_tscale;    // [E] fp32 applied to the accumulator (null => 1)
+  const float* b_tscale;    // [E] fp32 (FP4 / FP8 tensor scales) applied to the accumulator (null => 1)
   // split-K
   int splits;
   int k_split;              // k elements per split (multiple of 64)
@@ -63,8 +71,9 @@ struct GemmParams {
   long long partial_stride; // elements between splits
 };
 
-// weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes)
-void launch_gemm_stream(const GemmParams& p, bool fp4, hipStream_t s);
+// weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes); fmt is a
+// WFmt (FP8 with 64-row tiles only)
+void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s);
 // grouped MFMA GEMM for 64-row expert tiles of block-scaled FP4 weights with dual
 // activations (tens of rows per expert): activations staged in LDS, weights read once
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s);
@@ -107,8 +116,11 @@ void launch_place(const int* idx, const float* gates, const uint32_t* masks,
 // y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo
 void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
                     uint16_t* y_lat_lo, hipStream_t s);
-// FP4 dequantisation check helper: codes/scales -> bf16 (exercises the in-register path)
+// FP4 blocks (8 code bytes + 1 scale byte each) -> exact bf16 with the in-register
+// decoder (tensor scale not applied): decode check and the bf16 expansion at init
 void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n_blocks16,
                         uint16_t* out, hipStream_t s);
+// groups of 16 E4M3 bytes -> exact bf16 with the in-register decoder (tensor scale not applied)
+void launch_fp8_dequant(const uint8_t* codes, long long n_groups16, uint16_t* out, hipStream_t s);
 
 }  // namespace lmoe

@@ -122,6 +122,11 @@ struct Buffers {
   uint16_t* hs_lo = nullptr;
   uint8_t* w1_scale_sm = nullptr;  // FP4: expert block scales in the mid kernel's stage-major order
   uint8_t* w2_scale_sm = nullptr;
+  // exact bf16 values of FP4 / FP8 dense weights for the LDS-tiled kernel (T > 64)
+  uint16_t* s1_bf16 = nullptr;
+  uint16_t* s2_bf16 = nullptr;
+  uint16_t* wd_bf16 = nullptr;
+  uint16_t* wu_bf16 = nullptr;
 };
 
 struct Layout {
@@ -138,8 +143,13 @@ int check_config(const latentmoe_config* c) {
   if (c->d <= 0 || c->latent <= 0 || c->n_experts <= 0 || c->top_k <= 0 ||
       c->expert_hidden <= 0 || c->shared_hidden <= 0 || c->max_tokens <= 0)
     return LATENTMOE_ERR_INVALID_ARG;
-  if (c->expert_format != LATENTMOE_EXPERTS_BF16 &&
-      c->expert_format != LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16)
+  if (c->expert_format != LATENTMOE_FORMAT_BF16 &&
+      c->expert_format != LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16)
+    return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->shared_format != LATENTMOE_FORMAT_BF16 &&
+      c->shared_format != LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16)
+    return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->proj_format != LATENTMOE_FORMAT_BF16 && c->proj_format != LATENTMOE_FORMAT_FP8_E4M3)
     return LATENTMOE_ERR_UNSUPPORTED;
   if (c->d % 64 || c->latent % 64 || c->expert_hidden % 64 || c->shared_hidden % 64)
     return LATENTMOE_ERR_UNSUPPORTED;
@@ -215,6 +225,16 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
     L.add((void**)&b.w1_scale_sm, sc_bytes);
     L.add((void**)&b.w2_scale_sm, sc_bytes);
   }
+  if (c.max_tokens > STREAM_ROWS_BIG) {  // some dense GEMMs run on the LDS-tiled kernel
+    if (c.shared_format != LATENTMOE_FORMAT_BF16) {
+      L.add((void**)&b.s1_bf16, (size_t)c.shared_hidden * c.d * 2);
+      L.add((void**)&b.s2_bf16, (size_t)c.d * c.shared_hidden * 2);
+    }
+    if (c.proj_format != LATENTMOE_FORMAT_BF16) {
+      L.add((void**)&b.wd_bf16, (size_t)c.latent * c.d * 2);
+      L.add((void**)&b.wu_bf16, (size_t)c.d * c.latent * 2);
+    }
+  }
   return L;
 }
 
@@ -285,9 +305,11 @@ GemmParams base_params() {
 }
 
 // dense GEMM C[T, N] = sum_seg A_seg[T, K_seg] B_seg[N, K_seg]^T with a final epilogue;
-// returns the number of k splits (with force_partial the caller reduces them)
+// returns the number of k splits (with force_partial the caller reduces them).  fmt is
+// seg[0].B's stored format; the LDS-tiled kernel reads bf16_B (its exact bf16 values)
+// instead when fmt is not bf16.
 int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool force_partial,
-              float* partial = nullptr) {
+              float* partial = nullptr, int fmt = WF_BF16, const uint16_t* bf16_B = nullptr) {
   int Ktot = 0;
   for (int i = 0; i < p.nseg; ++i) Ktot += p.seg[i].K;
   Plan pl = plan_dense(T, p.N, Ktot);
@@ -306,10 +328,15 @@ int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool fo
     p.partial = partial ? partial : h->b.partial;
     p.partial_stride = (long long)T * p.N;
   }
-  if (pl.stream)
-    launch_gemm_stream(p, false, s);
-  else
+  if (pl.stream) {
+    launch_gemm_stream(p, fmt, s);
+  } else {
+    if (fmt != WF_BF16) {
+      p.seg[0].B = bf16_B;
+      p.b_scale = nullptr;
+    }
     launch_gemm_big(p, s);
+  }
   if (use_partial && !force_partial) {
     GemmParams r = p;
     r.epi = final_epi;
@@ -351,10 +378,16 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
   if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
       !w->shared_w1 || !w->shared_w2)
     return LATENTMOE_ERR_INVALID_ARG;
-  const bool fp4 = cfg->expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16;
+  const bool fp4 = cfg->expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
   if (fp4 && (!w->expert_w1_scale || !w->expert_w2_scale || !w->expert_w1_tscale ||
               !w->expert_w2_tscale))
     return LATENTMOE_ERR_INVALID_ARG;
+  const bool shared_fp4 = cfg->shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
+  if (shared_fp4 && (!w->shared_w1_scale || !w->shared_w2_scale || !w->shared_w1_tscale ||
+                     !w->shared_w2_tscale))
+    return LATENTMOE_ERR_INVALID_ARG;
+  const bool proj_fp8 = cfg->proj_format == LATENTMOE_FORMAT_FP8_E4M3;
+  if (proj_fp8 && (!w->w_down_tscale || !w->w_up_tscale)) return LATENTMOE_ERR_INVALID_ARG;
 
   latentmoe_handle_s* h = new (std::nothrow) latentmoe_handle_s();
   if (!h) return LATENTMOE_ERR_OUT_OF_MEMORY;
@@ -397,6 +430,18 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     launch_scale_stage_major(w->expert_w2_scale, h->b.w2_scale_sm, cfg->n_experts, cfg->latent,
                              cfg->expert_hidden, stream);
   }
+  const long long n_shared = (long long)cfg->shared_hidden * cfg->d;  // elements per matrix
+  const long long n_proj = (long long)cfg->latent * cfg->d;
+  if (h->b.s1_bf16) {
+    launch_fp4_dequant(static_cast<const uint8_t*>(w->shared_w1), w->shared_w1_scale,
+                       n_shared / 16, h->b.s1_bf16, stream);
+    launch_fp4_dequant(static_cast<const uint8_t*>(w->shared_w2), w->shared_w2_scale,
+                       n_shared / 16, h->b.s2_bf16, stream);
+  }
+  if (h->b.wd_bf16) {
+    launch_fp8_dequant(static_cast<const uint8_t*>(w->w_down), n_proj / 16, h->b.wd_bf16, stream);
+    launch_fp8_dequant(static_cast<const uint8_t*>(w->w_up), n_proj / 16, h->b.wu_bf16, stream);
+  }
   if (hipGetLastError() != hipSuccess) {
     latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
@@ -434,7 +479,9 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   Buffers& b = h->b;
   const int N = c.n_experts, K = c.top_k, d = c.d, L = c.latent, m = c.expert_hidden,
             ms = c.shared_hidden;
-  const bool fp4 = c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16;
+  const bool fp4 = c.expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
+  const int shared_fmt = c.shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 ? WF_FP4 : WF_BF16;
+  const int proj_fmt = c.proj_format == LATENTMOE_FORMAT_FP8_E4M3 ? WF_FP8 : WF_BF16;
   const long long TK = (long long)T * K;
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
@@ -462,11 +509,15 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     ps.lda = d;
     ps.ldb = d;
     ps.N = ms;
+    if (shared_fmt == WF_FP4) {
+      ps.b_scale = w.shared_w1_scale;
+      ps.b_tscale = w.shared_w1_tscale;
+    }
     ps.epi = EPI_SQRELU_HILO;
     ps.C = b.hs_hi;
     ps.C2 = b.hs_lo;
     ps.ldc = ms;
-    run_dense(h, ps, T, side, false, b.partial2);
+    run_dense(h, ps, T, side, false, b.partial2, shared_fmt, b.s1_bf16);
     tm.stop(LATENTMOE_STAGE_SHARED_UP, side);
 
     tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
@@ -477,10 +528,14 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     p2.lda = ms;
     p2.ldb = ms;
     p2.N = d;
+    if (shared_fmt == WF_FP4) {
+      p2.b_scale = w.shared_w2_scale;
+      p2.b_tscale = w.shared_w2_tscale;
+    }
     p2.epi = EPI_F32;
     p2.C = y;
     p2.ldc = d;
-    run_dense(h, p2, T, side, false, b.partial2);
+    run_dense(h, p2, T, side, false, b.partial2, shared_fmt, b.s2_bf16);
     tm.stop(LATENTMOE_STAGE_SHARED_DOWN, side);
 
     (void)hipEventRecord(h->ev_join, side);
@@ -494,11 +549,12 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     pd.lda = d;
     pd.ldb = d;
     pd.N = L;
+    if (proj_fmt == WF_FP8) pd.b_tscale = w.w_down_tscale;
     pd.epi = EPI_BF16_HILO;
     pd.C = b.z;
     pd.C2 = b.z_lo;
     pd.ldc = L;
-    run_dense(h, pd, T, side2, false, b.partial3);
+    run_dense(h, pd, T, side2, false, b.partial3, proj_fmt, b.wd_bf16);
     tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
     (void)hipEventRecord(h->ev_join2, side2);
   };
@@ -594,7 +650,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     else if (rows_per_tile == STREAM_ROWS_BIG && LMOE_MID_FP4 && gemm_mid_supports(g, fp4))
       launch_gemm_mid(g, fp4, s);
     else
-      launch_gemm_stream(g, fp4, s);
+      launch_gemm_stream(g, fp4 ? WF_FP4 : WF_BF16, s);
   };
 
   tm.start(LATENTMOE_STAGE_EXPERT_UP);
@@ -652,10 +708,11 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pp.lda = L;
   pp.ldb = L;
   pp.N = d;
+  if (proj_fmt == WF_FP8) pp.b_tscale = w.w_up_tscale;
   pp.epi = EPI_F32_ADD;
   pp.C = y;
   pp.ldc = d;
-  run_dense(h, pp, T, s, false);
+  run_dense(h, pp, T, s, false, nullptr, proj_fmt, b.wu_bf16);
   tm.stop(LATENTMOE_STAGE_UP_PROJ);
   tm.done();
   h->last_T = T;
@@ -784,6 +841,13 @@ int latentmoe_fp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t n_
   if (!codes || !scales || !out || n_blocks < 0) return LATENTMOE_ERR_INVALID_ARG;
   (void)hipGetLastError();
   launch_fp4_dequant(codes, scales, n_blocks, out, s);
+  return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}
+
+int latentmoe_fp8_decode(const uint8_t* codes, int64_t n_groups, uint16_t* out, hipStream_t s) {
+  if (!codes || !out || n_groups < 0) return LATENTMOE_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  launch_fp8_dequant(codes, n_groups, out, s);
   return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }
 

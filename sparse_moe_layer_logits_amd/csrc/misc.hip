@@ -1,7 +1,8 @@
-// Split-K reduction, gated combine, FP4 decode check.
+// Split-K reduction, gated combine, FP4 / FP8 decoders (checks and bf16 expansion).
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "fp4.hpp"
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace lmoe {
@@ -94,6 +95,21 @@ void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n
   if (n_blocks16 <= 0) return;
   fp4_dequant_kernel<<<(unsigned)((n_blocks16 + 255) / 256), 256, 0, s>>>(codes, scales,
                                                                           n_blocks16, out);
+}
+
+// decode n_groups16 groups of 16 E4M3 bytes to bf16
+__global__ void fp8_dequant_kernel(const uint8_t* __restrict__ codes, long long ng,
+                                   uint16_t* __restrict__ out) {
+  const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= ng) return;
+  const u32x4_t c = ld128(codes + 16 * g);
+  st128(out + 16 * g, fp8x8_to_bf16(c[0], c[1]));
+  st128(out + 16 * g + 8, fp8x8_to_bf16(c[2], c[3]));
+}
+
+void launch_fp8_dequant(const uint8_t* codes, long long n_groups16, uint16_t* out, hipStream_t s) {
+  if (n_groups16 <= 0) return;
+  fp8_dequant_kernel<<<(unsigned)((n_groups16 + 255) / 256), 256, 0, s>>>(codes, n_groups16, out);
 }
 
 }  // namespace lmoe

@@ -124,10 +124,19 @@ def full_check(wl, x, W, tol=1e-2, extra=("z", "z_lo", "y_lat", "y_lat_lo", "cou
     return out, ref, ratio
 
 
-def sampled_check(name, n_sample, tol, seed=0):
+def tolerance(wl):
+    """Output bound relative to rms(oracle): 3e-2 when any matrix is stored in FP4
+    (the oracle decodes the same bytes), 1e-2 otherwise."""
+    return 3e-2 if "fp4" in (wl.experts, wl.shared) else 1e-2
+
+
+def sampled_check(name, n_sample, tol, seed=0, T=None):
     """Full-size workload: top-K on every token against the oracle's fp64 logits,
-    bucketing invariants on every token, outputs on a spread sample of tokens."""
+    bucketing invariants on every token, outputs on a spread sample of tokens.
+    T: run the first T tokens of the workload's batch instead of all."""
     wl = synth.WORKLOADS[name]
+    if T is not None:
+        wl = wl.replace(T=T)
     t0 = time.time()
     x, W = synth.make(wl, seed, redraws=synth.load_redraws(name, seed))
     log("%s: generated inputs in %.1fs" % (name, time.time() - t0))

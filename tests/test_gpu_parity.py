@@ -10,7 +10,8 @@ import pytest
 import oracle
 from sparse_moe_layer_logits_amd import binding, synth
 
-from gpu_common import check_bucketing, check_topk, check_y, full_check, log, run_layer, sampled_check
+from gpu_common import (check_bucketing, check_topk, check_y, full_check, log, run_layer,
+                        sampled_check, tolerance)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +61,24 @@ def test_fp4_decoder_exhaustive():
     ref = oracle.fp4_dequant(packed, sc[:, None], np.float32(1.0))
     ref_bits = synth.f32_to_bf16_bits(ref.astype(np.float32))
     assert np.array_equal(oracle.bf16_to_f64(ref_bits), ref)   # products are bf16-exact
+    assert np.array_equal(got, ref_bits)
+
+
+def test_fp8_decoder_exhaustive():
+    import torch
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    # 16 groups of 16 bytes: every finite code, each at several byte positions
+    codes = np.concatenate([finite, finite[:2]])
+    codes = np.stack([np.roll(codes, 5 * i) for i in range(4)]).reshape(-1, 16)
+    out = torch.empty(codes.shape, dtype=torch.int16, device="cuda")
+    cd = binding.to_device(codes)
+    binding.latentmoe_fp8_decode(cd.data_ptr(), codes.shape[0], out.data_ptr(),
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    ref = oracle.fp8_dequant(codes, np.float32(1.0))
+    ref_bits = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    assert np.array_equal(oracle.bf16_to_f64(ref_bits), ref)   # E4M3 values are bf16-exact
     assert np.array_equal(got, ref_bits)
 
 
@@ -156,6 +175,32 @@ def test_fp4_experts_small():
     full_check(wl, x, W, tol=3e-2)
 
 
+@pytest.mark.parametrize("experts,shared,proj", [("bf16", "fp4", "bf16"), ("bf16", "bf16", "fp8"),
+                                                 ("fp4", "fp4", "fp8")])
+def test_precision_mix_stream_path(experts, shared, proj):
+    # <= 64 tokens: the FP4 shared expert and FP8 projections are streamed and decoded
+    # in registers; d = 512 splits the K = d GEMMs in two (partials, then the reduce
+    # applies the tensor scale)
+    wl = small_wl(T=40, d=512, latent=128, n_experts=32, top_k=4, expert_hidden=192,
+                  shared_hidden=320, experts=experts, shared=shared, proj=proj)
+    x, W = gen(wl, 17)
+    log("precision mix, stream path", wl)
+    full_check(wl, x, W, tol=tolerance(wl))
+
+
+def test_precision_mix_tiled_path():
+    # > 64 tokens: dense GEMMs on the LDS-tiled kernel read the bf16 values expanded
+    # at init, the tensor scales still applied in the epilogues; then a 40-token call
+    # on the same handle streams the stored bytes
+    wl = small_wl(T=300, d=256, latent=128, n_experts=32, top_k=8, expert_hidden=192,
+                  shared_hidden=320, shared="fp4", proj="fp8")
+    x, W = gen(wl, 18)
+    log("precision mix, tiled path", wl)
+    full_check(wl, x, W, tol=tolerance(wl))
+    wl40 = wl.replace(T=40)
+    full_check(wl40, x[:40], W, tol=tolerance(wl), max_tokens=300)
+
+
 def test_edge_token_counts_and_reuse():
     import torch
     wl = small_wl(T=33, d=256, latent=64, n_experts=16, top_k=4)
@@ -190,6 +235,16 @@ def test_super_decode_full():
 
 def test_super_fp4_full():
     sampled_check("super_fp4", 24, 3e-2)
+
+
+def test_super_recipe_full():
+    # FP4 experts and shared expert, FP8 W_down / W_up, 1024 tokens
+    sampled_check("super_recipe", 24, tolerance(synth.WORKLOADS["super_recipe"]))
+
+
+def test_super_recipe_decode():
+    # the same weights at a 64-token decode step: every dense GEMM streams its stored format
+    sampled_check("super_recipe", 32, tolerance(synth.WORKLOADS["super_recipe"]), T=64)
 
 
 def test_super_prefill_full():
