@@ -182,7 +182,10 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
  * than 48 routed rows per expert on average, T*K/N > 48), the rows of each
  * expert whose gate is at least 0.1 come first (sorted by token), then the
  * others (sorted by token): only the first group carries z and h as hi + lo
- * pairs, the others as bf16 (H_LO is not written for them).
+ * pairs, the others as bf16 (H_LO is not written for them).  GEMMs with FP4 or
+ * FP8 weights take single bf16 activations (weight-only quantisation, 16-bit
+ * activations): with FP4 experts H_LO is not written, with an FP4 shared expert
+ * HS_LO is not written, and FP8 projections read Y_LAT but not Y_LAT_LO.
  * Errors: INVALID_ARG for an unknown `which`, a null pointer or more bytes
  * than the intermediate holds. */
 #define LATENTMOE_INTER_Z 0

@@ -1,13 +1,13 @@
 // Grouped MFMA GEMM for block-scaled FP4 expert weights and tiles of up to 64
-// activation rows (experts that see tens of tokens), dual (hi + lo bf16)
-// activations.
+// activation rows (experts that see tens of tokens); NP activation parts: bf16
+// (1) or a bf16 hi + lo pair (2).
 //
 // Block: W waves (W = 8, 7 or 4, the largest that divides N into 64-row wave
 // slabs); wave w owns four 16-row MFMA tiles of weight rows (n0 + 64w ..)
 // against the tile's activation rows in 16-row groups (a tile of r rows runs
 // ceil(r/16) groups, no more).  The k loop runs in stages of 128.  Stage s is
 // loaded into register set s % NS, NS - 1 stages ahead: the activation stage
-// (64 rows x 128 k, hi and lo, shared by all W waves) and the stage's E4M3
+// (64 rows x 128 k per part, shared by all W waves) and the stage's E4M3
 // block scales go through one of two LDS slots; each wave keeps its FP4 codes
 // (64 contiguous bytes per weight row and stage) in registers.  The block
 // scales are read from a stage-major copy made at initialisation, so one
@@ -56,14 +56,14 @@ __device__ __forceinline__ void md_wait_lgkm0() {
 
 // one thread's share of one stage: XP 16-byte pieces of each activation part,
 // the 8 scale bytes of one weight row, 16 code bytes per weight tile
-template <int XP>
+template <int XP, int NP>
 struct MdStage {
-  u32x4_t x[2][XP];      // [part][piece]
+  u32x4_t x[NP][XP];     // [part][piece]
   u32x2_t sc;            // E4M3 scales of weight row n0 + thread
   u32x4_t codes[MD_NT];  // 32 E2M1 codes per weight tile
 };
 
-template <int W, int EPI, int MT>
+template <int W, int EPI, int MT, int NP>
 __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int expert, int row0,
                                          int rows, int n0, int nbase, bool active) {
   constexpr int NTH = 64 * W;
@@ -71,7 +71,7 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   constexpr int XP = (MD_PIECES + NTH - 1) / NTH;
   // register sets: three fit next to two activation pieces per thread
   constexpr int NS = XP <= 2 ? LMOE_MID_SETS : 2;
-  constexpr int SLOTB = 2 * MD_PARTB + BN * 8;  // hi + lo + scales
+  constexpr int SLOTB = NP * MD_PARTB + BN * 8;  // activation parts + scales
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -104,36 +104,37 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   for (int nt = 0; nt < MD_NT; ++nt) {
     const uint32_t n = wrow0 + nt * 16 + r16;
     w_off[nt] = n * (uint32_t)(p.ldb / 2) + 16u * g;
-    s_lds[nt] = 2 * MD_PARTB + (n - n0) * 8 + 2 * g;
+    s_lds[nt] = NP * MD_PARTB + (n - n0) * 8 + 2 * g;
   }
   // scales, stage-major [expert][stage][N][8]: thread tid moves row n0 + tid
   // (the last row below N past the end)
   const uint8_t* Sb = p.b_scale_sm + ((size_t)expert * P * p.N + min(n0 + tid, p.N - 1)) * 8;
   const size_t s_stage = (size_t)p.N * 8;
 
-  auto issue = [&](MdStage<XP>& st, int ps) {
+  auto issue = [&](MdStage<XP, NP>& st, int ps) {
     const uint8_t* xh = Xhi + ps * (MD_KS * 2);
-    const uint8_t* xl = Xlo + ps * (MD_KS * 2);
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       st.x[0][i] = *reinterpret_cast<const u32x4_t*>(xh + x_off[i]);
-      st.x[1][i] = *reinterpret_cast<const u32x4_t*>(xl + x_off[i]);
+      if constexpr (NP == 2)
+        st.x[NP - 1][i] = *reinterpret_cast<const u32x4_t*>(Xlo + ps * (MD_KS * 2) + x_off[i]);
     }
     st.sc = *reinterpret_cast<const u32x2_t*>(Sb + ps * s_stage);
     const uint8_t* wb = Wb + ps * (MD_KS / 2);
 #pragma unroll
     for (int nt = 0; nt < MD_NT; ++nt) st.codes[nt] = *reinterpret_cast<const u32x4_t*>(wb + w_off[nt]);
   };
-  auto stash = [&](const MdStage<XP>& st, int s) {
+  auto stash = [&](const MdStage<XP, NP>& st, int s) {
     uint8_t* slot = smem + (s & 1) * SLOTB;
 #pragma unroll
     for (int i = 0; i < XP; ++i) {
       if (XP * NTH == MD_PIECES || i * NTH + tid < MD_PIECES) {
-        *reinterpret_cast<u32x4_t*>(slot + x_lds[i]) = st.x[0][i];
-        *reinterpret_cast<u32x4_t*>(slot + MD_PARTB + x_lds[i]) = st.x[1][i];
+#pragma unroll
+        for (int part = 0; part < NP; ++part)
+          *reinterpret_cast<u32x4_t*>(slot + part * MD_PARTB + x_lds[i]) = st.x[part][i];
       }
     }
-    *reinterpret_cast<u32x2_t*>(slot + 2 * MD_PARTB + tid * 8) = st.sc;
+    *reinterpret_cast<u32x2_t*>(slot + NP * MD_PARTB + tid * 8) = st.sc;
   };
 
   f32x4_t acc[MD_NT][MT];
@@ -142,7 +143,7 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
     for (int b = 0; b < MT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const MdStage<XP>& st, int s) {
+  auto compute = [&](const MdStage<XP, NP>& st, int s) {
     const uint8_t* slot = smem + (s & 1) * SLOTB;
     float sc[MD_NT][2];
 #pragma unroll
@@ -153,11 +154,11 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x4_t xf[2][MT];
+      u32x4_t xf[NP][MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int part = 0; part < 2; ++part)
+        for (int part = 0; part < NP; ++part)
           xf[part][mt] = *reinterpret_cast<const u32x4_t*>(slot + md_off(part, mt * 16 + r16, 4 * g + j));
       u32x4_t wf[MD_NT];
 #pragma unroll
@@ -166,8 +167,9 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
       for (int nt = 0; nt < MD_NT; ++nt) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[nt][mt] = mfma_16x16x32(wf[nt], xf[0][mt], acc[nt][mt]);
-          acc[nt][mt] = mfma_16x16x32(wf[nt], xf[1][mt], acc[nt][mt]);
+#pragma unroll
+          for (int part = 0; part < NP; ++part)
+            acc[nt][mt] = mfma_16x16x32(wf[nt], xf[part][mt], acc[nt][mt]);
         }
       }
     }
@@ -182,7 +184,7 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   // sched_barrier keeps each stage's loads together and in stage order.  The
   // trip count is padded to a multiple of NS (one loop exit; a padding step
   // only moves data) so the register sets stay static.
-  MdStage<XP> st[NS];
+  MdStage<XP, NP> st[NS];
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) {
     issue(st[i], min(i, P - 1));
@@ -214,12 +216,12 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   }
 }
 
-template <int W>
+template <int W, int NP>
 constexpr int mid_lds_bytes() {
-  return 2 * (2 * MD_PARTB + 64 * W * 8);
+  return 2 * (NP * MD_PARTB + 64 * W * 8);
 }
 
-template <int W, int EPI>
+template <int W, int EPI, int NP>
 __global__ __launch_bounds__(64 * W) void gemm_mid_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int BN = 64 * W;
@@ -235,61 +237,76 @@ __global__ __launch_bounds__(64 * W) void gemm_mid_kernel(GemmParams p) {
   const int nbase = n0 + (threadIdx.x >> 6) * 16 * MD_NT;
   const bool active = nbase < p.N;  // wave-uniform; inactive waves still stage activations
   switch ((rows + 15) >> 4) {
-    case 1: mid_body<W, EPI, 1>(p, smem, expert, row0, rows, n0, nbase, active); break;
-    case 2: mid_body<W, EPI, 2>(p, smem, expert, row0, rows, n0, nbase, active); break;
-    case 3: mid_body<W, EPI, 3>(p, smem, expert, row0, rows, n0, nbase, active); break;
-    default: mid_body<W, EPI, 4>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    case 1: mid_body<W, EPI, 1, NP>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    case 2: mid_body<W, EPI, 2, NP>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    case 3: mid_body<W, EPI, 3, NP>(p, smem, expert, row0, rows, n0, nbase, active); break;
+    default: mid_body<W, EPI, 4, NP>(p, smem, expert, row0, rows, n0, nbase, active); break;
   }
 }
 
-template <int W, int EPI>
+template <int W, int EPI, int NP>
 static void mid_launch(const GemmParams& p, hipStream_t s) {
   const long long blocks = (long long)p.max_tiles * ((p.N + 64 * W - 1) / (64 * W));
   if (blocks <= 0) return;
-  gemm_mid_kernel<W, EPI><<<(unsigned)blocks, 64 * W, mid_lds_bytes<W>(), s>>>(p);
+  gemm_mid_kernel<W, EPI, NP><<<(unsigned)blocks, 64 * W, mid_lds_bytes<W, NP>(), s>>>(p);
 }
 
 // waves per block: the largest of 8, 7 that splits N into whole blocks, else 4
 static int mid_waves(int N) { return N % 512 == 0 ? 8 : N % 448 == 0 ? 7 : 4; }
 
-template <int EPI>
+template <int EPI, int NP>
 static void mid_launch_w(const GemmParams& p, hipStream_t s) {
   switch (mid_waves(p.N)) {
-    case 8: mid_launch<8, EPI>(p, s); break;
-    case 7: mid_launch<7, EPI>(p, s); break;
-    default: mid_launch<4, EPI>(p, s); break;
+    case 8: mid_launch<8, EPI, NP>(p, s); break;
+    case 7: mid_launch<7, EPI, NP>(p, s); break;
+    default: mid_launch<4, EPI, NP>(p, s); break;
   }
 }
 
+// epilogues offered: with a hi + lo activation, relu^2 to a pair or the gated fp32
+// rows; with a bf16 activation, relu^2 to bf16 or the gated fp32 rows
 bool gemm_mid_supports(const GemmParams& p, bool fp4) {
-  return fp4 && p.tile_expert && p.rows_per_tile <= MD_ROWS && p.a_lo && p.nseg == 1 &&
-         p.b_scale_sm && p.N % 64 == 0 && p.seg[0].K % MD_KS == 0 && p.seg[0].K >= MD_KS &&
-         (p.epi == EPI_SQRELU_HILO || p.epi == EPI_GATE_F32);
+  const bool epi_ok = p.a_lo ? (p.epi == EPI_SQRELU_HILO || p.epi == EPI_GATE_F32)
+                             : (p.epi == EPI_SQRELU_BF16 || p.epi == EPI_GATE_F32);
+  return fp4 && p.tile_expert && p.rows_per_tile <= MD_ROWS && p.nseg == 1 && epi_ok &&
+         p.b_scale_sm && p.N % 64 == 0 && p.seg[0].K % MD_KS == 0 && p.seg[0].K >= MD_KS;
 }
 
-template <int W, int EPI>
+template <int W, int EPI, int NP>
 static hipError_t mid_attr() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mid_kernel<W, EPI>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, mid_lds_bytes<W>());
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mid_kernel<W, EPI, NP>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, mid_lds_bytes<W, NP>());
+}
+
+template <int W>
+static hipError_t mid_attr_w() {
+  hipError_t e = mid_attr<W, EPI_SQRELU_HILO, 2>();
+  if (e == hipSuccess) e = mid_attr<W, EPI_GATE_F32, 2>();
+  if (e == hipSuccess) e = mid_attr<W, EPI_SQRELU_BF16, 1>();
+  if (e == hipSuccess) e = mid_attr<W, EPI_GATE_F32, 1>();
+  return e;
 }
 
 int gemm_mid_setup() {
-  hipError_t e = hipSuccess;
-  if (e == hipSuccess) e = mid_attr<8, EPI_SQRELU_HILO>();
-  if (e == hipSuccess) e = mid_attr<8, EPI_GATE_F32>();
-  if (e == hipSuccess) e = mid_attr<7, EPI_SQRELU_HILO>();
-  if (e == hipSuccess) e = mid_attr<7, EPI_GATE_F32>();
-  if (e == hipSuccess) e = mid_attr<4, EPI_SQRELU_HILO>();
-  if (e == hipSuccess) e = mid_attr<4, EPI_GATE_F32>();
+  hipError_t e = mid_attr_w<8>();
+  if (e == hipSuccess) e = mid_attr_w<7>();
+  if (e == hipSuccess) e = mid_attr_w<4>();
   return (int)e;
 }
 
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s) {
   (void)fp4;
-  if (p.epi == EPI_SQRELU_HILO)
-    mid_launch_w<EPI_SQRELU_HILO>(p, s);
-  else
-    mid_launch_w<EPI_GATE_F32>(p, s);
+  if (p.a_lo) {
+    if (p.epi == EPI_SQRELU_HILO)
+      mid_launch_w<EPI_SQRELU_HILO, 2>(p, s);
+    else
+      mid_launch_w<EPI_GATE_F32, 2>(p, s);
+  } else {
+    if (p.epi == EPI_SQRELU_BF16)
+      mid_launch_w<EPI_SQRELU_BF16, 1>(p, s);
+    else
+      mid_launch_w<EPI_GATE_F32, 1>(p, s);
+  }
 }
 
 // [E][N][K/16] -> [E][K/128][N][8]: one thread per 8-byte group

@@ -11,10 +11,13 @@
 // activations are the MFMA "B" operand (columns = token rows), so each lane
 // ends with four consecutive n of one row and stores them as one vector.
 //
-// k layout inside every 64-wide k block: lane group g = lane / 16 holds
-// k = 16g .. 16g+15; MFMA step j (0, 1) uses k = 16g + 8j .. 16g + 8j + 7.  The
-// same map is used for both operands, so the products pair up correctly, and a
-// block-scaled FP4 lane group covers exactly one 16-element scale block.
+// k layout inside every 64-wide k block (bf16, FP8): lane group g = lane / 16
+// holds k = 16g .. 16g+15; MFMA step j (0, 1) uses k = 16g + 8j .. 16g + 8j + 7.
+// FP4: lane group g holds the contiguous k range [16 PAIRS g, 16 PAIRS (g+1)) of
+// the chunk, so one lane reads its codes as 16-byte loads and all its block
+// scales (one per 16 k) as one 2- or 4-byte load; the 4-bit weights would
+// otherwise cost several times more memory requests per byte than bf16.
+// Both operands use the same map, so the products pair up correctly.
 //
 // DUAL: the activation comes as two bf16 parts (hi + lo); each weight
 // fragment feeds two MFMAs, so the weights are still read once.
@@ -29,23 +32,48 @@
 
 namespace lmoe {
 
+// global-memory (address space 1) pointers: the segment pointers are picked with
+// register selects, after which the compiler can no longer infer the address
+// space of a generic pointer and would issue flat loads (counted against the LDS
+// counter too, so every barrier would wait for the weight prefetches)
+typedef const __attribute__((address_space(1))) uint8_t* gptr8;
+typedef const __attribute__((address_space(1))) uint16_t* gptr16;
+typedef const __attribute__((address_space(1))) u32x4_t* gptr128;
+
+__device__ __forceinline__ u32x4_t gld128(gptr8 q) { return *reinterpret_cast<gptr128>(q); }
+__device__ __forceinline__ u32x4_t gld128(gptr16 q) { return *reinterpret_cast<gptr128>(q); }
+
 struct SegPtr {
-  const uint16_t* A;
-  const uint8_t* B;  // bytes
-  int kl;            // k inside the segment
+  gptr16 A;
+  gptr8 B;  // bytes
+  int kl;   // k inside the segment
 };
 
+// a kernel-argument pointer as a plain (uniform) value: selecting between such
+// values stays a register select, where a select between two argument loads may be
+// turned into one per-lane load from a selected address
+__device__ __forceinline__ uint64_t uniform_u64(const void* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// the segment holding global k index kg (at most three segments), branch-free: a
+// lane-dependent index into p.seg would make the compiler fetch the descriptor per
+// lane from memory and wait for every load in flight before using it
 __device__ __forceinline__ SegPtr seg_at(const GemmParams& p, int kg) {
-  int k = kg;
-  int s = 0;
-  while (s + 1 < p.nseg && k >= p.seg[s].K) {
-    k -= p.seg[s].K;
-    ++s;
-  }
+  const int k1 = p.seg[0].K, k2 = p.seg[0].K + p.seg[1].K;
+  const bool s1 = p.nseg > 1 && kg >= k1;
+  const bool s2 = p.nseg > 2 && kg >= k2;
+  const uint64_t a0 = uniform_u64(p.seg[0].A), a1 = uniform_u64(p.seg[1].A),
+                 a2 = uniform_u64(p.seg[2].A);
+  const uint64_t b0 = uniform_u64(p.seg[0].B), b1 = uniform_u64(p.seg[1].B),
+                 b2 = uniform_u64(p.seg[2].B);
   SegPtr r;
-  r.A = reinterpret_cast<const uint16_t*>(p.seg[s].A);
-  r.B = reinterpret_cast<const uint8_t*>(p.seg[s].B);
-  r.kl = k;
+  r.A = (gptr16)(s2 ? a2 : s1 ? a1 : a0);
+  r.B = (gptr8)(s2 ? b2 : s1 ? b1 : b0);
+  r.kl = kg - (s2 ? k2 : s1 ? k1 : 0);
   return r;
 }
 
@@ -58,15 +86,24 @@ struct BFrag<WF_BF16> {
 template <>
 struct BFrag<WF_FP4> {
   u32x2_t codes;   // 16 E2M1 codes
-  uint32_t scale;  // E4M3 byte
+  uint32_t scale;  // the lane's E4M3 block scales, one byte per 16 k (byte pr for sub-block pr)
 };
 template <>
 struct BFrag<WF_FP8> {
   u32x4_t codes;   // 16 E4M3 bytes: step 0 in words 0-1, step 1 in words 2-3
 };
 
+#ifndef LMOE_ST_FP4_RING
+#define LMOE_ST_FP4_RING 2
+#endif
+
+#ifndef LMOE_ST_FP4_WAVES
+#define LMOE_ST_FP4_WAVES 1
+#endif
+
 template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL>
-__global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
+    FMT == WF_FP4 ? LMOE_ST_FP4_WAVES : 1))) void gemm_stream_kernel(GemmParams p) {
   constexpr int MTMAX = ROWS / 16;
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int KC = 64 * PAIRS;                           // k per chunk
@@ -135,26 +172,55 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #pragma unroll
     for (int mt = 0; mt < MTMAX; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  static_assert(FMT != WF_FP4 || PAIRS == 2 || PAIRS == 4, "FP4 lane ranges need 2 or 4 pairs");
+  // FP4: does this lane group's k range of chunk c hold weights (within the chunk's pairs)?
+  auto fp4_live = [&](int c) { return g * PAIRS < 4 * min(PAIRS, npairs - c * PAIRS); };
   auto load_b = [&](BFrag<FMT> (&bf)[PAIRS][NT], int c) {
+    if constexpr (FMT == WF_FP4) {
+      // lane group g: sub-block pr of its range is k0 + 16 pr .. k0 + 16 pr + 15.  Every
+      // lane loads, so each chunk costs the same loads and the compiler's wait counts
+      // stay exact: a lane without data (a wave past N, or a group past the pairs of a
+      // short last chunk; PAIRS <= 4 makes groups wholly in or out) reads a valid
+      // address instead, and compute() zeroes its scales.
+      const bool live = fp4_live(c);
+      const SegPtr sp = seg_at(p, kbeg + c * PAIRS * 64);  // FP4 GEMMs have one segment
+      const long long k0 = sp.kl + (live ? 16 * PAIRS * g : 0);
 #pragma unroll
-    for (int pr = 0; pr < PAIRS; ++pr) {
-      const int pg = c * PAIRS + pr;
-      if (pg < npairs && wave_active) {
-        const SegPtr sp = seg_at(p, kbeg + pg * 64);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = min(nbase + nt * 16 + r16, p.N - 1);
+        u32x4_t cw[PAIRS / 2];
+        uint32_t sw;
+        const gptr8 bp = sp.B + (bexp + (long long)n * p.ldb + k0) / 2;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = nbase + nt * 16 + r16;
-          const long long kk = sp.kl + 16 * g;
-          if constexpr (FMT == WF_FP4) {
-            const uint8_t* bp = sp.B + (bexp + (long long)n * p.ldb + kk) / 2;
-            bf[pr][nt].codes = *reinterpret_cast<const u32x2_t*>(bp);
-            bf[pr][nt].scale = p.b_scale[sexp + (long long)n * (p.ldb / 16) + kk / 16];
-          } else if constexpr (FMT == WF_FP8) {
-            bf[pr][nt].codes = ld128(sp.B + bexp + (long long)n * p.ldb + kk);
-          } else {
-            const uint8_t* bp = sp.B + 2 * (bexp + (long long)n * p.ldb + kk);
-            bf[pr][nt].v[0] = ld128(bp);
-            bf[pr][nt].v[1] = ld128(bp + 16);
+        for (int i = 0; i < PAIRS / 2; ++i) cw[i] = gld128(bp + 16 * i);
+        const uint8_t* sb = p.b_scale + sexp + (long long)n * (p.ldb / 16) + k0 / 16;
+        if constexpr (PAIRS == 4)
+          sw = *reinterpret_cast<const uint32_t*>(sb);
+        else
+          sw = *reinterpret_cast<const uint16_t*>(sb);
+#pragma unroll
+        for (int pr = 0; pr < PAIRS; ++pr) {
+          bf[pr][nt].codes = u32x2_t{cw[pr / 2][2 * (pr % 2)], cw[pr / 2][2 * (pr % 2) + 1]};
+          bf[pr][nt].scale = sw;  // all PAIRS scale bytes; compute() takes byte pr
+        }
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        const int pg = c * PAIRS + pr;
+        if (pg < npairs && wave_active) {
+          const SegPtr sp = seg_at(p, kbeg + pg * 64);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int n = nbase + nt * 16 + r16;
+            const long long kk = sp.kl + 16 * g;
+            if constexpr (FMT == WF_FP8) {
+              bf[pr][nt].codes = gld128(sp.B + bexp + (long long)n * p.ldb + kk);
+            } else {
+              const gptr8 bp = sp.B + 2 * (bexp + (long long)n * p.ldb + kk);
+              bf[pr][nt].v[0] = gld128(bp);
+              bf[pr][nt].v[1] = gld128(bp + 16);
+            }
           }
         }
       }
@@ -162,6 +228,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
   };
 
   u32x4_t a_regs[APT];
+  const gptr16 a_lo = (gptr16)uniform_u64(p.a_lo);
   auto load_a = [&](int c) {
 #pragma unroll
     for (int u = 0; u < APT; ++u) {
@@ -172,9 +239,40 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
       const int pg = c * PAIRS + (pc >> 3);
       if (pg < npairs) {
         const SegPtr sp = seg_at(p, kbeg + pg * 64);
-        const uint16_t* base = (DUAL && part) ? reinterpret_cast<const uint16_t*>(p.a_lo) : sp.A;
-        a_regs[u] = ld128(base + (long long)a_row[u] * p.lda + sp.kl + (pc & 7) * 8);
+        const gptr16 base = (DUAL && part) ? a_lo : sp.A;
+        a_regs[u] = gld128(base + (long long)a_row[u] * p.lda + sp.kl + (pc & 7) * 8);
       }
+    }
+  };
+  // FP4 path: every lane issues its loads (uniform load counts, as for the weights);
+  // pieces without data read the tile's first row / the chunk's first pair instead and
+  // store_a_sel writes zeros for them
+  const int a_src0 = p.row_index ? p.row_index[row0] : row0;
+  auto load_a_all = [&](u32x4_t (&ar)[APT], int c) {
+#pragma unroll
+    for (int u = 0; u < APT; ++u) {
+      const int piece = a_piece[u] < 0 ? 0 : a_piece[u];
+      const int part = piece / (ROWS * PPR);
+      const int pc = piece % PPR;
+      int pg = c * PAIRS + (pc >> 3);
+      pg = pg < npairs ? pg : c * PAIRS;
+      const SegPtr sp = seg_at(p, kbeg + pg * 64);
+      const gptr16 base = (DUAL && part) ? a_lo : sp.A;
+      const int src = a_row[u] < 0 ? a_src0 : a_row[u];
+      ar[u] = gld128(base + (long long)src * p.lda + sp.kl + (pc & 7) * 8);
+    }
+  };
+  auto store_a_sel = [&](const u32x4_t (&ar)[APT], int buf, int c) {
+#pragma unroll
+    for (int u = 0; u < APT; ++u) {
+      if (a_piece[u] < 0) continue;
+      const int part = a_piece[u] / (ROWS * PPR);
+      const int row = (a_piece[u] % (ROWS * PPR)) / PPR;
+      const int pc = a_piece[u] % PPR;
+      const int phys = pc ^ (row & 15);
+      const bool ok = a_row[u] >= 0 && c * PAIRS + (pc >> 3) < npairs;
+      *reinterpret_cast<u32x4_t*>(&As[buf][(part * ROWS + row) * ROWB + phys * 16]) =
+          ok ? ar[u] : zero128();
     }
   };
   auto store_a = [&](int buf) {
@@ -188,45 +286,98 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
       *reinterpret_cast<u32x4_t*>(&As[buf][(part * ROWS + row) * ROWB + phys * 16]) = a_regs[u];
     }
   };
+  // MFMAs of one 8-k step: bw holds the weights, `piece` the step's 16-byte column
+  // of the activation rows in LDS (k = 8 piece .. 8 piece + 7 of the chunk)
+  auto mfma_step = [&](const u32x4_t (&bw)[NT], int piece, int buf) {
+#pragma unroll
+    for (int mt = 0; mt < MTMAX; ++mt) {
+      if (mt < MT) {
+        const int row = mt * 16 + r16;
+        const int phys = piece ^ (row & 15);
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
+              &As[buf][(part * ROWS + row) * ROWB + phys * 16]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma_16x16x32(bw[nt], av, acc[nt][mt]);
+        }
+      }
+    }
+  };
   auto compute = [&](const BFrag<FMT> (&bf)[PAIRS][NT], int buf, int c) {
     if (!wave_active) return;
+    if constexpr (FMT == WF_FP4) {
+      // every step carries data from the live lane groups: no per-pair skip; the other
+      // groups hold re-read weights, zeroed through their scales
+      const bool live = fp4_live(c);
 #pragma unroll
-    for (int pr = 0; pr < PAIRS; ++pr) {
-      const int pg = c * PAIRS + pr;
-      if (pg < npairs) {
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        float sc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          sc[nt] = live ? e4m3_to_f32(bf[pr][nt].scale >> (8 * pr)) : 0.0f;  // reads the low byte
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
           u32x4_t bw[NT];
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            if constexpr (FMT == WF_FP4) {
-              const float sc = e4m3_to_f32(bf[pr][nt].scale);
-              bw[nt] = fp4x8_to_bf16(bf[pr][nt].codes[js], sc);
-            } else if constexpr (FMT == WF_FP8) {
-              bw[nt] = fp8x8_to_bf16(bf[pr][nt].codes[2 * js], bf[pr][nt].codes[2 * js + 1]);
-            } else {
-              bw[nt] = bf[pr][nt].v[js];
+          for (int nt = 0; nt < NT; ++nt) bw[nt] = fp4x8_to_bf16(bf[pr][nt].codes[js], sc[nt]);
+          mfma_step(bw, 2 * PAIRS * g + 2 * pr + js, buf);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < PAIRS; ++pr) {
+        const int pg = c * PAIRS + pr;
+        if (pg < npairs) {
+#pragma unroll
+          for (int js = 0; js < 2; ++js) {
+            u32x4_t bw[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              if constexpr (FMT == WF_FP8)
+                bw[nt] = fp8x8_to_bf16(bf[pr][nt].codes[2 * js], bf[pr][nt].codes[2 * js + 1]);
+              else
+                bw[nt] = bf[pr][nt].v[js];
             }
-          }
-#pragma unroll
-          for (int mt = 0; mt < MTMAX; ++mt) {
-            if (mt < MT) {
-              const int row = mt * 16 + r16;
-              const int phys = (pr * 8 + 2 * g + js) ^ (row & 15);
-#pragma unroll
-              for (int part = 0; part < NPART; ++part) {
-                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
-                    &As[buf][(part * ROWS + row) * ROWB + phys * 16]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt][mt] = mfma_16x16x32(bw[nt], av, acc[nt][mt]);
-              }
-            }
+            mfma_step(bw, pr * 8 + 2 * g + js, buf);
           }
         }
       }
     }
   };
 
+  if constexpr (FMT == WF_FP4) {
+    // FP4 fragments are small (3 registers per pair): rings of R chunks of weights and
+    // activation pieces (registers) keep R - 2 chunks of loads in flight while a chunk
+    // is computed.  Step cc loads chunk cc + R - 1 (activations first, then weights) and
+    // moves chunk cc + 1's activations to LDS; loads complete in order, so that wait
+    // leaves the younger chunks in flight.  Every step issues the same loads (clamped
+    // to the last chunk past the end) and the loop has one exit, so the compiler's
+    // wait counts stay exact.
+    constexpr int R = LMOE_ST_FP4_RING;
+    static_assert(R == 2 || R == 4, "ring of 2 or 4 chunks");
+    BFrag<FMT> ring[R][PAIRS][NT];
+    u32x4_t aring[R][APT];
+    const int last = nchunks - 1;
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) {
+      load_a_all(aring[i], min(i, last));
+      load_b(ring[i], min(i, last));
+    }
+    store_a_sel(aring[0], 0, 0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int cc = c + u;
+        load_a_all(aring[(u + R - 1) % R], min(cc + R - 1, last));
+        load_b(ring[(u + R - 1) % R], min(cc + R - 1, last));
+        if (cc < nchunks) compute(ring[u], u & 1, cc);
+        store_a_sel(aring[(u + 1) % R], (u + 1) & 1, min(cc + 1, last));
+        __syncthreads();
+      }
+    }
+  } else {
   BFrag<FMT> b0[PAIRS][NT], b1[PAIRS][NT];
   load_a(0);
   load_b(b0, 0);
@@ -251,6 +402,7 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
     if (has2) store_a(0);
     __syncthreads();
   }
+  }
 
   if (!wave_active) return;
 #pragma unroll
@@ -271,6 +423,12 @@ __global__ __launch_bounds__(W * 64) void gemm_stream_kernel(GemmParams p) {
 #ifndef LMOE_ST_PAIRS16
 #define LMOE_ST_PAIRS16 4
 #endif
+#ifndef LMOE_ST_PAIRS16_FP4
+#define LMOE_ST_PAIRS16_FP4 4
+#endif
+#ifndef LMOE_ST_PAIRS_FP4
+#define LMOE_ST_PAIRS_FP4 0
+#endif
 
 template <int ROWS, int PAIRS, int FMT, bool DUAL>
 static void launch_rows(const GemmParams& p, long long blocks, hipStream_t s) {
@@ -284,12 +442,15 @@ static void launch_fmt(const GemmParams& p, int rows, long long blocks, hipStrea
     // FP8 weights are the dense projections only: 64-row tiles
     launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
   } else {
+    constexpr bool F4 = FMT == WF_FP4;
+    constexpr int P16 = F4 ? LMOE_ST_PAIRS16_FP4 : LMOE_ST_PAIRS16;
+    constexpr int P = (F4 && LMOE_ST_PAIRS_FP4) ? LMOE_ST_PAIRS_FP4 : DUAL ? 2 : 4;
     if (rows == 16)
-      launch_rows<16, LMOE_ST_PAIRS16, FMT, DUAL>(p, blocks, s);
+      launch_rows<16, P16, FMT, DUAL>(p, blocks, s);
     else if (rows == 32)
-      launch_rows<32, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+      launch_rows<32, P, FMT, DUAL>(p, blocks, s);
     else
-      launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+      launch_rows<64, P, FMT, DUAL>(p, blocks, s);
   }
 }
 

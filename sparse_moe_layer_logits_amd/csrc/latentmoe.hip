@@ -58,6 +58,16 @@ constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kerne
 #ifndef LMOE_MID_FP4
 #define LMOE_MID_FP4 1  // FP4 experts with 64-row tiles use the mid kernel
 #endif
+// Activations of GEMMs whose weights are stored in FP4 or FP8 are single bf16
+// values: weight-only quantisation with 16-bit activations, the W4A16 mode in
+// which Hopper GPUs serve the NVFP4 checkpoint ("Nemotron 3.5 Super and
+// Lightning", limitations; "Nemotron 3 Ultra", contributions).  bf16 weights keep
+// the hi + lo pairs.  The bf16 rounding of an activation (2^-9 relative) is far
+// below the weight formats' own step.
+#ifndef LMOE_LOWP_A16
+#define LMOE_LOWP_A16 1
+#endif
+
 #ifndef LMOE_TARGET_BLOCKS
 #define LMOE_TARGET_BLOCKS 256
 #endif
@@ -482,6 +492,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const bool fp4 = c.expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
   const int shared_fmt = c.shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 ? WF_FP4 : WF_BF16;
   const int proj_fmt = c.proj_format == LATENTMOE_FORMAT_FP8_E4M3 ? WF_FP8 : WF_BF16;
+  const bool shared_a16 = shared_fmt != WF_BF16 && LMOE_LOWP_A16;  // single bf16 h_s
+  const bool expert_a16 = fp4 && LMOE_LOWP_A16;                   // single bf16 z, h
   const long long TK = (long long)T * K;
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
@@ -513,7 +525,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       ps.b_scale = w.shared_w1_scale;
       ps.b_tscale = w.shared_w1_tscale;
     }
-    ps.epi = EPI_SQRELU_HILO;
+    ps.epi = shared_a16 ? EPI_SQRELU_BF16 : EPI_SQRELU_HILO;
     ps.C = b.hs_hi;
     ps.C2 = b.hs_lo;
     ps.ldc = ms;
@@ -523,7 +535,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
     GemmParams p2 = base_params();
     p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
-    p2.a_lo = b.hs_lo;
+    p2.a_lo = shared_a16 ? nullptr : b.hs_lo;
     p2.nseg = 1;
     p2.lda = ms;
     p2.ldb = ms;
@@ -656,7 +668,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_EXPERT_UP);
   GemmParams pu = pe;
   pu.seg[0] = GemmSeg{b.z, w.expert_w1, L};
-  pu.a_lo = b.z_lo;
+  pu.a_lo = expert_a16 ? nullptr : b.z_lo;
   pu.lda = L;
   pu.ldb = L;
   pu.N = m;
@@ -666,9 +678,9 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pu.b_scale = fp4 ? w.expert_w1_scale : nullptr;
   pu.b_scale_sm = b.w1_scale_sm;
   pu.b_tscale = fp4 ? w.expert_w1_tscale : nullptr;
-  pu.epi = EPI_SQRELU_HILO;
+  pu.epi = expert_a16 ? EPI_SQRELU_BF16 : EPI_SQRELU_HILO;
   pu.C = b.h;
-  pu.C2 = b.h_lo;
+  pu.C2 = expert_a16 ? nullptr : b.h_lo;
   pu.ldc = m;
   launch_expert(pu, EPI_SQRELU_BF16);
   tm.stop(LATENTMOE_STAGE_EXPERT_UP);
@@ -676,7 +688,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
   GemmParams pw = pe;
   pw.seg[0] = GemmSeg{b.h, w.expert_w2, m};
-  pw.a_lo = b.h_lo;
+  pw.a_lo = expert_a16 ? nullptr : b.h_lo;
   pw.lda = m;
   pw.ldb = m;
   pw.N = L;
@@ -703,7 +715,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_UP_PROJ);
   GemmParams pp = base_params();
   pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
-  pp.a_lo = b.y_lat_lo;
+  pp.a_lo = proj_fmt != WF_BF16 && LMOE_LOWP_A16 ? nullptr : b.y_lat_lo;
   pp.nseg = 1;
   pp.lda = L;
   pp.ldb = L;

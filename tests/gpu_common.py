@@ -115,10 +115,14 @@ def full_check(wl, x, W, tol=1e-2, extra=("z", "z_lo", "y_lat", "y_lat_lo", "cou
     split = splits_rows(wl)
     if "y_lat" in out:
         # every stage carries ~16 bits: the latent sum matches closely (rows
-        # carried at bf16 on the large-tile path add up to ~3e-3 of it)
+        # carried at bf16 on the large-tile path add up to ~3e-3 of it).  FP4
+        # experts take bf16 activations (weight-only quantisation): their z and h
+        # roundings reach ~1e-2 of the latent sum, held to the FP4 output bound
         yl = oracle.bf16_to_f64(out["y_lat"]) + oracle.bf16_to_f64(out["y_lat_lo"])
         ry = ref["y_lat"]
-        assert np.max(np.abs(yl - ry)) <= (1e-2 if split else 1e-3) * np.sqrt(np.mean(ry ** 2))
+        err = np.max(np.abs(yl - ry)) / np.sqrt(np.mean(ry ** 2))
+        log("y_lat: max|gpu-oracle| / rms = %.3e" % err)
+        assert err <= (3e-2 if wl.experts == "fp4" else 1e-2 if split else 1e-3)
     if "counts" in out:
         check_bucketing(out, out["idx"], wl.n_experts, wl.top_k, out["gates"] if split else None)
     return out, ref, ratio
