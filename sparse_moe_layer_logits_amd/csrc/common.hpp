@@ -6,6 +6,7 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -36,14 +37,3 @@ __device__ __forceinline__ u32x4_t ld128(const void* p) { return *reinterpret_ca
 __device__ __forceinline__ void st128(void* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 __device__ __forceinline__ u32x4_t zero128() { u32x4_t z = {0u, 0u, 0u, 0u}; return z; }
-
-// E4M3FN byte -> float (bias 7, subnormals at exponent 0; the all-ones NaN code is not
-// produced by the quantiser and decodes here to 480).  Branch-free and exact: the
-// exponent/mantissa bits go straight into an fp32 with the bias moved from 7 to 127; a
-// subnormal code m is built as 2^-6 * (1 + m/8) and 2^-6 is then subtracted.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t em = b & 0x7Fu;
-  const uint32_t sub = em < 8u ? 1u : 0u;
-  const float v = __uint_as_float((em << 20) + ((120u + sub) << 23)) - (sub ? 0.015625f : 0.0f);
-  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
-}

@@ -1,15 +1,15 @@
 // Block-scaled FP4 (E2M1 values, one E4M3 scale per 16 input-dim elements)
-// decoded to bf16 in registers.  Format: "Nemotron 3 Super", section 3.6 (a
+// decoded to bf16 in registers; the E4M3 block scales go through the exact
+// hardware FP8 -> fp32 conversion (fp8.hpp).  Format: "Nemotron 3 Super", section 3.6 (a
 // per-tensor and a per-block scale); "Nemotron 3 Ultra" (E2M1 elements, E4M3
 // block scales).  Every E2M1 value times every E4M3 scale is a bf16 number,
 // so the decoded operand is exact; the per-tensor fp32 scale is applied to the
 // fp32 accumulator instead.
 #pragma once
 #include "common.hpp"
+#include "fp8.hpp"
 
 namespace lmoe {
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // the two E2M1 codes of byte I of `codes` (low nibble first) times a block scale
 // -> two bf16 in one word.  The conversion with a unit scale gives the exact

@@ -15,6 +15,12 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL));
 }
 
+// bytes 2*SEL and 2*SEL+1 of w as E4M3FN -> two fp32 (exact), e.g. FP4 block scales
+template <bool SEL>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, SEL);
+}
+
 // eight E4M3FN bytes (w0 = bytes 0..3, w1 = bytes 4..7) -> eight bf16
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   u32x4_t r;

@@ -149,8 +149,9 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
 #pragma unroll
     for (int nt = 0; nt < MD_NT; ++nt) {
       const uint32_t two = *reinterpret_cast<const uint16_t*>(slot + s_lds[nt]);
-      sc[nt][0] = e4m3_to_f32(two & 0xFFu);
-      sc[nt][1] = e4m3_to_f32(two >> 8);
+      const f32x2_t v = fp8x2_to_f32<false>(two);
+      sc[nt][0] = v.x;
+      sc[nt][1] = v.y;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

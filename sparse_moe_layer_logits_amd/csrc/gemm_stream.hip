@@ -175,6 +175,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   static_assert(FMT != WF_FP4 || PAIRS == 2 || PAIRS == 4, "FP4 lane ranges need 2 or 4 pairs");
   // FP4: does this lane group's k range of chunk c hold weights (within the chunk's pairs)?
   auto fp4_live = [&](int c) { return g * PAIRS < 4 * min(PAIRS, npairs - c * PAIRS); };
+  // FP4 GEMMs have one segment: the lane's weight-code and block-scale rows are set
+  // once (rows past N clamped to N - 1) and every chunk only adds its k offset
+  gptr8 w4_row[NT], s4_row[NT];
+  if constexpr (FMT == WF_FP4) {
+    const gptr8 B0 = (gptr8)uniform_u64(p.seg[0].B);
+    const gptr8 S0 = (gptr8)uniform_u64(p.b_scale);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = min(nbase + nt * 16 + r16, p.N - 1);
+      w4_row[nt] = B0 + (bexp + (long long)n * p.ldb) / 2;
+      s4_row[nt] = S0 + sexp + (long long)n * (p.ldb / 16);
+    }
+  }
   auto load_b = [&](BFrag<FMT> (&bf)[PAIRS][NT], int c) {
     if constexpr (FMT == WF_FP4) {
       // lane group g: sub-block pr of its range is k0 + 16 pr .. k0 + 16 pr + 15.  Every
@@ -182,26 +195,23 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
       // stay exact: a lane without data (a wave past N, or a group past the pairs of a
       // short last chunk; PAIRS <= 4 makes groups wholly in or out) reads a valid
       // address instead, and compute() zeroes its scales.
-      const bool live = fp4_live(c);
-      const SegPtr sp = seg_at(p, kbeg + c * PAIRS * 64);  // FP4 GEMMs have one segment
-      const long long k0 = sp.kl + (live ? 16 * PAIRS * g : 0);
+      const int k0 = kbeg + c * PAIRS * 64 + (fp4_live(c) ? 16 * PAIRS * g : 0);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int n = min(nbase + nt * 16 + r16, p.N - 1);
         u32x4_t cw[PAIRS / 2];
         uint32_t sw;
-        const gptr8 bp = sp.B + (bexp + (long long)n * p.ldb + k0) / 2;
+        const gptr8 bp = w4_row[nt] + k0 / 2;
 #pragma unroll
         for (int i = 0; i < PAIRS / 2; ++i) cw[i] = gld128(bp + 16 * i);
-        const uint8_t* sb = p.b_scale + sexp + (long long)n * (p.ldb / 16) + k0 / 16;
+        const gptr8 sb = s4_row[nt] + k0 / 16;
         if constexpr (PAIRS == 4)
-          sw = *reinterpret_cast<const uint32_t*>(sb);
+          sw = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(sb);
         else
-          sw = *reinterpret_cast<const uint16_t*>(sb);
+          sw = *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(sb);
 #pragma unroll
         for (int pr = 0; pr < PAIRS; ++pr) {
           bf[pr][nt].codes = u32x2_t{cw[pr / 2][2 * (pr % 2)], cw[pr / 2][2 * (pr % 2) + 1]};
-          bf[pr][nt].scale = sw;  // all PAIRS scale bytes; compute() takes byte pr
+          bf[pr][nt].scale = sw;  // all PAIRS scale bytes; compute() decodes them from bf[0]
         }
       }
     } else {
@@ -246,33 +256,38 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   };
   // FP4 path: every lane issues its loads (uniform load counts, as for the weights);
   // pieces without data read the tile's first row / the chunk's first pair instead and
-  // store_a_sel writes zeros for them
-  const int a_src0 = p.row_index ? p.row_index[row0] : row0;
-  auto load_a_all = [&](u32x4_t (&ar)[APT], int c) {
+  // store_a_sel writes zeros for them.  One segment: each piece's row pointer (with its
+  // 8-element offset in the pair) and LDS address are set once.
+  gptr16 a4_ptr[APT];
+  int a4_pair[APT], a4_lds[APT];
+  if constexpr (FMT == WF_FP4) {
+    const int a_src0 = p.row_index ? p.row_index[row0] : row0;
+    const gptr16 A0 = (gptr16)uniform_u64(p.seg[0].A);
 #pragma unroll
     for (int u = 0; u < APT; ++u) {
       const int piece = a_piece[u] < 0 ? 0 : a_piece[u];
       const int part = piece / (ROWS * PPR);
+      const int row = (piece % (ROWS * PPR)) / PPR;
       const int pc = piece % PPR;
-      int pg = c * PAIRS + (pc >> 3);
-      pg = pg < npairs ? pg : c * PAIRS;
-      const SegPtr sp = seg_at(p, kbeg + pg * 64);
-      const gptr16 base = (DUAL && part) ? a_lo : sp.A;
       const int src = a_row[u] < 0 ? a_src0 : a_row[u];
-      ar[u] = gld128(base + (long long)src * p.lda + sp.kl + (pc & 7) * 8);
+      a4_ptr[u] = ((DUAL && part) ? a_lo : A0) + (long long)src * p.lda + (pc & 7) * 8;
+      a4_pair[u] = pc >> 3;
+      a4_lds[u] = (part * ROWS + row) * ROWB + (pc ^ (row & 15)) * 16;
+    }
+  }
+  auto load_a_all = [&](u32x4_t (&ar)[APT], int c) {
+#pragma unroll
+    for (int u = 0; u < APT; ++u) {
+      const int pg = c * PAIRS + a4_pair[u];
+      ar[u] = gld128(a4_ptr[u] + kbeg + (pg < npairs ? pg : c * PAIRS) * 64);
     }
   };
   auto store_a_sel = [&](const u32x4_t (&ar)[APT], int buf, int c) {
 #pragma unroll
     for (int u = 0; u < APT; ++u) {
       if (a_piece[u] < 0) continue;
-      const int part = a_piece[u] / (ROWS * PPR);
-      const int row = (a_piece[u] % (ROWS * PPR)) / PPR;
-      const int pc = a_piece[u] % PPR;
-      const int phys = pc ^ (row & 15);
-      const bool ok = a_row[u] >= 0 && c * PAIRS + (pc >> 3) < npairs;
-      *reinterpret_cast<u32x4_t*>(&As[buf][(part * ROWS + row) * ROWB + phys * 16]) =
-          ok ? ar[u] : zero128();
+      const bool ok = a_row[u] >= 0 && c * PAIRS + a4_pair[u] < npairs;
+      *reinterpret_cast<u32x4_t*>(&As[buf][a4_lds[u]]) = ok ? ar[u] : zero128();
     }
   };
   auto store_a = [&](int buf) {
@@ -310,12 +325,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
       // every step carries data from the live lane groups: no per-pair skip; the other
       // groups hold re-read weights, zeroed through their scales
       const bool live = fp4_live(c);
+      // the lane's PAIRS block scales (bytes of one word, the same in every bf[pr])
+      float scl[NT][PAIRS];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int h = 0; h < PAIRS / 2; ++h) {
+          const f32x2_t v = h ? fp8x2_to_f32<true>(bf[0][nt].scale) : fp8x2_to_f32<false>(bf[0][nt].scale);
+          scl[nt][2 * h] = live ? v.x : 0.0f;
+          scl[nt][2 * h + 1] = live ? v.y : 0.0f;
+        }
+      }
 #pragma unroll
       for (int pr = 0; pr < PAIRS; ++pr) {
         float sc[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          sc[nt] = live ? e4m3_to_f32(bf[pr][nt].scale >> (8 * pr)) : 0.0f;  // reads the low byte
+        for (int nt = 0; nt < NT; ++nt) sc[nt] = scl[nt][pr];
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
           u32x4_t bw[NT];
@@ -466,7 +491,9 @@ void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s) {
   constexpr int W = LMOE_ST_W, NT = 1;
   // tile height: the grouped tile list's (16, 32 or 64 rows), 64 for dense GEMMs
   const int rows = !p.tile_expert ? 64 : p.rows_per_tile <= 16 ? 16 : p.rows_per_tile <= 32 ? 32 : 64;
-  if (fmt == WF_FP8 && rows != 64) return;  // not offered (callers check gemm_stream_supports)
+  // FP8 weights come only as dense GEMMs (64-row tiles) and FP4 ones with one
+  // segment (the FP4 path indexes seg[0] only); other shapes are not instantiated
+  if ((fmt == WF_FP8 && rows != 64) || (fmt == WF_FP4 && p.nseg != 1)) return;
   const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
   const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows - 1) / rows;
   const long long blocks = tiles * NQ * p.splits;

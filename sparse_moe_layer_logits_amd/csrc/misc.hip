@@ -85,7 +85,7 @@ __global__ void fp4_dequant_kernel(const uint8_t* __restrict__ codes,
   const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nb) return;
   const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes + 8 * b);
-  const float sc = e4m3_to_f32(scales[b]);
+  const float sc = fp8x2_to_f32<false>(scales[b]).x;
   st128(out + 16 * b, fp4x8_to_bf16(c[0], sc));
   st128(out + 16 * b + 8, fp4x8_to_bf16(c[1], sc));
 }
