@@ -455,55 +455,71 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
 #define LMOE_ST_PAIRS_FP4 0
 #endif
 
+#ifndef LMOE_ST_W_FP4
+#define LMOE_ST_W_FP4 8
+#endif
+#ifndef LMOE_ST_NT_FP4
+#define LMOE_ST_NT_FP4 1
+#endif
+
+// block shape: W waves of NT 16-row weight tiles each
+template <int FMT>
+struct StShape {
+  static constexpr int W = LMOE_ST_W, NT = 1;
+};
+template <>
+struct StShape<WF_FP4> {
+  static constexpr int W = LMOE_ST_W_FP4, NT = LMOE_ST_NT_FP4;
+};
+
 template <int ROWS, int PAIRS, int FMT, bool DUAL>
-static void launch_rows(const GemmParams& p, long long blocks, hipStream_t s) {
-  constexpr int W = LMOE_ST_W, NT = 1;
+static void launch_rows(const GemmParams& p, long long tiles, hipStream_t s) {
+  constexpr int W = StShape<FMT>::W, NT = StShape<FMT>::NT;
+  const long long NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
+  const long long blocks = tiles * NQ * p.splits;
+  if (blocks <= 0) return;
   gemm_stream_kernel<W, NT, ROWS, PAIRS, FMT, DUAL><<<(unsigned)blocks, W * 64, 0, s>>>(p);
 }
 
 template <int FMT, bool DUAL>
-static void launch_fmt(const GemmParams& p, int rows, long long blocks, hipStream_t s) {
+static void launch_fmt(const GemmParams& p, int rows, long long tiles, hipStream_t s) {
   if constexpr (FMT == WF_FP8) {
     // FP8 weights are the dense projections only: 64-row tiles
-    launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, blocks, s);
+    launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, tiles, s);
   } else {
     constexpr bool F4 = FMT == WF_FP4;
     constexpr int P16 = F4 ? LMOE_ST_PAIRS16_FP4 : LMOE_ST_PAIRS16;
     constexpr int P = (F4 && LMOE_ST_PAIRS_FP4) ? LMOE_ST_PAIRS_FP4 : DUAL ? 2 : 4;
     if (rows == 16)
-      launch_rows<16, P16, FMT, DUAL>(p, blocks, s);
+      launch_rows<16, P16, FMT, DUAL>(p, tiles, s);
     else if (rows == 32)
-      launch_rows<32, P, FMT, DUAL>(p, blocks, s);
+      launch_rows<32, P, FMT, DUAL>(p, tiles, s);
     else
-      launch_rows<64, P, FMT, DUAL>(p, blocks, s);
+      launch_rows<64, P, FMT, DUAL>(p, tiles, s);
   }
 }
 
 template <int FMT>
-static void launch_dual(const GemmParams& p, int rows, long long blocks, hipStream_t s) {
+static void launch_dual(const GemmParams& p, int rows, long long tiles, hipStream_t s) {
   if (p.a_lo != nullptr)
-    launch_fmt<FMT, true>(p, rows, blocks, s);
+    launch_fmt<FMT, true>(p, rows, tiles, s);
   else
-    launch_fmt<FMT, false>(p, rows, blocks, s);
+    launch_fmt<FMT, false>(p, rows, tiles, s);
 }
 
 void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s) {
-  constexpr int W = LMOE_ST_W, NT = 1;
   // tile height: the grouped tile list's (16, 32 or 64 rows), 64 for dense GEMMs
   const int rows = !p.tile_expert ? 64 : p.rows_per_tile <= 16 ? 16 : p.rows_per_tile <= 32 ? 32 : 64;
   // FP8 weights come only as dense GEMMs (64-row tiles) and FP4 ones with one
   // segment (the FP4 path indexes seg[0] only); other shapes are not instantiated
   if ((fmt == WF_FP8 && rows != 64) || (fmt == WF_FP4 && p.nseg != 1)) return;
-  const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
   const long long tiles = p.tile_expert ? p.max_tiles : (p.M + rows - 1) / rows;
-  const long long blocks = tiles * NQ * p.splits;
-  if (blocks <= 0) return;
   if (fmt == WF_FP4)
-    launch_dual<WF_FP4>(p, rows, blocks, s);
+    launch_dual<WF_FP4>(p, rows, tiles, s);
   else if (fmt == WF_FP8)
-    launch_dual<WF_FP8>(p, rows, blocks, s);
+    launch_dual<WF_FP8>(p, rows, tiles, s);
   else
-    launch_dual<WF_BF16>(p, rows, blocks, s);
+    launch_dual<WF_BF16>(p, rows, tiles, s);
 }
 
 }  // namespace lmoe
