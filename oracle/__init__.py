@@ -14,12 +14,16 @@ expert in the same FP4 format and W_down / W_up as per-tensor FP8 per the
 released precision mix ("Nemotron 3.5 Super and Lightning", 4-bit
 quantisation section).
 
+`ssm` holds the Mamba-2 state recurrence used to check the checkpoint + replay
+verification kernels ("Nemotron 3.5 Super and Lightning", serving section).
+
 Every function here is pinned by the CPU tests (closed forms, special cases
 that reduce to a textbook mixture, brute force on tiny inputs, exhaustive
 format tables).  Nothing here is pinned against values printed on the pages:
 the pages print no numeric LatentMoE example.
 """
 from .formats import bf16_to_f64, e2m1_to_f64, e4m3fn_to_f64, fp4_dequant, fp8_dequant  # noqa: F401
+from . import ssm  # noqa: F401
 from .latentmoe import (  # noqa: F401
     expert_ffn,
     forward,

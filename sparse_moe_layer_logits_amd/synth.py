@@ -86,6 +86,32 @@ WORKLOADS = {
                              experts="fp4", shared="fp4", proj="fp8"),
 }
 
+@dataclasses.dataclass(frozen=True)
+class SsmWorkload:
+    """Mamba-2 speculative-verify step: R requests, each verifying T tokens (the
+    drafts plus the verified token) against a checkpoint and a record buffer."""
+    name: str
+    R: int            # requests
+    T: int            # tokens verified per request
+    H: int            # heads
+    G: int            # groups (heads of a group share key and query)
+    P: int            # head dimension
+    N: int            # state dimension
+    cap: int = 16     # buffer capacity: records between checkpoints
+
+    def replace(self, **kw) -> "SsmWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+SSM_WORKLOADS = {
+    "ssm_tiny": SsmWorkload("ssm_tiny", R=3, T=4, H=8, G=2, P=64, N=128, cap=8),
+    # Super's Mamba shapes ("Nemotron 3 Super", section 3.1 table), 64 users each
+    # verifying 7 drafts + 1 token, 16-record buffer
+    "super_mamba_verify": SsmWorkload("super_mamba_verify", R=64, T=8, H=128, G=8, P=64,
+                                      N=128, cap=16),
+}
+
+
 # stream identifiers (one PCG64 stream per tensor / expert / row)
 TID_X = 1
 TID_ROUTER_W = 2
@@ -96,6 +122,14 @@ TID_EXPERT_W1 = 6
 TID_EXPERT_W2 = 7
 TID_SHARED_W1 = 8
 TID_SHARED_W2 = 9
+
+TID_SSM_STATE = 20
+TID_SSM_K = 21
+TID_SSM_V = 22
+TID_SSM_Q = 23
+TID_SSM_DT = 24
+TID_SSM_A = 25
+TID_SSM_LEN = 26
 
 FP4_BLOCK = 16
 
@@ -325,3 +359,35 @@ def make(wl: Workload | str, seed: int = 0, redraws: dict | None = None,
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     return make_x(wl, seed, redraws), make_weights(wl, seed, threads)
+
+
+# --------------------------------------------------------------------------
+# Mamba-2 verify inputs
+# --------------------------------------------------------------------------
+
+
+def make_ssm(wl: SsmWorkload, seed: int = 0) -> dict:
+    """Checkpoint, record buffer (with n_buf records per request) and the T tokens
+    to verify.  bf16 tensors as bit patterns, decays and lengths as fp32 / int32.
+
+    checkpoint ~ N(0, 1); keys and queries ~ N(0, 1/N); values ~ N(0, 1); decays
+    a = exp(-dt * A) with A ~ U[1, 16] per head and dt log-uniform on [1e-3, 1e-1]
+    per token and head (the usual Mamba-2 ranges); n_buf ~ U{0 .. cap - T}.
+    """
+    R, T, H, G, P, N, C = wl.R, wl.T, wl.H, wl.G, wl.P, wl.N, wl.cap
+    out = {"ckpt": _normal_bf16(seed, (TID_SSM_STATE,), (R, H, P, N), 1.0)}
+    A = _rng(seed, TID_SSM_A).uniform(1.0, 16.0, H)
+
+    def decays(key, L):
+        u = _rng(seed, TID_SSM_DT, key).uniform(np.log(1e-3), np.log(1e-1), (R, L, H))
+        return np.exp(-np.exp(u) * A).astype(np.float32)
+
+    out["buf_k"] = _normal_bf16(seed, (TID_SSM_K, 0), (R, C, G, N), 1.0 / np.sqrt(N))
+    out["buf_v"] = _normal_bf16(seed, (TID_SSM_V, 0), (R, C, H, P), 1.0)
+    out["buf_a"] = decays(0, C)
+    out["draft_q"] = _normal_bf16(seed, (TID_SSM_Q, 1), (R, T, G, N), 1.0 / np.sqrt(N))
+    out["draft_k"] = _normal_bf16(seed, (TID_SSM_K, 1), (R, T, G, N), 1.0 / np.sqrt(N))
+    out["draft_v"] = _normal_bf16(seed, (TID_SSM_V, 1), (R, T, H, P), 1.0)
+    out["draft_a"] = decays(1, T)
+    out["buf_len"] = _rng(seed, TID_SSM_LEN).integers(0, C - T + 1, R).astype(np.int32)
+    return out
