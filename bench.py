@@ -1,6 +1,7 @@
 """LatentMoE layer forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload super_decode]
+    python bench.py --workload super_mamba_verify     (Mamba-2 checkpoint + replay verify)
 
 One step is one whole layer forward (router, top-K, bucketing, W_down, grouped
 expert GEMMs, combine, shared expert, W_up) over one batch of seeded synthetic
@@ -134,9 +135,12 @@ def main():
                     help="also run a plain fp32 copy kernel of this size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel "
-              "sharding is described in DESIGN.md, not built); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (expert-parallel "
+              "sharding is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    from sparse_moe_layer_logits_amd import synth as _synth
+    if args.workload in _synth.SSM_WORKLOADS:
+        return bench_ssm(args)
 
     import torch
 
@@ -254,6 +258,146 @@ def main():
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(wl, x, W)
     print(json.dumps(result), flush=True)
+
+
+SSM_METRIC = "Mamba-2 speculative-verify tokens/s (checkpoint + replay); % HBM peak"
+
+
+def ssm_bytes(wl, lens):
+    """Algorithmic HBM bytes of one checkpoint + replay verify launch: every head's
+    checkpoint once, the buffered and new records, the outputs and the appended
+    records."""
+    R, T, H, G, P, N = wl.R, wl.T, wl.H, wl.G, wl.P, wl.N
+    n = int(np.sum(lens))
+    state = R * H * P * N * 2
+    reads = (n + 2 * R * T) * G * N * 2 + (n + R * T) * (H * P * 2 + H * 4)
+    writes = R * T * H * P * 4 + R * T * (G * N * 2 + H * P * 2 + H * 4)
+    return state + reads + writes
+
+
+def bench_ssm(args):
+    import torch
+
+    from sparse_moe_layer_logits_amd import binding, synth
+
+    wl = synth.SSM_WORKLOADS[args.workload]
+    d = synth.make_ssm(wl, args.seed)
+    torch.cuda.set_device(0)
+    dev = {k: binding.to_device(v) for k, v in d.items()}
+    shape = binding.ssm_shape(wl.H, wl.G, wl.P, wl.N, wl.cap)
+    st = torch.cuda.current_stream()
+    y = torch.empty((wl.R, wl.T, wl.H, wl.P), dtype=torch.float32, device="cuda")
+    states = torch.empty((wl.R, wl.T, wl.H, wl.P, wl.N), dtype=torch.int16, device="cuda")
+    lens0 = dev["buf_len"].clone()
+
+    def verify():
+        binding.ssm_replay_verify(shape, wl.R, wl.T, dev["ckpt"].data_ptr(), dev["buf_k"].data_ptr(),
+                                  dev["buf_v"].data_ptr(), dev["buf_a"].data_ptr(), dev["buf_len"].data_ptr(),
+                                  dev["draft_q"].data_ptr(), dev["draft_k"].data_ptr(),
+                                  dev["draft_v"].data_ptr(), dev["draft_a"].data_ptr(), y.data_ptr(),
+                                  st.cuda_stream)
+
+    def states_scheme():
+        binding.ssm_states_verify(shape, wl.R, wl.T, dev["ckpt"].data_ptr(), dev["draft_q"].data_ptr(),
+                                  dev["draft_k"].data_ptr(), dev["draft_v"].data_ptr(),
+                                  dev["draft_a"].data_ptr(), states.data_ptr(), y.data_ptr(), st.cuda_stream)
+
+    def timed(fn, steps, before=None):
+        """Mean ms per call, HIP events on the calls' stream around each call."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            if before:
+                before()
+            e0.record(st)
+            fn()
+            e1.record(st)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+
+    for _ in range(args.warmup):
+        verify()
+        states_scheme()
+    torch.cuda.synchronize()
+    # timed region: K verify steps back to back (the buffer counters are not advanced,
+    # so every step appends to the same slots and reads the same records)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        verify()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    verify_ms = timed(verify, args.steps)
+    states_ms = timed(states_scheme, args.steps)
+    ckpt0 = dev["ckpt"].clone()
+
+    def restore():
+        dev["buf_len"].copy_(lens0)
+        dev["ckpt"].copy_(ckpt0)
+
+    def flush():
+        binding.ssm_replay_flush(shape, wl.R, dev["ckpt"].data_ptr(), dev["buf_k"].data_ptr(),
+                                 dev["buf_v"].data_ptr(), dev["buf_a"].data_ptr(), dev["buf_len"].data_ptr(),
+                                 st.cuda_stream)
+    flush_ms = timed(flush, max(1, args.steps // 4), before=restore)
+    restore()
+    torch.cuda.synchronize()
+
+    lens = d["buf_len"]
+    kb = ssm_bytes(wl, lens)
+    states_bytes = wl.R * wl.H * wl.P * wl.N * 2 * (1 + wl.T) + wl.R * wl.T * wl.H * wl.P * 4
+    achieved = kb / (verify_ms * 1e-3) / 1e9
+    tokens = wl.R * wl.T
+    log("verify %.4f ms (events) / %.4f ms (wall), state-writing scheme %.4f ms, flush %.4f ms"
+        % (verify_ms, ms_per_step, states_ms, flush_ms))
+    result = {
+        "metric": SSM_METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal states, keys, values, queries; Mamba-2 decay ranges)",
+        "config": {"workload": wl.name, "requests": wl.R, "tokens_per_request": wl.T, "heads": wl.H,
+                   "groups": wl.G, "head_dim": wl.P, "state_dim": wl.N, "buffer_capacity": wl.cap,
+                   "buffered_records_mean": float(np.mean(lens)), "seed": args.seed,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "ssm_verify_kernel", "launch_ms": round(verify_ms, 5),
+                     "alg_bytes_per_launch": int(kb)},
+        "state_writing_scheme": {"launch_ms": round(states_ms, 5), "alg_bytes_per_launch": int(states_bytes),
+                                 "achieved_GBs": round(states_bytes / (states_ms * 1e-3) / 1e9, 2),
+                                 "replay_speedup": round(states_ms / verify_ms, 3)},
+        "flush": {"launch_ms": round(flush_ms, 5),
+                  "alg_bytes_per_launch": int(wl.R * wl.H * wl.P * wl.N * 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = ssm_cpu_baseline(wl, d)
+    print(json.dumps(result), flush=True)
+
+
+def ssm_cpu_baseline(wl, d, budget_s=10.0):
+    """The fp64 recurrence oracle on the host cores over whole requests, repeated
+    for about budget_s."""
+    import oracle
+    from oracle.formats import bf16_to_f64 as f
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.time()
+    tokens, r = 0, 0
+    while time.time() - t0 < budget_s or tokens == 0:
+        n = int(d["buf_len"][r % wl.R])
+        rr = r % wl.R
+        oracle.ssm.verify_outputs(f(d["ckpt"][rr]), f(d["buf_k"][rr]), f(d["buf_v"][rr]),
+                                  d["buf_a"][rr].astype(np.float64), n, f(d["draft_q"][rr]),
+                                  f(d["draft_k"][rr]), f(d["draft_v"][rr]), d["draft_a"][rr].astype(np.float64))
+        tokens += wl.T
+        r += 1
+    dt = time.time() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d whole requests (%d tokens each) of the %s batch, fp64 numpy recurrence, %.1f s"
+                      % (r, wl.T, wl.name, dt)}
 
 
 if __name__ == "__main__":

@@ -37,6 +37,13 @@ EXPORTED = [
     "latentmoe_workspace_bytes", "latentmoe_debug_copy", "latentmoe_profile_begin",
     "latentmoe_profile_end", "latentmoe_fp4_decode", "latentmoe_fp8_decode",
 ]
+# include/ssm_replay.h: Mamba-2 checkpoint + replay verification
+SSM_EXPORTED = ["ssm_check_shape", "ssm_replay_verify", "ssm_replay_commit", "ssm_replay_flush",
+                "ssm_states_verify"]
+SSM_OK = 0
+SSM_ERR_INVALID_ARG = -1
+SSM_ERR_UNSUPPORTED = -2
+SSM_ERR_HIP = -4
 
 
 class latentmoe_config(ctypes.Structure):
@@ -51,6 +58,10 @@ class latentmoe_weights(ctypes.Structure):
         "expert_w1_scale", "expert_w2_scale", "expert_w1_tscale", "expert_w2_tscale",
         "shared_w1", "shared_w2", "shared_w1_scale", "shared_w2_scale", "shared_w1_tscale",
         "shared_w2_tscale", "w_down_tscale", "w_up_tscale")]
+
+
+class ssm_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("heads", "groups", "head_dim", "state_dim", "capacity")]
 
 
 class LatentMoEError(RuntimeError):
@@ -86,7 +97,13 @@ def load(path: str = LIB_PATH):
                                           ctypes.POINTER(ctypes.c_int)]
     lib.latentmoe_fp4_decode.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
     lib.latentmoe_fp8_decode.argtypes = [vp, ctypes.c_int64, vp, vp]
-    for name in EXPORTED:
+    sp = ctypes.POINTER(ssm_shape)
+    lib.ssm_check_shape.argtypes = [sp]
+    lib.ssm_replay_verify.argtypes = [sp, i32, i32] + [vp] * 11  # 10 pointers + stream
+    lib.ssm_replay_commit.argtypes = [i32, vp, vp, vp]
+    lib.ssm_replay_flush.argtypes = [sp, i32] + [vp] * 6  # 5 pointers + stream
+    lib.ssm_states_verify.argtypes = [sp, i32, i32] + [vp] * 8  # 7 pointers + stream
+    for name in EXPORTED + SSM_EXPORTED:
         if name != "latentmoe_status_string":
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -162,6 +179,48 @@ def latentmoe_fp4_decode(codes_ptr: int, scales_ptr: int, n_blocks: int, out_ptr
 def latentmoe_fp8_decode(codes_ptr: int, n_groups: int, out_ptr: int, stream: int) -> None:
     _check("latentmoe_fp8_decode", load().latentmoe_fp8_decode(
         ctypes.c_void_p(codes_ptr), int(n_groups), ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream)))
+
+
+class SsmError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed with status %d" % (fn, status))
+        self.status = status
+
+
+def _ssm_check(fn, st):
+    if st != SSM_OK:
+        raise SsmError(fn, st)
+
+
+def _vp(x):
+    return ctypes.c_void_p(int(x))
+
+
+def ssm_check_shape(shape: ssm_shape) -> int:
+    return load().ssm_check_shape(ctypes.byref(shape))
+
+
+def ssm_replay_verify(shape, R, T, ckpt, buf_k, buf_v, buf_a, buf_len, q, k, v, a, y, stream):
+    """Device pointers (ints); see include/ssm_replay.h."""
+    _ssm_check("ssm_replay_verify", load().ssm_replay_verify(
+        ctypes.byref(shape), int(R), int(T), *[_vp(x) for x in (ckpt, buf_k, buf_v, buf_a, buf_len,
+                                                                q, k, v, a, y, stream)]))
+
+
+def ssm_replay_commit(R, accepted, buf_len, stream):
+    _ssm_check("ssm_replay_commit", load().ssm_replay_commit(
+        int(R), _vp(accepted), _vp(buf_len), _vp(stream)))
+
+
+def ssm_replay_flush(shape, R, ckpt, buf_k, buf_v, buf_a, buf_len, stream):
+    _ssm_check("ssm_replay_flush", load().ssm_replay_flush(
+        ctypes.byref(shape), int(R), *[_vp(x) for x in (ckpt, buf_k, buf_v, buf_a, buf_len, stream)]))
+
+
+def ssm_states_verify(shape, R, T, state, q, k, v, a, states_out, y, stream):
+    _ssm_check("ssm_states_verify", load().ssm_states_verify(
+        ctypes.byref(shape), int(R), int(T), *[_vp(x) for x in (state, q, k, v, a, states_out, y,
+                                                                stream)]))
 
 
 # ---- torch-facing convenience layer ----

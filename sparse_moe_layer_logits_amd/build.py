@@ -12,7 +12,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "liblatentmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["latentmoe.hip", "route.hip", "gemm_stream.hip", "gemm_big.hip", "gemm_mid.hip", "misc.hip"]
+SOURCES = ["latentmoe.hip", "route.hip", "gemm_stream.hip", "gemm_big.hip", "gemm_mid.hip", "misc.hip",
+           "ssm_replay.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # no packed fp32 instructions in device code

@@ -1,5 +1,6 @@
 """The C-ABI library: it builds, loads without a GPU, and exports every
-function that include/latentmoe.h declares.  No compute calls are made."""
+function that include/latentmoe.h and include/ssm_replay.h declare.  No compute
+calls are made."""
 import ctypes
 import os
 import re
@@ -10,12 +11,13 @@ from sparse_moe_layer_logits_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "latentmoe.h")
+SSM_HEADER = os.path.join(ROOT, "include", "ssm_replay.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER, prefix="latentmoe_"):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(latentmoe_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(%s[a-z0-9_]+)\s*\(" % prefix, text)))
 
 
 def test_header_declares_the_boundary():
@@ -23,6 +25,7 @@ def test_header_declares_the_boundary():
     for must in ("latentmoe_init", "latentmoe_forward", "latentmoe_destroy"):
         assert must in names
     assert set(names) == set(binding.EXPORTED)
+    assert set(declared_functions(SSM_HEADER, "ssm_")) == set(binding.SSM_EXPORTED)
 
 
 @pytest.fixture(scope="module")
@@ -33,8 +36,29 @@ def lib():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(SSM_HEADER, "ssm_"):
         assert hasattr(lib, name), name
+
+
+def test_ssm_shape_checks_on_the_host(lib):
+    ok = binding.ssm_shape(128, 8, 64, 128, 16)
+    assert binding.ssm_check_shape(ok) == binding.SSM_OK
+    for bad, st in ((binding.ssm_shape(128, 7, 64, 128, 16), binding.SSM_ERR_UNSUPPORTED),   # G does not divide H
+                    (binding.ssm_shape(128, 8, 48, 128, 16), binding.SSM_ERR_UNSUPPORTED),   # head dim
+                    (binding.ssm_shape(128, 8, 64, 96, 16), binding.SSM_ERR_UNSUPPORTED),    # state dim
+                    (binding.ssm_shape(128, 8, 64, 128, 64), binding.SSM_ERR_UNSUPPORTED),   # capacity
+                    (binding.ssm_shape(0, 8, 64, 128, 16), binding.SSM_ERR_INVALID_ARG)):
+        assert binding.ssm_check_shape(bad) == st
+    # argument checks happen before any device work
+    with pytest.raises(binding.SsmError) as e:
+        binding.ssm_replay_verify(ok, 1, 17, *([0] * 11))     # T above the capacity
+    assert e.value.status == binding.SSM_ERR_INVALID_ARG
+    with pytest.raises(binding.SsmError) as e:
+        binding.ssm_replay_verify(ok, 1, 8, *([0] * 11))      # null pointers
+    assert e.value.status == binding.SSM_ERR_INVALID_ARG
+    with pytest.raises(binding.SsmError) as e:
+        binding.ssm_replay_flush(ok, -1, *([0] * 6))
+    assert e.value.status == binding.SSM_ERR_INVALID_ARG
 
 
 def test_status_strings_and_host_side_validation(lib):
