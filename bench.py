@@ -30,6 +30,7 @@ KERNEL_SOURCES = {  # kernel -> source file whose hash pins stored counter data
     "gemm_stream_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_stream.hip",
     "gemm_mid_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_mid.hip",
     "gemm_big_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_big.hip",
+    "ssm_verify_kernel": "sparse_moe_layer_logits_amd/csrc/ssm_replay.hip",
 }
 
 
@@ -245,19 +246,24 @@ def main():
     del Wd, xd
     torch.cuda.empty_cache()
     if args.copy_probe_mib:
-        # elementwise copy that reads and writes exactly n*4 bytes per launch
-        n = args.copy_probe_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
-        log("copy probe: 5 launches of %d MiB read + %d MiB write" % (args.copy_probe_mib, args.copy_probe_mib))
-        del a, b
+        copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(wl, x, W)
     print(json.dumps(result), flush=True)
+
+
+def copy_probe(mib):
+    """Elementwise copy that reads and writes exactly mib MiB per launch (counter
+    calibration for the FETCH_SIZE / WRITE_SIZE runs)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log("copy probe: 5 launches of %d MiB read + %d MiB write" % (mib, mib))
 
 
 SSM_METRIC = "Mamba-2 speculative-verify tokens/s (checkpoint + replay); % HBM peak"
@@ -344,6 +350,8 @@ def bench_ssm(args):
 
     lens = d["buf_len"]
     kb = ssm_bytes(wl, lens)
+    tr = stored_traffic("ssm_verify_kernel", wl.name)
+    traffic = None if tr is None else tr["hbm_bytes_per_launch"]
     states_bytes = wl.R * wl.H * wl.P * wl.N * 2 * (1 + wl.T) + wl.R * wl.T * wl.H * wl.P * 4
     achieved = kb / (verify_ms * 1e-3) / 1e9
     tokens = wl.R * wl.T
@@ -359,8 +367,9 @@ def bench_ssm(args):
                    "buffered_records_mean": float(np.mean(lens)), "seed": args.seed,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "ssm_verify_kernel", "launch_ms": round(verify_ms, 5),
+                     "source_sha": source_sha(KERNEL_SOURCES["ssm_verify_kernel"]),
                      "alg_bytes_per_launch": int(kb)},
         "state_writing_scheme": {"launch_ms": round(states_ms, 5), "alg_bytes_per_launch": int(states_bytes),
                                  "achieved_GBs": round(states_bytes / (states_ms * 1e-3) / 1e9, 2),
@@ -368,6 +377,8 @@ def bench_ssm(args):
         "flush": {"launch_ms": round(flush_ms, 5),
                   "alg_bytes_per_launch": int(wl.R * wl.H * wl.P * wl.N * 4)},
     }
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = ssm_cpu_baseline(wl, d)
