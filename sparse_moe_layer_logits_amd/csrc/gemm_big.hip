@@ -1,10 +1,11 @@
 // Large-tile MFMA GEMM for many rows per tile (prefill-like shapes).
 //
 // Block tile: 256 weight rows (output columns n) x 256 activation rows, k step
-// 32, four waves in a 2 x 2 arrangement, each wave 128 x 128 = 8 x 8 MFMA
-// 16x16x32 tiles (256 fp32 accumulators per lane).  A wave's LDS traffic per
-// MFMA falls with its tile size: per k step a wave reads 16 (24 in dual mode)
-// 16-byte fragments for 64 (128) MFMAs.
+// 32, eight waves in a 2 x 4 arrangement, each wave 128 x 64 = 8 x 4 MFMA
+// 16x16x32 tiles (128 fp32 accumulators per lane), two waves per SIMD so that
+// one wave's LDS reads and waits overlap the other's MFMAs (one wave per SIMD
+// with 128 x 128 wave tiles ran 11 % slower at prefill).  Per k step a wave
+// reads 12 (16 in dual mode) 16-byte fragments for 32 (64) MFMAs.
 //
 // Operand tiles go from global memory straight into a ring of STAGES LDS
 // buffers (global_load_lds, 16 bytes per lane, no staging registers): while
@@ -42,12 +43,25 @@ __device__ __forceinline__ int bg_off(int row, int piece) {
 template <bool DUAL>
 constexpr int bg_stages() { return DUAL ? 3 : 4; }
 
+// waves per block: 4 (2 x 2 waves of 128 x 128) or 8 (2 x 4 waves of 128 x 64, two
+// waves per SIMD: one wave's LDS reads and waits overlap the other's MFMAs)
+#ifndef LMOE_BIG_WAVES
+#define LMOE_BIG_WAVES 8
+#endif
+constexpr int BG_WAVES = LMOE_BIG_WAVES;
+constexpr int BG_THREADS = 64 * BG_WAVES;
+constexpr int BG_WM = BG_WAVES / 2;        // waves along the activation rows
+constexpr int BG_MB = BG_BM / BG_WM / 16;  // 16-row activation tiles per wave
+constexpr int BG_CPW = 16 / BG_WAVES;      // 1 KB chunks per wave per operand tile
+
 // wait until at most n of this wave's vector-memory loads are outstanding
 __device__ __forceinline__ void wait_vmcnt(int n) {
   // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at max
 #define LMOE_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
   switch (n) {
     case 0: LMOE_VMCNT(0); break;
+    case 4: LMOE_VMCNT(4); break;
+    case 6: LMOE_VMCNT(6); break;
     case 8: LMOE_VMCNT(8); break;
     case 12: LMOE_VMCNT(12); break;
     case 16: LMOE_VMCNT(16); break;
@@ -58,17 +72,17 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 template <bool DUAL, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
+__global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int STAGES = bg_stages<DUAL>();
   constexpr int STAGEB = BG_TILEB * (1 + NPART);  // weights + activation part(s)
-  constexpr int LOADS = 4 * (1 + NPART);          // direct loads per wave per stage
+  constexpr int LOADS = BG_CPW * (1 + NPART);     // direct loads per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;  // 128 weight rows x BG_MB * 16 activation rows
   const int r16 = lane & 15, g = lane >> 4;
 
   const int NQ = (p.N + BG_BN - 1) / BG_BN;
@@ -99,15 +113,15 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
   const int KT = (kend - kbeg) / BG_BK;
   const long long bexp = (long long)expert * p.b_stride;
 
-  // This wave loads 1 KB chunks c = wave + 4i (i = 0..3) of each 16 KB operand
+  // This wave loads 1 KB chunks c = wave + BG_WAVES i of each 16 KB operand
   // tile: lane l fills slot l of the chunk, i.e. row 16c + l/4, stored piece
   // l%4, which holds logical piece (l%4) ^ ((row >> 2) & 3).  Rows past the
   // tile are clamped to a valid row: their products land in outputs that are
   // never stored.
-  uint32_t w_off[4], x_off[4];
+  uint32_t w_off[BG_CPW], x_off[BG_CPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (wave + 4 * i) + (lane >> 2);
+  for (int i = 0; i < BG_CPW; ++i) {
+    const int row = 16 * (wave + BG_WAVES * i) + (lane >> 2);
     const int piece = (lane & 3) ^ ((row >> 2) & 3);
     const int wrow = min(n0 + row, p.N - 1) - n0;
     const int xr = min(row, rows - 1);
@@ -142,8 +156,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     }
     uint8_t* st = smem + (kt % STAGES) * STAGEB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int chunk = (wave + 4 * i) * 1024;
+    for (int i = 0; i < BG_CPW; ++i) {
+      const int chunk = (wave + BG_WAVES * i) * 1024;
       __builtin_amdgcn_global_load_lds(B + k + w_off[i], st + chunk, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(A + k + x_off[i], st + BG_TILEB + chunk, 16, 0, 0);
       if constexpr (DUAL)
@@ -151,11 +165,11 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
     }
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][BG_MB];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < BG_MB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int kt) {
     const uint8_t* base = smem + (kt % STAGES) * STAGEB;
@@ -165,15 +179,15 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
       wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
-      u32x4_t xf[8];
+      u32x4_t xf[BG_MB];
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
+      for (int b = 0; b < BG_MB; ++b)
         xf[b] = *reinterpret_cast<const u32x4_t*>(base + (1 + part) * BG_TILEB +
-                                                  bg_off(wm * 128 + b * 16 + r16, g));
+                                                  bg_off(wm * (BG_MB * 16) + b * 16 + r16, g));
 #pragma unroll
       for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[b], acc[a][b]);
+        for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[b], acc[a][b]);
     }
   };
 
@@ -195,8 +209,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmParams p) {
   for (int a = 0; a < 8; ++a) {
     const int n = n0 + wn * 128 + a * 16 + 4 * g;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int m = wm * 128 + b * 16 + r16;
+    for (int b = 0; b < BG_MB; ++b) {
+      const int m = wm * (BG_MB * 16) + b * 16 + r16;
       if (n < p.N && m < rows) epi4<EPI>(p, expert, split, row0 + m, n, acc[a][b]);
     }
   }
@@ -251,11 +265,11 @@ void launch_gemm_big(const GemmParams& p, hipStream_t s) {
   if (blocks <= 0) return;
   if (p.a_lo)
     big_for_each_epi(p.epi, [&](auto E) {
-      gemm_big_kernel<true, decltype(E)::value><<<(unsigned)blocks, 256, big_lds_bytes<true>(), s>>>(p);
+      gemm_big_kernel<true, decltype(E)::value><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<true>(), s>>>(p);
     });
   else
     big_for_each_epi(p.epi, [&](auto E) {
-      gemm_big_kernel<false, decltype(E)::value><<<(unsigned)blocks, 256, big_lds_bytes<false>(), s>>>(p);
+      gemm_big_kernel<false, decltype(E)::value><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<false>(), s>>>(p);
     });
 }
 
