@@ -206,15 +206,8 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   }
 
   if (!active) return;
-#pragma unroll
-  for (int nt = 0; nt < MD_NT; ++nt) {
-    const int n = nbase + nt * 16 + 4 * g;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + r16;
-      if (m < rows) epi4<EPI>(p, expert, 0, row0 + m, n, acc[nt][mt]);
-    }
-  }
+  epi_tile<EPI>(p, expert, 0, row0, rows, MT, [&](int nt) { return nbase + nt * 16 + 4 * g; },
+                [&](int mt) { return mt * 16 + r16; }, acc);
 }
 
 template <int W, int NP>

@@ -430,16 +430,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   }
 
   if (!wave_active) return;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = nbase + nt * 16 + 4 * g;
-    if (n >= p.N) continue;
-#pragma unroll
-    for (int mt = 0; mt < MTMAX; ++mt) {
-      const int m = mt * 16 + r16;
-      if (mt < MT && m < rows) epilogue4(p, expert, split, row0 + m, n, acc[nt][mt]);
-    }
-  }
+  epi_dispatch(p.epi, [&](auto E) {
+    epi_tile<decltype(E)::value>(p, expert, split, row0, rows, MTMAX,
+                                 [&](int nt) { return nbase + nt * 16 + 4 * g; },
+                                 [&](int mt) { return mt * 16 + r16; }, acc);
+  });
 }
 
 #ifndef LMOE_ST_W
