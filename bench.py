@@ -26,11 +26,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "LatentMoE layer tokens/s; % HBM peak (decode) / % MFMA peak (prefill)"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {  # kernel -> source file whose hash pins stored counter data
-    "gemm_stream_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_stream.hip",
-    "gemm_mid_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_mid.hip",
-    "gemm_big_kernel": "sparse_moe_layer_logits_amd/csrc/gemm_big.hip",
-    "ssm_verify_kernel": "sparse_moe_layer_logits_amd/csrc/ssm_replay.hip",
+CSRC = "sparse_moe_layer_logits_amd/csrc/"
+KERNEL_SOURCES = {  # kernel -> the files (source and included headers) whose hash pins stored counter data
+    "gemm_stream_kernel": ("gemm_stream.hip", "common.hpp", "epilogue.hpp", "fp4.hpp", "fp8.hpp", "kernels.hpp"),
+    "gemm_mid_kernel": ("gemm_mid.hip", "common.hpp", "epilogue.hpp", "fp4.hpp", "fp8.hpp", "kernels.hpp"),
+    "gemm_big_kernel": ("gemm_big.hip", "common.hpp", "epilogue.hpp", "kernels.hpp"),
+    "ssm_verify_kernel": ("ssm_replay.hip", "common.hpp", "../../include/ssm_replay.h"),
 }
 
 
@@ -38,12 +39,10 @@ def log(*a):
     print("[bench %s]" % time.strftime("%H:%M:%S"), *a, file=sys.stderr, flush=True)
 
 
-def source_sha(path):
+def source_sha(kernel):
     h = hashlib.sha256()
-    for p in (path, "sparse_moe_layer_logits_amd/csrc/epilogue.hpp",
-              "sparse_moe_layer_logits_amd/csrc/common.hpp", "sparse_moe_layer_logits_amd/csrc/fp4.hpp",
-              "sparse_moe_layer_logits_amd/csrc/fp8.hpp"):
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -117,7 +116,7 @@ def stored_traffic(kernel, workload):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+    if d.get("source_sha") != source_sha(kernel):
         return None    # the kernel changed since the counters were taken
     return d
 
@@ -223,7 +222,7 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "%s (%s)" % (kernel, dom), "launch_ms": round(dom_s * 1e3, 5),
-                "source_sha": source_sha(KERNEL_SOURCES[kernel]),
+                "source_sha": source_sha(kernel),
                 "alg_bytes_per_launch": int(kb), "alg_flops_per_launch": kf}
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -369,7 +368,7 @@ def bench_ssm(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "ssm_verify_kernel", "launch_ms": round(verify_ms, 5),
-                     "source_sha": source_sha(KERNEL_SOURCES["ssm_verify_kernel"]),
+                     "source_sha": source_sha("ssm_verify_kernel"),
                      "alg_bytes_per_launch": int(kb)},
         "state_writing_scheme": {"launch_ms": round(states_ms, 5), "alg_bytes_per_launch": int(states_bytes),
                                  "achieved_GBs": round(states_bytes / (states_ms * 1e-3) / 1e9, 2),
