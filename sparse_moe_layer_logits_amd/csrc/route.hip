@@ -43,7 +43,19 @@ void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStrea
 // the lowest-index experts equal to tau (ties go to the lower index) form the
 // selection, which is then ranked by (-logit, index) for the output order.
 // ---------------------------------------------------------------------------
-constexpr int TOPK_TOKENS_PER_BLOCK = 16;  // one wave each; masks are 16 bits wide
+constexpr int TOPK_TOKENS_PER_BLOCK = 16;  // tokens per mask group: masks are 16 bits wide
+// Top-K runs TOPK_WAVES tokens (one wave each) per workgroup, so a mask group is
+// written by 16 / TOPK_WAVES workgroups on as many CUs: the bisection is a chain of
+// scalar ballot counts, and a CU has one scalar unit for all its waves (16 tokens
+// on one CU took ~16 us at 64 tokens).  Each workgroup owns one byte of the group's
+// mask word for expert e: byte s holds tokens 4s .. 4s + 3 in its low 4 bits, and
+// readers unpack the word with mask16().
+constexpr int TOPK_WAVES = 4;
+static_assert(TOPK_TOKENS_PER_BLOCK == 4 * TOPK_WAVES, "four workgroups of four tokens per mask group");
+
+__device__ __forceinline__ uint32_t mask16(uint32_t w) {
+  return (w & 0xFu) | ((w >> 4) & 0xF0u) | ((w >> 8) & 0xF00u) | ((w >> 12) & 0xF000u);
+}
 
 __device__ __forceinline__ uint32_t orderable(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal logits must tie
@@ -64,7 +76,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <int SLOTS>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias, int T, int N,
                                                     int K, int* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
@@ -72,10 +84,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
                                                     uint32_t* __restrict__ masks_hi) {
   __shared__ uint32_t smask[1024];
   __shared__ uint32_t smask_hi[1024];
-  __shared__ unsigned long long cand[TOPK_TOKENS_PER_BLOCK][64];
+  __shared__ unsigned long long cand[TOPK_WAVES][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int t = blockIdx.x * TOPK_TOKENS_PER_BLOCK + w;
+  const int t = blockIdx.x * TOPK_WAVES + w;  // workgroups past T only write zero bytes
   for (int e = threadIdx.x; e < N; e += blockDim.x) smask[e] = smask_hi[e] = 0u;
   __syncthreads();
 
@@ -140,21 +152,27 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ lo
     }
   }
   __syncthreads();
+  // this workgroup's byte of each mask word of its group
+  const long long grp = blockIdx.x / (TOPK_TOKENS_PER_BLOCK / TOPK_WAVES);
+  const int byte = blockIdx.x % (TOPK_TOKENS_PER_BLOCK / TOPK_WAVES);
+  uint8_t* m8 = reinterpret_cast<uint8_t*>(masks);
+  uint8_t* mh8 = reinterpret_cast<uint8_t*>(masks_hi);
   for (int e = threadIdx.x; e < N; e += blockDim.x) {
-    masks[(long long)blockIdx.x * N + e] = smask[e];
-    if (masks_hi) masks_hi[(long long)blockIdx.x * N + e] = smask_hi[e];
+    m8[(grp * N + e) * 4 + byte] = (uint8_t)smask[e];
+    if (masks_hi) mh8[(grp * N + e) * 4 + byte] = (uint8_t)smask_hi[e];
   }
 }
 
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
                  float* gates, uint32_t* masks, float hi_tau, uint32_t* masks_hi, hipStream_t s) {
-  const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  // whole mask groups: every byte of every group's words is written
+  const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK * (TOPK_TOKENS_PER_BLOCK / TOPK_WAVES);
   if (N <= 512)
-    topk_kernel<8><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates,
-                                                                masks, hi_tau, masks_hi);
+    topk_kernel<8><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, hi_tau,
+                                                      masks_hi);
   else
-    topk_kernel<16><<<blocks, 64 * TOPK_TOKENS_PER_BLOCK, 0, s>>>(logits, bias, T, N, K, idx, gates,
-                                                                 masks, hi_tau, masks_hi);
+    topk_kernel<16><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, hi_tau,
+                                                       masks_hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,12 +214,12 @@ __device__ __forceinline__ void place_one(long long i, const int* __restrict__ i
   const int tl = t % TOPK_TOKENS_PER_BLOCK;
   const long long be = (long long)b * N + e;
   const uint32_t below = (1u << tl) - 1u;
-  const uint32_t m = bm.all[be];
+  const uint32_t m = mask16(bm.all[be]);
   int pos;
   if (!bm.hi) {
     pos = offsets[e] + bm.prefix_hi[be] + __popc(m & below);
   } else {
-    const uint32_t mh = bm.hi[be];
+    const uint32_t mh = mask16(bm.hi[be]);
     if ((mh >> tl) & 1u)
       pos = offsets[e] + bm.prefix_hi[be] + __popc(mh & below);
     else
@@ -232,8 +250,8 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
         uint32_t m[U], mh[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          m[u] = bm.all[(long long)(b + u) * N + e];
-          if constexpr (HI) mh[u] = bm.hi[(long long)(b + u) * N + e];
+          m[u] = mask16(bm.all[(long long)(b + u) * N + e]);
+          if constexpr (HI) mh[u] = mask16(bm.hi[(long long)(b + u) * N + e]);
           else mh[u] = m[u];
         }
 #pragma unroll
