@@ -102,17 +102,20 @@ void launch_topk(const float* logits, const float* bias, int T, int N, int K, in
 // with masks_hi the rows of each expert are split into the hi class (first) and the rest,
 // hi tiles first in the list: n_tiles[0] hi tiles, then n_tiles[1] others.  With place_idx
 // set it also does launch_place's work in the same workgroup (small T)
+// (chunk_hi, chunk_lo non-null: [bucket_chunks(T), N] scratch; the prefix is split
+// over chunks of mask groups, and launch_place must get the same two pointers)
 void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, int N,
                         int tile_rows_max, int* counts, int* counts_hi, int* offsets,
                         int* prefix_hi, int* prefix_lo, int* tile_expert, int* tile_row0,
                         int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
                         const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
-                        hipStream_t s);
+                        int* chunk_hi, int* chunk_lo, hipStream_t s);
+int bucket_chunks(int T);
 // permuted positions: row_src[p] = token, row_gate[p] = gate, inv[t*K+k] = p
 void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
-                  float* row_gate, int* inv, hipStream_t s);
+                  float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s);
 // y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo
 void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
                     uint16_t* y_lat_lo, hipStream_t s);

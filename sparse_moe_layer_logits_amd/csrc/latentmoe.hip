@@ -68,6 +68,9 @@ constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kerne
 #define LMOE_LOWP_A16 1
 #endif
 
+#ifndef LMOE_BUCKET_MIN_CHUNKS
+#define LMOE_BUCKET_MIN_CHUNKS 4  // chunks of 16 mask blocks (256 tokens) from which the count is split
+#endif
 #ifndef LMOE_TARGET_BLOCKS
 #define LMOE_TARGET_BLOCKS 256
 #endif
@@ -110,6 +113,8 @@ struct Buffers {
   uint32_t* masks_hi = nullptr;  // rows whose gate reaches LMOE_HI_TAU (large-tile path)
   int* block_prefix = nullptr;   // per (block, expert) prefix of the (hi-class) rows
   int* prefix_lo = nullptr;      // the same for the other rows
+  int* chunk_hi = nullptr;       // per (chunk of mask blocks, expert) counts -> offsets (large T)
+  int* chunk_lo = nullptr;
   int* counts_hi = nullptr;
   int* counts = nullptr;
   int* offsets = nullptr;
@@ -210,6 +215,8 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.masks_hi, nblk * N * 4);
   L.add((void**)&b.block_prefix, nblk * N * 4);
   L.add((void**)&b.prefix_lo, nblk * N * 4);
+  L.add((void**)&b.chunk_hi, (size_t)bucket_chunks((int)Tm) * N * 4);
+  L.add((void**)&b.chunk_lo, (size_t)bucket_chunks((int)Tm) * N * 4);
   L.add((void**)&b.counts_hi, N * 4);
   L.add((void**)&b.counts, N * 4);
   L.add((void**)&b.offsets, (N + 1) * 4);
@@ -618,13 +625,17 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       ceil_div(TK, rows_per_tile) + (split_rows ? 2 : 1) * (int)std::min<long long>(N, TK);
   tm.start(LATENTMOE_STAGE_BUCKET);
   const bool fuse_place = TK <= 8192;  // one workgroup places a few thousand rows quickly
+  // many mask blocks: count them in chunks on many workgroups first
+  const bool chunked = !fuse_place && bucket_chunks(T) >= LMOE_BUCKET_MIN_CHUNKS;
+  int* chunk_hi = chunked ? b.chunk_hi : nullptr;
+  int* chunk_lo = chunked ? b.chunk_lo : nullptr;
   launch_bucket_scan(b.masks, masks_hi, T, N, rows_per_tile, b.counts, b.counts_hi, b.offsets,
                      b.block_prefix, b.prefix_lo, b.tile_expert, b.tile_row0, b.tile_rows,
                      b.n_tiles, max_tiles, fuse_place ? idx_buf : nullptr, gate_buf, K, b.row_src,
-                     b.row_gate, b.inv, s);
+                     b.row_gate, b.inv, chunk_hi, chunk_lo, s);
   if (!fuse_place)
     launch_place(idx_buf, gate_buf, b.masks, masks_hi, b.offsets, b.counts_hi, b.block_prefix,
-                 b.prefix_lo, T, N, K, b.row_src, b.row_gate, b.inv, s);
+                 b.prefix_lo, T, N, K, b.row_src, b.row_gate, b.inv, chunk_hi, chunk_lo, s);
   tm.stop(LATENTMOE_STAGE_BUCKET);
 #if LMOE_SHARED_FORK_AT == 2
   fork_to(side, h->ev_fork2);

@@ -195,12 +195,21 @@ struct PlaceArgs {  // fused placement (small T): see place_kernel
   int* inv;
 };
 
+// Large T splits the prefix over mask groups in chunks of BK_CHUNK groups: one
+// workgroup per chunk counts it (prefixes inside the chunk), the scan turns the
+// chunk counts into offsets, and a row's position adds its chunk's offset.  (One
+// workgroup walking 512 groups per expert was a chain of 32 rounds of loads, ~55 us
+// alone and ~220 us beside the shared expert's GEMMs at 8192 tokens.)
+constexpr int BK_CHUNK = 16;
+
 struct BucketMasks {
   const uint32_t* all;      // [nblk, N] rows of each expert per 16-token block
   const uint32_t* hi;       // [nblk, N] the hi-class subset, or null (all rows are hi)
-  int* prefix_hi;           // [nblk, N] hi rows of expert e in blocks before b
+  int* prefix_hi;           // [nblk, N] hi rows of expert e in blocks before b (of its chunk)
   int* prefix_lo;           // [nblk, N] the other rows likewise (used with hi)
   int* counts_hi;           // [N]
+  const int* chunk_hi;      // [nchunk, N] hi rows of expert e in chunks before c, or null
+  const int* chunk_lo;      // [nchunk, N] the other rows likewise
 };
 
 __device__ __forceinline__ void place_one(long long i, const int* __restrict__ idx,
@@ -215,32 +224,101 @@ __device__ __forceinline__ void place_one(long long i, const int* __restrict__ i
   const long long be = (long long)b * N + e;
   const uint32_t below = (1u << tl) - 1u;
   const uint32_t m = mask16(bm.all[be]);
+  const long long ce = (long long)(b / BK_CHUNK) * N + e;
   int pos;
   if (!bm.hi) {
     pos = offsets[e] + bm.prefix_hi[be] + __popc(m & below);
+    if (bm.chunk_hi) pos += bm.chunk_hi[ce];
   } else {
     const uint32_t mh = mask16(bm.hi[be]);
-    if ((mh >> tl) & 1u)
+    if ((mh >> tl) & 1u) {
       pos = offsets[e] + bm.prefix_hi[be] + __popc(mh & below);
-    else
+      if (bm.chunk_hi) pos += bm.chunk_hi[ce];
+    } else {
       pos = offsets[e] + bm.counts_hi[e] + bm.prefix_lo[be] + __popc(m & ~mh & below);
+      if (bm.chunk_hi) pos += bm.chunk_lo[ce];
+    }
   }
   row_src[pos] = t;
   row_gate[pos] = gates[i];
   inv[i] = pos;
 }
 
+// chunk c = blockIdx.x: prefixes inside the chunk and the chunk's counts per expert
+template <bool HI>
+__global__ __launch_bounds__(256) void bucket_count_kernel(BucketMasks bm, int nblk, int N,
+                                                           int* __restrict__ chunk_hi,
+                                                           int* __restrict__ chunk_lo) {
+  const int b0 = blockIdx.x * BK_CHUNK;
+  const int nb = min(BK_CHUNK, nblk - b0);
+  for (int e = threadIdx.x; e < N; e += blockDim.x) {
+    uint32_t m[BK_CHUNK], mh[BK_CHUNK];
+#pragma unroll
+    for (int u = 0; u < BK_CHUNK; ++u) {
+      m[u] = mh[u] = 0u;
+      if (u < nb) {
+        m[u] = mask16(bm.all[(long long)(b0 + u) * N + e]);
+        if constexpr (HI) mh[u] = mask16(bm.hi[(long long)(b0 + u) * N + e]);
+        else mh[u] = m[u];
+      }
+    }
+    int run_hi = 0, run_lo = 0;
+#pragma unroll
+    for (int u = 0; u < BK_CHUNK; ++u) {
+      if (u < nb) {
+        const long long be = (long long)(b0 + u) * N + e;
+        bm.prefix_hi[be] = run_hi;
+        run_hi += __popc(mh[u]);
+        if constexpr (HI) {
+          bm.prefix_lo[be] = run_lo;
+          run_lo += __popc(m[u] & ~mh[u]);
+        }
+      }
+    }
+    chunk_hi[(long long)blockIdx.x * N + e] = run_hi;
+    if constexpr (HI) chunk_lo[(long long)blockIdx.x * N + e] = run_lo;
+  }
+}
+
+// nchunk > 0: the prefixes inside chunks and the chunk counts are in place (from
+// bucket_count_kernel); the counts become exclusive chunk offsets here
 template <bool HI>
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     BucketMasks bm, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ tile_expert, int* __restrict__ tile_row0,
-    int* __restrict__ tile_rows, int* __restrict__ n_tiles, int max_tiles, PlaceArgs pa) {
+    int* __restrict__ tile_rows, int* __restrict__ n_tiles, int max_tiles, PlaceArgs pa,
+    int nchunk, int* __restrict__ chunk_hi, int* __restrict__ chunk_lo) {
   __shared__ int scan_a[1024];
   __shared__ int scan_b[1024];
   __shared__ int scan_c[1024];
   const int e = threadIdx.x;
   int run_hi = 0, run_lo = 0;
-  if (e < N) {
+  if (e < N && nchunk > 0) {
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {  // 16 chunk counts in flight
+      int ch[16], cl[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        ch[u] = cl[u] = 0;
+        if (c0 + u < nchunk) {
+          ch[u] = chunk_hi[(long long)(c0 + u) * N + e];
+          if constexpr (HI) cl[u] = chunk_lo[(long long)(c0 + u) * N + e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (c0 + u < nchunk) {
+          chunk_hi[(long long)(c0 + u) * N + e] = run_hi;
+          run_hi += ch[u];
+          if constexpr (HI) {
+            chunk_lo[(long long)(c0 + u) * N + e] = run_lo;
+            run_lo += cl[u];
+          }
+        }
+      }
+    }
+    if constexpr (HI) bm.counts_hi[e] = run_hi;
+    counts[e] = run_hi + run_lo;
+  } else if (e < N) {
     // U blocks of masks in flight per step (16, then 4, then 1): the loads do
     // not wait on the prefix
     int b = 0;
@@ -332,23 +410,32 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
   }
 }
 
+int bucket_chunks(int T) {
+  const int nblk = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  return (nblk + BK_CHUNK - 1) / BK_CHUNK;
+}
+
 void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, int N,
                         int tile_rows_max, int* counts, int* counts_hi, int* offsets,
                         int* prefix_hi, int* prefix_lo, int* tile_expert, int* tile_row0,
                         int* tile_rows, int* n_tiles, int max_tiles, const int* place_idx,
                         const float* place_gates, int K, int* row_src, float* row_gate, int* inv,
-                        hipStream_t s) {
+                        int* chunk_hi, int* chunk_lo, hipStream_t s) {
   const int nblk = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK;
+  const int nchunk = chunk_hi ? bucket_chunks(T) : 0;
   PlaceArgs pa{place_idx, place_gates, T, K, row_src, row_gate, inv};
-  BucketMasks bm{masks, masks_hi, prefix_hi, prefix_lo, counts_hi};
-  if (masks_hi)
+  BucketMasks bm{masks, masks_hi, prefix_hi, prefix_lo, counts_hi, nullptr, nullptr};
+  if (masks_hi) {
+    if (nchunk) bucket_count_kernel<true><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
     bucket_scan_kernel<true><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
                                                 tile_expert, tile_row0, tile_rows, n_tiles,
-                                                max_tiles, pa);
-  else
+                                                max_tiles, pa, nchunk, chunk_hi, chunk_lo);
+  } else {
+    if (nchunk) bucket_count_kernel<false><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
     bucket_scan_kernel<false><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
                                                  tile_expert, tile_row0, tile_rows, n_tiles,
-                                                 max_tiles, pa);
+                                                 max_tiles, pa, nchunk, chunk_hi, chunk_lo);
+  }
 }
 
 __global__ void place_kernel(const int* __restrict__ idx, const float* __restrict__ gates,
@@ -363,10 +450,10 @@ __global__ void place_kernel(const int* __restrict__ idx, const float* __restric
 void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
-                  float* row_gate, int* inv, hipStream_t s) {
+                  float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s) {
   const long long n = (long long)T * K;
   BucketMasks bm{masks, masks_hi, const_cast<int*>(prefix_hi), const_cast<int*>(prefix_lo),
-                 const_cast<int*>(counts_hi)};
+                 const_cast<int*>(counts_hi), chunk_hi, chunk_lo};
   place_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, gates, bm, offsets, T, N, K,
                                                            row_src, row_gate, inv);
 }

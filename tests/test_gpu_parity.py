@@ -201,6 +201,19 @@ def test_precision_mix_tiled_path():
     full_check(wl40, x[:40], W, tol=tolerance(wl), max_tokens=300)
 
 
+@pytest.mark.parametrize("n_experts", [32, 256])
+def test_chunked_bucketing(n_experts):
+    # 1100 tokens x 8 rows: more rows than one workgroup places and 69 mask blocks, so
+    # the prefix runs in 5 chunks of 16 blocks (the last one partial); 32 experts put
+    # ~275 rows on each (large tiles, two row classes), 256 experts ~34 (64-row streaming
+    # tiles, one class).  Every token's output and the whole permutation are checked.
+    wl = small_wl(T=1100, d=256, latent=64, n_experts=n_experts, top_k=8, expert_hidden=128,
+                  shared_hidden=256)
+    x, W = gen(wl, 21)
+    log("chunked bucketing", wl)
+    full_check(wl, x, W)
+
+
 def test_edge_token_counts_and_reuse():
     import torch
     wl = small_wl(T=33, d=256, latent=64, n_experts=16, top_k=4)
