@@ -10,7 +10,6 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-#define LMOE_WAVE 64
 
 // D[16x16] += A[16 x 32] * B[32 x 16] on the matrix cores, bf16 in, fp32 accumulate.
 // Lane l supplies row (l % 16) of A and column (l % 16) of B with eight k values
