@@ -304,7 +304,9 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.seg[2].B) + bexp + (long long)n0 * p.ldb;
   const uint16_t* Alo = reinterpret_cast<const uint16_t*>(p.a_lo);
 
-  auto issue = [&](int kt) {
+  // direct load u of stage kt: chunk i = u / (1 + NPART) of the weights (part 0),
+  // the activations (1) or their low halves (2)
+  auto issue_one = [&](int kt, int u) {
     int k = kbeg + kt * BG_BK;
     const uint16_t* A = A0;
     const uint16_t* B = B0;
@@ -319,19 +321,23 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       }
     }
     uint8_t* st = smem + (kt % STAGES) * STAGEB;
+    const int i = u / (1 + NPART), part = u % (1 + NPART);
+    const int chunk = (wave + BG_WAVES * i) * 1024;
     // uniform base + 32-bit byte offset (below 4 GB: a 256-row weight slice and
     // an activation matrix of at most 2^31 elements), the scalar-base form
-    const uint8_t* Bk = reinterpret_cast<const uint8_t*>(B + k);
-    const uint8_t* Ak = reinterpret_cast<const uint8_t*>(A + k);
-    const uint8_t* Lk = reinterpret_cast<const uint8_t*>(Alo + k);
+    if (part == 0)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(B + k) + (uint64_t)(w_off[i] * 2u),
+                                       st + chunk, 16, 0, 0);
+    else if (part == 1)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(A + k) + (uint64_t)(x_off[i] * 2u),
+                                       st + BG_TILEB + chunk, 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(Alo + k) + (uint64_t)(x_off[i] * 2u),
+                                       st + 2 * BG_TILEB + chunk, 16, 0, 0);
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < BG_CPW; ++i) {
-      const int chunk = (wave + BG_WAVES * i) * 1024;
-      __builtin_amdgcn_global_load_lds(Bk + (uint64_t)(w_off[i] * 2u), st + chunk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Ak + (uint64_t)(x_off[i] * 2u), st + BG_TILEB + chunk, 16, 0, 0);
-      if constexpr (DUAL)
-        __builtin_amdgcn_global_load_lds(Lk + (uint64_t)(x_off[i] * 2u), st + 2 * BG_TILEB + chunk, 16, 0, 0);
-    }
+    for (int u = 0; u < LOADS; ++u) issue_one(kt, u);
   };
 
   f32x4_t acc[8][BG_MB];
@@ -393,7 +399,6 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
       wait_vmcnt(min(STAGES - 2, KT - 2 - kt) * LOADS);
       asm volatile("s_barrier" ::: "memory");
-      if (kt + STAGES < KT) issue(kt + STAGES);
       const uint8_t* base = smem + ((kt + 1) % STAGES) * STAGEB;
 #pragma unroll
       for (int b = 0; b < BG_MB; ++b)
@@ -403,6 +408,13 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
         for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xc[0][b], acc[a][b]);
         wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
+        // stage kt + STAGES (into the slot every wave finished reading before this
+        // step's barrier), its loads spread over the step: issued together after
+        // the barrier, all waves' loads queue at the memory unit at once and each
+        // wave's MFMAs wait behind its own loads
+#pragma unroll
+        for (int u = a * LOADS / 8; u < (a + 1) * LOADS / 8; ++u)
+          if (kt + STAGES < KT) issue_one(kt + STAGES, u);
       }
       // keep the interleave: the activation reads, then 4 MFMAs and one read per a
       __builtin_amdgcn_sched_group_barrier(0x100, BG_MB, 0);
@@ -437,11 +449,23 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       // a plain barrier: the step's own loads were waited for above; a fenced
       // __syncthreads would wait for every load in flight, draining the ring
       asm volatile("s_barrier" ::: "memory");
-      if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1);
       u32x4_t wf[8], xf[NPART][BG_MB];
       read_frags(kt, wf, xf);
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(wf, xf);
+      // stage kt + STAGES - 1 goes to the slot every wave finished reading before
+      // this barrier; its loads are spread over the MFMAs (see the pipelined path)
+      const bool more = kt + STAGES - 1 < KT;
+#pragma unroll
+      for (int part = 0; part < NPART; ++part)
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+#pragma unroll
+          for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[part][b], acc[a][b]);
+          const int grp = part * 8 + a;
+#pragma unroll
+          for (int u = grp * LOADS / (8 * NPART); u < (grp + 1) * LOADS / (8 * NPART); ++u)
+            if (more) issue_one(kt + STAGES - 1, u);
+        }
     }
   }
 
