@@ -21,15 +21,15 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t& a, const u32x4_t
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// round-to-nearest-even float -> bf16 bits (finite inputs)
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Round-to-nearest-even float -> bf16 on gfx950's converter (one v_cvt_pk_bf16_f32
+// per pair).  For every non-NaN input it returns what the bit formula
+// (u + 0x7FFF + ((u >> 16) & 1)) >> 16 gives, denormals and overflow to infinity
+// included (all 2^32 patterns compared on the device).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 
 // 128-bit global load / store helpers
 __device__ __forceinline__ u32x4_t ld128(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

@@ -125,28 +125,41 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
     rf[b] = m < rows ? epi_rowf<EPI>(p, row0 + m) : 1.0f;
   }
   epi_wait_all();
+  // the staged values of all eight waves at once (the halves are staged in turn,
+  // and a wave computing its values only in its own half left the other SIMD
+  // slots idle): fp32, or bf16 pairs per plane
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t sf[EB == 4 ? 8 : 1][BG_MB];
+  u32x2_t sb[EB == 2 ? PL : 1][EB == 2 ? 8 : 1][BG_MB];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < BG_MB; ++b) {
+      const Epi4 o = epi_math<SE>(p, acc[a][b], ts, rf[b], zero);
+      if constexpr (EB == 4) {
+        sf[a][b] = o.v0;
+      } else {
+        sb[0][a][b] = u32x2_t{pack_bf16x2(o.v0[0], o.v0[1]), pack_bf16x2(o.v0[2], o.v0[3])};
+        if constexpr (PL == 2) sb[PL - 1][a][b] = u32x2_t{pack_bf16x2(o.v1[0], o.v1[1]), pack_bf16x2(o.v1[2], o.v1[3])};
+      }
+    }
   __syncthreads();  // every wave has read its last operands from the ring
 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wrow / HR == half) {
-      const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
         const int col = wn * 128 + a * 16 + 4 * g;
 #pragma unroll
         for (int b = 0; b < BG_MB; ++b) {
           const int r = wrow % HR + b * 16 + r16;
-          const Epi4 o = epi_math<SE>(p, acc[a][b], ts, rf[b], zero);
           if constexpr (EB == 4) {
-            *reinterpret_cast<f32x4_t*>(smem + r * RB + (((col >> 2) ^ (r & 7)) << 4)) = o.v0;
+            *reinterpret_cast<f32x4_t*>(smem + r * RB + (((col >> 2) ^ (r & 7)) << 4)) = sf[a][b];
           } else {
             const int at = r * RB + (((col >> 3) ^ (r & 7)) << 4) + ((col >> 2) & 1) * 8;
-            *reinterpret_cast<u32x2_t*>(smem + at) =
-                u32x2_t{pack_bf16x2(o.v0[0], o.v0[1]), pack_bf16x2(o.v0[2], o.v0[3])};
-            if constexpr (PL == 2)
-              *reinterpret_cast<u32x2_t*>(smem + PLANEB + at) =
-                  u32x2_t{pack_bf16x2(o.v1[0], o.v1[1]), pack_bf16x2(o.v1[2], o.v1[3])};
+            *reinterpret_cast<u32x2_t*>(smem + at) = sb[0][a][b];
+            if constexpr (PL == 2) *reinterpret_cast<u32x2_t*>(smem + PLANEB + at) = sb[PL - 1][a][b];
           }
         }
       }
