@@ -226,6 +226,9 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int STAGES = bg_stages<DUAL>();
   constexpr int STAGEB = BG_TILEB * (1 + NPART);  // weights + activation part(s)
+  // the epilogue stages half a tile (128 rows, every plane) in the ring's LDS
+  static_assert(epi_planes<EPI>() * 128 * BG_BN * epi_bytes<EPI>() <= STAGES * STAGEB,
+                "the staged half of the output tile must fit in the ring");
   constexpr int LOADS = BG_CPW * (1 + NPART);     // direct loads per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
