@@ -50,17 +50,17 @@ __device__ __forceinline__ void epi_wait_all() {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-// The values of one 4-column group as they go to memory: v0 is the output (the
-// high bf16 part of a hi/lo pair, rounded to bf16 by bf16 stores), v1 the low part
-// of a pair.  EPI_F32_ADD gives the addend acc * ts; the store adds the old value.
+// The values of one 4-column group before they go to memory: v0 is the output in
+// fp32 (bf16 kinds round it when packing, and a hi/lo pair's low part is formed
+// there from the packed high part).  EPI_F32_ADD gives the addend acc * ts; the
+// store adds the old value.
 struct Epi4 {
-  f32x4_t v0, v1;
+  f32x4_t v0;
 };
 
 template <int EPI>
 __device__ __forceinline__ Epi4 epi_math(const GemmParams& p, f32x4_t v, float ts, float rf, f32x4_t add) {
   Epi4 o;
-  o.v1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (EPI == EPI_PARTIAL || EPI == EPI_BF16) {
     o.v0 = v;
   } else if constexpr (EPI == EPI_SQRELU_BF16 || EPI == EPI_SQRELU_HILO || EPI == EPI_BF16_HILO) {
@@ -71,8 +71,7 @@ __device__ __forceinline__ Epi4 epi_math(const GemmParams& p, f32x4_t v, float t
         u = fmaxf(u, 0.0f);
         u = u * u;
       }
-      o.v0[i] = bf16_bits_to_f32(f32_to_bf16_bits(u));
-      o.v1[i] = u - o.v0[i];
+      o.v0[i] = u;
     }
   } else if constexpr (EPI == EPI_F32) {
     o.v0 = v * ts;
@@ -88,6 +87,19 @@ __device__ __forceinline__ Epi4 epi_math(const GemmParams& p, f32x4_t v, float t
 // output arrays (hi and lo for the pair kinds) and bytes per element
 template <int EPI>
 constexpr int epi_planes() { return EPI == EPI_SQRELU_HILO || EPI == EPI_BF16_HILO ? 2 : 1; }
+
+// bf16 planes of a 4-column group: hi = bf16(u) (round to nearest even) and, for
+// the pair kinds, lo = bf16(u - hi) (u - hi is exact in fp32)
+template <int EPI>
+__device__ __forceinline__ void epi_pack(const f32x4_t& u, u32x2_t& hi, u32x2_t& lo) {
+  hi = u32x2_t{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
+  if constexpr (epi_planes<EPI>() == 2) {
+    const f32x4_t h = {__uint_as_float(hi.x << 16), __uint_as_float(hi.x & 0xFFFF0000u),
+                       __uint_as_float(hi.y << 16), __uint_as_float(hi.y & 0xFFFF0000u)};
+    const f32x4_t l = u - h;
+    lo = u32x2_t{pack_bf16x2(l[0], l[1]), pack_bf16x2(l[2], l[3])};
+  }
+}
 template <int EPI>
 constexpr int epi_bytes() {
   return EPI == EPI_PARTIAL || EPI == EPI_F32 || EPI == EPI_F32_ADD || EPI == EPI_GATE_F32 ? 4 : 2;
@@ -102,8 +114,10 @@ __device__ __forceinline__ void epi4(const GemmParams& p, int split, int row, in
     float* dst = p.partial + (long long)split * p.partial_stride + (long long)row * p.N + n;
     *reinterpret_cast<f32x4_t*>(dst) = o.v0;
   } else if constexpr (epi_bytes<EPI>() == 2) {
-    store_bf16x4(p.C, off, o.v0[0], o.v0[1], o.v0[2], o.v0[3]);
-    if constexpr (epi_planes<EPI>() == 2) store_bf16x4(p.C2, off, o.v1[0], o.v1[1], o.v1[2], o.v1[3]);
+    u32x2_t hi, lo;
+    epi_pack<EPI>(o.v0, hi, lo);
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.C) + off) = hi;
+    if constexpr (epi_planes<EPI>() == 2) *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(p.C2) + off) = lo;
   } else if constexpr (EPI == EPI_F32_ADD) {
     *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(p.C) + off) = add + o.v0;
   } else {

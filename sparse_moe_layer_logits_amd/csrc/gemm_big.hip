@@ -139,8 +139,7 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
       if constexpr (EB == 4) {
         sf[a][b] = o.v0;
       } else {
-        sb[0][a][b] = u32x2_t{pack_bf16x2(o.v0[0], o.v0[1]), pack_bf16x2(o.v0[2], o.v0[3])};
-        if constexpr (PL == 2) sb[PL - 1][a][b] = u32x2_t{pack_bf16x2(o.v1[0], o.v1[1]), pack_bf16x2(o.v1[2], o.v1[3])};
+        epi_pack<SE>(o.v0, sb[0][a][b], sb[PL - 1][a][b]);
       }
     }
   __syncthreads();  // every wave has read its last operands from the ring
