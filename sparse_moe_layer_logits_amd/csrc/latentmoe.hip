@@ -68,6 +68,9 @@ constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kerne
 #define LMOE_LOWP_A16 1
 #endif
 
+#ifndef LMOE_HI_DOWN_SIDE
+#define LMOE_HI_DOWN_SIDE 1  // hi-class expert down on side stream 2 beside the bf16-class expert up
+#endif
 #ifndef LMOE_BUCKET_MIN_CHUNKS
 #define LMOE_BUCKET_MIN_CHUNKS 4  // chunks of 16 mask blocks (256 tokens) from which the count is split
 #endif
@@ -279,6 +282,7 @@ struct latentmoe_handle_s {
   hipStream_t side = nullptr;
   hipStream_t side2 = nullptr;  // W_down, concurrent with routing
   hipEvent_t ev_fork = nullptr, ev_fork2 = nullptr, ev_join = nullptr, ev_join2 = nullptr;
+  hipEvent_t ev_hi = nullptr, ev_hi_done = nullptr;  // the hi class's expert down beside the bf16 class
   // graph replay of the whole forward (latentmoe_forward_graph)
   hipStream_t cap = nullptr;  // capture stream
   hipGraph_t graph = nullptr;
@@ -435,7 +439,9 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
       hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_fork2, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_join2, hipEventDisableTiming) != hipSuccess) {
+      hipEventCreateWithFlags(&h->ev_join2, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_hi, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_hi_done, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
     latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
@@ -474,6 +480,8 @@ int latentmoe_destroy(latentmoe_handle_t h) {
   if (h->ev_fork2) (void)hipEventDestroy(h->ev_fork2);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_join2) (void)hipEventDestroy(h->ev_join2);
+  if (h->ev_hi) (void)hipEventDestroy(h->ev_hi);
+  if (h->ev_hi_done) (void)hipEventDestroy(h->ev_hi_done);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->side2) (void)hipStreamDestroy(h->side2);
   drop_graph(h);
@@ -676,7 +684,6 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       launch_gemm_stream(g, fp4 ? WF_FP4 : WF_BF16, s);
   };
 
-  tm.start(LATENTMOE_STAGE_EXPERT_UP);
   GemmParams pu = pe;
   pu.seg[0] = GemmSeg{b.z, w.expert_w1, L};
   pu.a_lo = expert_a16 ? nullptr : b.z_lo;
@@ -693,10 +700,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pu.C = b.h;
   pu.C2 = expert_a16 ? nullptr : b.h_lo;
   pu.ldc = m;
-  launch_expert(pu, EPI_SQRELU_BF16);
-  tm.stop(LATENTMOE_STAGE_EXPERT_UP);
 
-  tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
   GemmParams pw = pe;
   pw.seg[0] = GemmSeg{b.h, w.expert_w2, m};
   pw.a_lo = expert_a16 ? nullptr : b.h_lo;
@@ -713,8 +717,37 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pw.row_scale = b.row_gate;
   pw.C = b.og;
   pw.ldc = L;
-  launch_expert(pw, EPI_GATE_F32);
-  tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
+
+  // With split rows the hi class is a few tiles (often one expert's: the launches
+  // fill part of the GPU); its expert down needs only its own expert up, so it runs
+  // on side stream 2 beside the bf16 class's expert up, and the combine waits for
+  // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
+  const bool hi_side = split_rows && LMOE_HI_DOWN_SIDE && !tm.on;
+  if (hi_side) {
+    launch_gemm_big(pu, s);  // expert up, hi tiles
+    (void)hipEventRecord(h->ev_hi, s);
+    (void)hipStreamWaitEvent(side2, h->ev_hi, 0);
+    launch_gemm_big(pw, side2);  // expert down, hi tiles
+    (void)hipEventRecord(h->ev_hi_done, side2);
+    auto lo = [&](GemmParams g, int epi_lo) {  // tiles [n_tiles[0], n_tiles[0] + n_tiles[1])
+      g.n_tiles = b.n_tiles + 1;
+      g.tile_first = b.n_tiles;
+      g.a_lo = nullptr;
+      g.epi = epi_lo;
+      g.C2 = nullptr;
+      launch_gemm_big(g, s);
+    };
+    lo(pu, EPI_SQRELU_BF16);
+    lo(pw, EPI_GATE_F32);
+    (void)hipStreamWaitEvent(s, h->ev_hi_done, 0);
+  } else {
+    tm.start(LATENTMOE_STAGE_EXPERT_UP);
+    launch_expert(pu, EPI_SQRELU_BF16);
+    tm.stop(LATENTMOE_STAGE_EXPERT_UP);
+    tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
+    launch_expert(pw, EPI_GATE_F32);
+    tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
+  }
 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);

@@ -301,6 +301,34 @@ def test_graph_replay_matches_eager_and_oracle():
     layer.close()
 
 
+def test_graph_replay_large_tiles():
+    """The large-tile path with two row classes in a graph (the hi class's expert
+    down runs on a side stream beside the other class's expert up): every replay
+    equals the eager forward bit for bit, and the oracle within the bar."""
+    import torch
+    wl = small_wl(T=1100, d=256, latent=64, n_experts=32, top_k=8, expert_hidden=128, shared_hidden=256)
+    x, W = gen(wl, 23)
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    y = torch.empty((wl.T, wl.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.T, wl.top_k), dtype=torch.int32, device="cuda")
+    g = torch.empty((wl.T, wl.top_k), dtype=torch.float32, device="cuda")
+    for rep in range(3):
+        y.fill_(float("nan"))
+        layer.forward(xd, y, idx, g, graph=True)
+        torch.cuda.synchronize()
+        ye, ie, ge = layer.forward(xd)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ye) and torch.equal(idx, ie) and torch.equal(g, ge), rep
+    ref = oracle.forward(x, W, wl.top_k)
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    err = np.max(np.abs(y.cpu().numpy() - ref["y"]))
+    log("large-tile graph replay: max|gpu-oracle| / rms = %.2e" % (err / rms))
+    assert err <= 1e-2 * rms
+    layer.close()
+
+
 def test_super_verify_sweep():
     """Speculative-verify decode batches at Super shapes, T = users x 8 from 8 to
     512 (prefixes of one 512-token batch; the 16- and 64-row expert tiles):
