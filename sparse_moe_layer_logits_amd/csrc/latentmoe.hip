@@ -68,6 +68,9 @@ constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kerne
 #define LMOE_LOWP_A16 1
 #endif
 
+#ifndef LMOE_BIG_KGRAN
+#define LMOE_BIG_KGRAN 512
+#endif
 #ifndef LMOE_HI_DOWN_SIDE
 #define LMOE_HI_DOWN_SIDE 1  // hi-class expert down on side stream 2 beside the bf16-class expert up
 #endif
@@ -94,7 +97,9 @@ Plan plan_dense(int M, int N, int K) {
   p.stream = M <= STREAM_ROWS_BIG;
   const int per_split = p.stream ? ceil_div(N, 128) * ceil_div(M, STREAM_ROWS_BIG)
                                  : ceil_div(N, 256) * ceil_div(M, TILE_ROWS);
-  const int gran = 256;
+  // smallest k range of a split: with four or more row tiles the large-tile GEMMs
+  // have blocks enough, and halving their splits halves the partial sums' traffic
+  const int gran = !p.stream && M >= 4 * TILE_ROWS ? LMOE_BIG_KGRAN : 256;
   int want = std::max(1, ceil_div(p.stream ? TARGET_BLOCKS : TARGET_BLOCKS_BIG, per_split));
   want = std::min(want, std::max(1, K / gran));
   int ks = ceil_div(ceil_div(K, want), gran) * gran;
