@@ -507,13 +507,14 @@ static void big_for_each_epi(int epi, F&& f) {
     case EPI_F32: f(std::integral_constant<int, EPI_F32>{}); break;
     case EPI_F32_ADD: f(std::integral_constant<int, EPI_F32_ADD>{}); break;
     case EPI_GATE_F32: f(std::integral_constant<int, EPI_GATE_F32>{}); break;
+    case EPI_GATE_BF16: f(std::integral_constant<int, EPI_GATE_BF16>{}); break;
     default: break;
   }
 }
 
 int gemm_big_setup() {
   const int kinds[] = {EPI_PARTIAL, EPI_BF16_HILO, EPI_SQRELU_HILO, EPI_SQRELU_BF16,
-                       EPI_F32, EPI_F32_ADD, EPI_GATE_F32};
+                       EPI_F32, EPI_F32_ADD, EPI_GATE_F32, EPI_GATE_BF16};
   hipError_t e = hipSuccess;
   for (int k : kinds) {
     big_for_each_epi(k, [&](auto E) {
@@ -526,7 +527,8 @@ int gemm_big_setup() {
 
 bool gemm_big_supports(int epi) {
   return epi == EPI_PARTIAL || epi == EPI_BF16_HILO || epi == EPI_SQRELU_HILO ||
-         epi == EPI_SQRELU_BF16 || epi == EPI_F32 || epi == EPI_F32_ADD || epi == EPI_GATE_F32;
+         epi == EPI_SQRELU_BF16 || epi == EPI_F32 || epi == EPI_F32_ADD || epi == EPI_GATE_F32 ||
+         epi == EPI_GATE_BF16;
 }
 
 void launch_gemm_big(const GemmParams& p, hipStream_t s) {

@@ -116,9 +116,12 @@ void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
                   float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s);
-// y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo
-void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
-                    uint16_t* y_lat_lo, hipStream_t s);
+// y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo.  With og16,
+// rows whose gate is below tau are read from og16 (bf16) instead; z32 / z16 are
+// zero rows of L elements.
+void launch_combine(const float* og, const uint16_t* og16, const float* row_gate, float tau,
+                    const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
+                    uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s);
 // FP4 blocks (8 code bytes + 1 scale byte each) -> exact bf16 with the in-register
 // decoder (tensor scale not applied): decode check and the bf16 expansion at init
 void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n_blocks16,

@@ -71,6 +71,9 @@ constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kerne
 #ifndef LMOE_BIG_KGRAN
 #define LMOE_BIG_KGRAN 512
 #endif
+#ifndef LMOE_OG16
+#define LMOE_OG16 1  // bf16-class expert-down rows stored as bf16 (two row classes)
+#endif
 #ifndef LMOE_HI_DOWN_SIDE
 #define LMOE_HI_DOWN_SIDE 1  // hi-class expert down on side stream 2 beside the bf16-class expert up
 #endif
@@ -139,6 +142,9 @@ struct Buffers {
   uint16_t* h = nullptr;
   uint16_t* h_lo = nullptr;
   float* og = nullptr;
+  uint16_t* og16 = nullptr;  // bf16-class expert-down rows (large-tile path, two row classes)
+  float* zrow32 = nullptr;   // zero rows of `latent` elements (fp32, bf16) for the combine
+  uint16_t* zrow16 = nullptr;
   uint16_t* y_lat = nullptr;
   uint16_t* y_lat_lo = nullptr;
   uint16_t* hs_hi = nullptr;
@@ -240,6 +246,9 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.h, TK * c.expert_hidden * 2);
   L.add((void**)&b.h_lo, TK * c.expert_hidden * 2);
   L.add((void**)&b.og, TK * c.latent * 4);
+  L.add((void**)&b.og16, TK * c.latent * 2);
+  L.add((void**)&b.zrow32, (size_t)c.latent * 4);
+  L.add((void**)&b.zrow16, (size_t)c.latent * 2);
   L.add((void**)&b.y_lat, Tm * c.latent * 2);
   L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
   L.add((void**)&b.hs_hi, Tm * c.shared_hidden * 2);
@@ -452,6 +461,12 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_HIP;
   }
   launch_router_split(w->router_w, h->b.pieces, (long long)cfg->n_experts * cfg->d, stream);
+  if (hipMemsetAsync(h->b.zrow32, 0, (size_t)cfg->latent * 4, stream) != hipSuccess ||
+      hipMemsetAsync(h->b.zrow16, 0, (size_t)cfg->latent * 2, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    latentmoe_destroy(h);
+    return LATENTMOE_ERR_HIP;
+  }
   if (h->b.w1_scale_sm) {
     launch_scale_stage_major(w->expert_w1_scale, h->b.w1_scale_sm, cfg->n_experts,
                              cfg->expert_hidden, cfg->latent, stream);
@@ -670,8 +685,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pe.M = rows_per_tile;
   pe.splits = 1;
 
-  // epi_lo: the epilogue of the bf16-class launch (split rows)
-  auto launch_expert = [&](const GemmParams& g, int epi_lo) {
+  // epi_lo, c_lo: the epilogue and output of the bf16-class launch (split rows)
+  auto launch_expert = [&](const GemmParams& g, int epi_lo, void* c_lo) {
     if (split_rows) {
       launch_gemm_big(g, s);  // hi tiles: tiles [0, n_tiles[0])
       GemmParams gl = g;      // then tiles [n_tiles[0], n_tiles[0] + n_tiles[1]), one part
@@ -679,6 +694,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       gl.tile_first = b.n_tiles;
       gl.a_lo = nullptr;
       gl.epi = epi_lo;
+      gl.C = c_lo;
       gl.C2 = nullptr;
       launch_gemm_big(gl, s);
     } else if (!expert_stream)
@@ -728,35 +744,40 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // on side stream 2 beside the bf16 class's expert up, and the combine waits for
   // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
   const bool hi_side = split_rows && LMOE_HI_DOWN_SIDE && !tm.on;
+  // the bf16 class's expert-down rows go out as bf16: their rounding enters y_lat times
+  // a gate below the class threshold, like that of their bf16 z and h
+  const bool og_mix = split_rows && LMOE_OG16;
   if (hi_side) {
     launch_gemm_big(pu, s);  // expert up, hi tiles
     (void)hipEventRecord(h->ev_hi, s);
     (void)hipStreamWaitEvent(side2, h->ev_hi, 0);
     launch_gemm_big(pw, side2);  // expert down, hi tiles
     (void)hipEventRecord(h->ev_hi_done, side2);
-    auto lo = [&](GemmParams g, int epi_lo) {  // tiles [n_tiles[0], n_tiles[0] + n_tiles[1])
+    auto lo = [&](GemmParams g, int epi_lo, void* c_lo) {  // tiles [n_tiles[0], n_tiles[0] + n_tiles[1])
       g.n_tiles = b.n_tiles + 1;
       g.tile_first = b.n_tiles;
       g.a_lo = nullptr;
       g.epi = epi_lo;
+      g.C = c_lo;
       g.C2 = nullptr;
       launch_gemm_big(g, s);
     };
-    lo(pu, EPI_SQRELU_BF16);
-    lo(pw, EPI_GATE_F32);
+    lo(pu, EPI_SQRELU_BF16, b.h);
+    lo(pw, og_mix ? EPI_GATE_BF16 : EPI_GATE_F32, og_mix ? (void*)b.og16 : (void*)b.og);
     (void)hipStreamWaitEvent(s, h->ev_hi_done, 0);
   } else {
     tm.start(LATENTMOE_STAGE_EXPERT_UP);
-    launch_expert(pu, EPI_SQRELU_BF16);
+    launch_expert(pu, EPI_SQRELU_BF16, b.h);
     tm.stop(LATENTMOE_STAGE_EXPERT_UP);
     tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
-    launch_expert(pw, EPI_GATE_F32);
+    launch_expert(pw, og_mix ? EPI_GATE_BF16 : EPI_GATE_F32, og_mix ? (void*)b.og16 : (void*)b.og);
     tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
   }
 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);
-  launch_combine(b.og, b.inv, T, K, L, b.y_lat, b.y_lat_lo, s);
+  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.row_gate, (float)LMOE_HI_TAU, b.zrow32, b.zrow16, b.inv,
+                 T, K, L, b.y_lat, b.y_lat_lo, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
   // ---- 8. y += W_up y_lat (after the shared expert wrote y) ----

@@ -41,26 +41,61 @@ void launch_reduce(const GemmParams& p, hipStream_t s) {
 // their gate; the sum runs k = 0 .. K-1, so the result does not depend on
 // scheduling.  The fp32 sum leaves as a bf16 pair (hi, lo = sum - hi) so the
 // up-projection sees it to about 16 significant bits.
+//
+// MIX (large-tile path with two row classes): a row whose gate is below tau (the
+// bf16 class) was written to og16 as bf16, the others to og as fp32.  Every k
+// loads one fp32 and one bf16 row, one of them the zero row z32 / z16, and adds
+// both: the sum and its order are those of a single format, and a bf16-class row
+// costs half the bytes from memory (the zero rows stay cached).
+template <bool MIX>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ og,
+                                                     const uint16_t* __restrict__ og16,
+                                                     const float* __restrict__ row_gate, float tau,
+                                                     const float* __restrict__ z32,
+                                                     const uint16_t* __restrict__ z16,
                                                      const int* __restrict__ inv, int K, int L,
                                                      uint16_t* __restrict__ y_lat,
                                                      uint16_t* __restrict__ y_lat_lo) {
   __shared__ int pos[64];
+  __shared__ int wide[64];
   const int t = blockIdx.x;
-  if (threadIdx.x < K) pos[threadIdx.x] = inv[(long long)t * K + threadIdx.x];
+  if (threadIdx.x < K) {
+    const int q = inv[(long long)t * K + threadIdx.x];
+    pos[threadIdx.x] = q;
+    wide[threadIdx.x] = !MIX || row_gate[q] >= tau;  // the class top-K assigned (same fp32 test)
+  }
   __syncthreads();
   const int c = (blockIdx.y * 64 + threadIdx.x) * 4;
   if (c >= L) return;
+  // row k's two sources, formed from the global arguments (addresses kept in LDS
+  // would be generic and turn the loads into flat ones)
+  auto p32 = [&](int k) { return wide[k] ? og + (long long)pos[k] * L + c : z32 + c; };
+  auto p16 = [&](int k) { return wide[k] ? z16 + c : og16 + (long long)pos[k] * L + c; };
+  auto widen = [](const u32x2_t& w) {
+    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int k = 0;
-  for (; k + 8 <= K; k += 8) {  // eight loads in flight, summed in k order
+  for (; k + 8 <= K; k += 8) {  // eight rows in flight, summed in k order
     f32x4_t v[8];
+    u32x2_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const f32x4_t*>(og + (long long)pos[k + i] * L + c);
+    for (int i = 0; i < 8; ++i) {
+      v[i] = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k + i) : og + (long long)pos[k + i] * L + c);
+      if constexpr (MIX) w[i] = *reinterpret_cast<const u32x2_t*>(p16(k + i));
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc += v[i];
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (MIX) v[i] += widen(w[i]);
+      acc += v[i];
+    }
   }
-  for (; k < K; ++k) acc += *reinterpret_cast<const f32x4_t*>(og + (long long)pos[k] * L + c);
+  for (; k < K; ++k) {
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k) : og + (long long)pos[k] * L + c);
+    if constexpr (MIX) v += widen(*reinterpret_cast<const u32x2_t*>(p16(k)));
+    acc += v;
+  }
   float hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -71,11 +106,16 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   store_bf16x4(y_lat_lo, (long long)t * L + c, lo[0], lo[1], lo[2], lo[3]);
 }
 
-void launch_combine(const float* og, const int* inv, int T, int K, int L, uint16_t* y_lat,
-                    uint16_t* y_lat_lo, hipStream_t s) {
+void launch_combine(const float* og, const uint16_t* og16, const float* row_gate, float tau,
+                    const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
+                    uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s) {
   if (T <= 0) return;
   dim3 grid(T, (L / 4 + 63) / 64);
-  combine_kernel<<<grid, 64, 0, s>>>(og, inv, K, L, y_lat, y_lat_lo);
+  if (og16)
+    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, row_gate, tau, z32, z16, inv, K, L, y_lat, y_lat_lo);
+  else
+    combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, 0.f, nullptr, nullptr, inv, K, L, y_lat,
+                                              y_lat_lo);
 }
 
 // decode n_blocks16 FP4 blocks (8 code bytes + 1 scale byte each) to bf16

@@ -115,7 +115,8 @@ def full_check(wl, x, W, tol=1e-2, extra=("z", "z_lo", "y_lat", "y_lat_lo", "cou
     split = splits_rows(wl)
     if "y_lat" in out:
         # every stage carries ~16 bits: the latent sum matches closely (rows
-        # carried at bf16 on the large-tile path add up to ~3e-3 of it).  FP4
+        # carried at bf16 on the large-tile path, their z, h and gated expert
+        # output, add up to ~8e-3 of it at most: 1100 tokens, top-8 of 32).  FP4
         # experts take bf16 activations (weight-only quantisation): their z and h
         # roundings reach ~1e-2 of the latent sum, held to the FP4 output bound
         yl = oracle.bf16_to_f64(out["y_lat"]) + oracle.bf16_to_f64(out["y_lat_lo"])
