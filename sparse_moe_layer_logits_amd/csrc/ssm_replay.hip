@@ -105,7 +105,39 @@ __global__ __launch_bounds__(SSM_THREADS) void ssm_verify_kernel(SsmArgs A) {
   const bool key_writer = h % (A.H / A.G) == 0;  // one head per group appends the keys
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, gq = lane >> 4;
+
   const int T = A.T, cap = A.cap;
+  // Loads that do not depend on the buffer's record count go first, so that their
+  // latency overlaps the count's (a branch on the count would otherwise hold them).
+  // ---- state rows of this wave's tiles: A operands of the U products, in flight
+  // while the records are staged ----
+  u32x4_t sa[TPW][N / 32];
+#pragma unroll
+  for (int w = 0; w < TPW; ++w) {
+    const int tile = wave + 4 * w;
+    if (tile < TILES) {
+      const uint16_t* row = A.ckpt + (((long long)r * A.H + h) * P + tile * 16 + r16) * N;
+#pragma unroll
+      for (int st = 0; st < N / 32; ++st) sa[w][st] = ld128(row + 32 * st + 8 * gq);
+    }
+  }
+
+  // ---- records (16-byte pieces, loads issued before use; the T tokens are appended
+  // to the buffer on the way): the drafts first ----
+  const long long rq = (long long)r * T;
+  constexpr int KQ_IT = (SSM_T_MAX * N8 + SSM_THREADS - 1) / SSM_THREADS;
+  constexpr int KB_IT = (SSM_CAP_MAX * N8 + SSM_THREADS - 1) / SSM_THREADS;
+  constexpr int V_IT = (SSM_CAP_MAX * P8 + SSM_THREADS - 1) / SSM_THREADS;
+  u32x4_t dq[KQ_IT], dk[KQ_IT], bk[KB_IT], vv[V_IT];
+#pragma unroll
+  for (int u = 0; u < KQ_IT; ++u) {
+    const int i = tid + u * SSM_THREADS;
+    if (i < T * N8) {
+      const long long src = ((rq + i / N8) * A.G + g) * N + (i % N8) * 8;
+      dq[u] = ld128(A.q + src);
+      dk[u] = ld128(A.k + src);
+    }
+  }
   const int len = A.buf_len[r];
   const int J = len + T;  // records up to the last verified token
 
@@ -125,35 +157,6 @@ __global__ __launch_bounds__(SSM_THREADS) void ssm_verify_kernel(SsmArgs A) {
   float* coef = as + 32;                              // [16][33] C * w
   float* D = coef + 16 * 33;                          // [16]
 
-  // ---- state rows of this wave's tiles: A operands of the U products, in flight
-  // while the records are staged ----
-  u32x4_t sa[TPW][N / 32];
-#pragma unroll
-  for (int w = 0; w < TPW; ++w) {
-    const int tile = wave + 4 * w;
-    if (tile < TILES) {
-      const uint16_t* row = A.ckpt + (((long long)r * A.H + h) * P + tile * 16 + r16) * N;
-#pragma unroll
-      for (int st = 0; st < N / 32; ++st) sa[w][st] = ld128(row + 32 * st + 8 * gq);
-    }
-  }
-
-  // ---- records (16-byte pieces, loads issued before use; the T tokens are appended
-  // to the buffer on the way) ----
-  const long long rq = (long long)r * T;
-  constexpr int KQ_IT = (SSM_T_MAX * N8 + SSM_THREADS - 1) / SSM_THREADS;
-  constexpr int KB_IT = (SSM_CAP_MAX * N8 + SSM_THREADS - 1) / SSM_THREADS;
-  constexpr int V_IT = (SSM_CAP_MAX * P8 + SSM_THREADS - 1) / SSM_THREADS;
-  u32x4_t dq[KQ_IT], dk[KQ_IT], bk[KB_IT], vv[V_IT];
-#pragma unroll
-  for (int u = 0; u < KQ_IT; ++u) {
-    const int i = tid + u * SSM_THREADS;
-    if (i < T * N8) {
-      const long long src = ((rq + i / N8) * A.G + g) * N + (i % N8) * 8;
-      dq[u] = ld128(A.q + src);
-      dk[u] = ld128(A.k + src);
-    }
-  }
 #pragma unroll
   for (int u = 0; u < KB_IT; ++u) {
     const int i = tid + u * SSM_THREADS;
