@@ -329,6 +329,31 @@ def test_graph_replay_large_tiles():
     layer.close()
 
 
+def test_stage_timing_keeps_outputs():
+    """Stage-timed forwards (latentmoe_profile_begin) keep the plain launch order on
+    the large-tile path, where untimed ones run the hi class's expert down beside
+    the other class's expert up: both give the same outputs bit for bit, and every
+    stage reports a time."""
+    import torch
+    wl = small_wl(T=1100, d=256, latent=64, n_experts=32, top_k=8, expert_hidden=128, shared_hidden=256)
+    x, W = gen(wl, 24)
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    y0, i0, g0 = layer.forward(xd)
+    torch.cuda.synchronize()
+    layer.profile_begin(2)
+    for _ in range(2):
+        y1, i1, g1 = layer.forward(xd)
+    stages, calls = layer.profile_end()
+    torch.cuda.synchronize()
+    assert calls == 2
+    assert torch.equal(y0, y1) and torch.equal(i0, i1) and torch.equal(g0, g1)
+    log("stage ms over 2 calls: %s" % {k: round(v, 4) for k, v in stages.items()})
+    assert all(v > 0 for v in stages.values()), stages
+    layer.close()
+
+
 def test_super_verify_sweep():
     """Speculative-verify decode batches at Super shapes, T = users x 8 from 8 to
     512 (prefixes of one 512-token batch; the 16- and 64-row expert tiles):
