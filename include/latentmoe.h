@@ -71,7 +71,10 @@ typedef struct latentmoe_handle_s* latentmoe_handle_t;
 /* Layer shape (host struct).  Requirements, checked by latentmoe_init:
  * d, latent, expert_hidden, shared_hidden multiples of 64; n_experts a
  * multiple of 16 and at most 1024; 1 <= top_k <= min(n_experts, 64);
- * max_tokens >= 1. */
+ * max_tokens >= 1; the activation matrices the kernels address with 32-bit
+ * offsets stay below 2^31 elements: max_tokens * top_k * max(latent,
+ * expert_hidden) and max_tokens * max(d, shared_hidden) (at the Super shapes,
+ * d = 4096, l = 1024, m = 2688, m_s = 5376, K = 22: max_tokens <= 36314). */
 typedef struct {
   int32_t d;             /* model width                                   */
   int32_t latent;        /* latent width l                                */
@@ -117,6 +120,8 @@ typedef struct {
  * workspace on `stream`: dense GEMMs of more than 64 tokens run on the
  * LDS-tiled kernel, which reads bf16 weights; up to 64 tokens the stored
  * format is streamed and decoded in registers.  No other work is enqueued.
+ * The call waits for that work to finish (it synchronises `stream`) before it
+ * returns, so the handle may be used on any stream afterwards.
  * cfg, w: host pointers, read during the call only.  out: host pointer that
  * receives the handle (set to NULL on failure).
  * Errors: INVALID_ARG (null pointer, including a scale pointer that the
@@ -177,12 +182,17 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
  *   LATENTMOE_INTER_HS_LO    [T, m_s] bf16     shared hidden, remainder
  *   LATENTMOE_INTER_Z_LO     [T, l] bf16       latent tokens, remainder
  *   LATENTMOE_INTER_H_LO     [T*K, m] bf16     expert hidden, remainder
+ *   LATENTMOE_INTER_PAIRED   [T, K] uint8      large-tile path only: 1 where the
+ *                                              routed row (t, k) carries hi + lo
  * Permuted order: the rows of expert e are [OFFSETS[e], OFFSETS[e+1]), sorted
  * by token.  When the layer runs its large-tile path (bf16 experts and more
- * than 48 routed rows per expert on average, T*K/N > 48), the rows of each
- * expert whose gate is at least 0.1 come first (sorted by token), then the
- * others (sorted by token): only the first group carries z and h as hi + lo
- * pairs, the others as bf16 (H_LO is not written for them).  GEMMs with FP4 or
+ * than 48 routed rows per expert on average, T*K/N > 48), each token's rows
+ * with the largest gates are "paired": in top-K order (largest gate first),
+ * row k is paired unless sum_{j >= k} g_j^2 <= sum_j g_j^2 / 32 (fp32, sums over
+ * the token's K rows).  The paired rows of each expert come first (sorted by
+ * token), then the others (sorted by token): only the first group carries z,
+ * h and the gated expert output as hi + lo pairs or fp32, the others as bf16
+ * (H_LO is not written for them).  GEMMs with FP4 or
  * FP8 weights take single bf16 activations (weight-only quantisation, 16-bit
  * activations): with FP4 experts H_LO is not written, with an FP4 shared expert
  * HS_LO is not written, and FP8 projections read Y_LAT but not Y_LAT_LO.
@@ -200,6 +210,7 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
 #define LATENTMOE_INTER_Y_LAT_LO 9
 #define LATENTMOE_INTER_Z_LO 10
 #define LATENTMOE_INTER_H_LO 11
+#define LATENTMOE_INTER_PAIRED 12
 int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t bytes,
                          hipStream_t stream);
 

@@ -27,7 +27,8 @@ LATENTMOE_FORMAT_FP8_E4M3 = 2
 LATENTMOE_EXPERTS_BF16 = LATENTMOE_FORMAT_BF16
 LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 = LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16
 
-INTER = dict(z=0, y_lat=1, counts=2, offsets=3, row_src=4, inv=5, h=6, hs_hi=7, hs_lo=8, y_lat_lo=9, z_lo=10, h_lo=11)
+INTER = dict(z=0, y_lat=1, counts=2, offsets=3, row_src=4, inv=5, h=6, hs_hi=7, hs_lo=8, y_lat_lo=9, z_lo=10, h_lo=11,
+             paired=12)
 STAGES = ["router", "topk", "bucket", "down_proj", "expert_up", "expert_down", "combine",
           "shared_up", "shared_down", "up_proj"]
 

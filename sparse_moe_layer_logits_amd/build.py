@@ -30,16 +30,14 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, out_dir: str = OUT_DIR, defines=()) -> str:
-    """Compile every source and link liblatentmoe.so into out_dir.  `defines`
-    are extra -D settings for the kernels' tunables."""
+def build(verbose: bool = False, out_dir: str = OUT_DIR) -> str:
+    """Compile every source and link liblatentmoe.so into out_dir."""
     os.makedirs(out_dir, exist_ok=True)
     lib = os.path.join(out_dir, "liblatentmoe.so")
     objs = [os.path.join(out_dir, s.replace(".hip", ".o")) for s in SOURCES]
-    extra = ["-D" + d for d in defines]
 
     def one(i):
-        return _run([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
+        return _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, SOURCES[i]), "-o", objs[i]])
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         for out in ex.map(one, range(len(SOURCES))):

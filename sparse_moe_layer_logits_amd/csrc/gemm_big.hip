@@ -44,27 +44,13 @@ __device__ __forceinline__ int bg_off(int row, int piece) {
   return row * BG_ROWB + ((piece ^ ((row >> 1) & 3)) << 4);
 }
 
-#ifndef LMOE_BIG_STAGES
-#define LMOE_BIG_STAGES 4
-#endif
+// ring depth: 3 stages of 48 KB (dual) or 4 of 32 KB (single)
 template <bool DUAL>
-constexpr int bg_stages() { return DUAL ? 3 : LMOE_BIG_STAGES; }
+constexpr int bg_stages() { return DUAL ? 3 : 4; }
 
-// waves per block: 4 (2 x 2 waves of 128 x 128) or 8 (2 x 4 waves of 128 x 64, two
-// waves per SIMD: one wave's LDS reads and waits overlap the other's MFMAs)
-#ifndef LMOE_BIG_WAVES
-#define LMOE_BIG_WAVES 8
-#endif
-constexpr int BG_WAVES = LMOE_BIG_WAVES;
-#ifndef LMOE_BIG_PIPE
-#define LMOE_BIG_PIPE 1
-#endif
-#ifndef LMOE_BIG_NT
-#define LMOE_BIG_NT 1
-#endif
-#ifndef LMOE_BIG_XCD
-#define LMOE_BIG_XCD 1
-#endif
+// 8 waves of 128 x 64 (2 x 4), two waves per SIMD: one wave's LDS reads and waits
+// overlap the other's MFMAs
+constexpr int BG_WAVES = 8;
 constexpr int BG_THREADS = 64 * BG_WAVES;
 constexpr int BG_WM = BG_WAVES / 2;        // waves along the activation rows
 constexpr int BG_MB = BG_BM / BG_WM / 16;  // 16-row activation tiles per wave
@@ -73,18 +59,18 @@ constexpr int BG_CPW = 16 / BG_WAVES;      // 1 KB chunks per wave per operand t
 // wait until at most n of this wave's vector-memory loads are outstanding
 __device__ __forceinline__ void wait_vmcnt(int n) {
   // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at max
-#define LMOE_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define VMCNT_WAIT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
   switch (n) {
-    case 0: LMOE_VMCNT(0); break;
-    case 4: LMOE_VMCNT(4); break;
-    case 6: LMOE_VMCNT(6); break;
-    case 8: LMOE_VMCNT(8); break;
-    case 12: LMOE_VMCNT(12); break;
-    case 16: LMOE_VMCNT(16); break;
-    case 24: LMOE_VMCNT(24); break;
-    default: LMOE_VMCNT(0); break;
+    case 0: VMCNT_WAIT(0); break;
+    case 4: VMCNT_WAIT(4); break;
+    case 6: VMCNT_WAIT(6); break;
+    case 8: VMCNT_WAIT(8); break;
+    case 12: VMCNT_WAIT(12); break;
+    case 16: VMCNT_WAIT(16); break;
+    case 24: VMCNT_WAIT(24); break;
+    default: VMCNT_WAIT(0); break;
   }
-#undef LMOE_VMCNT
+#undef VMCNT_WAIT
 }
 
 // Output tile through LDS.  A lane's accumulators hold 4 columns of one row, so
@@ -209,11 +195,7 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
             v = __builtin_bit_cast(u32x4_t, w);
           }
         }
-#if LMOE_BIG_NT
         __builtin_nontemporal_store(v, dst);
-#else
-        *dst = v;
-#endif
       }
     }
     if (half == 0) __syncthreads();  // the copy has read the staged half
@@ -241,7 +223,6 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   int item = blockIdx.x;
   bool mapped = false;
   int j = 0, q = 0;
-#if LMOE_BIG_XCD
   // Blocks are dealt to the 8 XCDs in turn (block b to XCD b % 8), and each XCD
   // has its own L2.  Expert tiles: XCD x takes the contiguous tile range
   // [x TPX, (x + 1) TPX) of the n_tiles listed, each tile's NQ column blocks in a
@@ -262,7 +243,6 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     }
     mapped = true;
   }
-#endif
   int split = 0;
   if (!mapped) {
     split = item % p.splits;
@@ -387,7 +367,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
         for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[part][b], acc[a][b]);
   };
 
-  if constexpr (!DUAL && LMOE_BIG_PIPE) {
+  if constexpr (!DUAL) {
     // Next step's fragments are read while this step's MFMAs run: after step
     // kt + 1's barrier the wave reads that step's activation fragments into a
     // second set and, as soon as the 4 MFMAs of weight fragment a have issued,
@@ -534,9 +514,7 @@ bool gemm_big_supports(int epi) {
 void launch_gemm_big(const GemmParams& p, hipStream_t s) {
   const int NQ = (p.N + BG_BN - 1) / BG_BN;
   long long tiles = p.tile_expert ? p.max_tiles : (p.M + BG_BM - 1) / BG_BM;
-#if LMOE_BIG_XCD
   if (p.splits == 1) tiles = (tiles + 7) / 8 * 8;  // whole groups of 8 tiles
-#endif
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
   if (p.a_lo)

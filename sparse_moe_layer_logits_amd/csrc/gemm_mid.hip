@@ -30,9 +30,6 @@
 
 #include <type_traits>
 
-#ifndef LMOE_MID_SETS
-#define LMOE_MID_SETS 3  // register sets: loads run LMOE_MID_SETS - 1 stages ahead
-#endif
 
 namespace lmoe {
 
@@ -70,7 +67,7 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   constexpr int BN = 64 * W;
   constexpr int XP = (MD_PIECES + NTH - 1) / NTH;
   // register sets: three fit next to two activation pieces per thread
-  constexpr int NS = XP <= 2 ? LMOE_MID_SETS : 2;
+  constexpr int NS = XP <= 2 ? 3 : 2;  // loads run NS - 1 stages ahead
   constexpr int SLOTB = NP * MD_PARTB + BN * 8;  // activation parts + scales
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -93,17 +93,8 @@ struct BFrag<WF_FP8> {
   u32x4_t codes;   // 16 E4M3 bytes: step 0 in words 0-1, step 1 in words 2-3
 };
 
-#ifndef LMOE_ST_FP4_RING
-#define LMOE_ST_FP4_RING 2
-#endif
-
-#ifndef LMOE_ST_FP4_WAVES
-#define LMOE_ST_FP4_WAVES 1
-#endif
-
 template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
-    FMT == WF_FP4 ? LMOE_ST_FP4_WAVES : 1))) void gemm_stream_kernel(GemmParams p) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) void gemm_stream_kernel(GemmParams p) {
   constexpr int MTMAX = ROWS / 16;
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int KC = 64 * PAIRS;                           // k per chunk
@@ -379,8 +370,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
     // leaves the younger chunks in flight.  Every step issues the same loads (clamped
     // to the last chunk past the end) and the loop has one exit, so the compiler's
     // wait counts stay exact.
-    constexpr int R = LMOE_ST_FP4_RING;
-    static_assert(R == 2 || R == 4, "ring of 2 or 4 chunks");
+    constexpr int R = 2;
     BFrag<FMT> ring[R][PAIRS][NT];
     u32x4_t aring[R][APT];
     const int last = nchunks - 1;
@@ -437,39 +427,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(
   });
 }
 
-#ifndef LMOE_ST_W
-#define LMOE_ST_W 8
-#endif
-#ifndef LMOE_ST_PAIRS16
-#define LMOE_ST_PAIRS16 4
-#endif
-#ifndef LMOE_ST_PAIRS16_FP4
-#define LMOE_ST_PAIRS16_FP4 4
-#endif
-#ifndef LMOE_ST_PAIRS_FP4
-#define LMOE_ST_PAIRS_FP4 0
-#endif
-
-#ifndef LMOE_ST_W_FP4
-#define LMOE_ST_W_FP4 8
-#endif
-#ifndef LMOE_ST_NT_FP4
-#define LMOE_ST_NT_FP4 1
-#endif
-
-// block shape: W waves of NT 16-row weight tiles each
-template <int FMT>
-struct StShape {
-  static constexpr int W = LMOE_ST_W, NT = 1;
-};
-template <>
-struct StShape<WF_FP4> {
-  static constexpr int W = LMOE_ST_W_FP4, NT = LMOE_ST_NT_FP4;
-};
+// block shape: 8 waves of one 16-row weight tile each
+constexpr int ST_W = 8, ST_NT = 1;
 
 template <int ROWS, int PAIRS, int FMT, bool DUAL>
 static void launch_rows(const GemmParams& p, long long tiles, hipStream_t s) {
-  constexpr int W = StShape<FMT>::W, NT = StShape<FMT>::NT;
+  constexpr int W = ST_W, NT = ST_NT;
   const long long NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
@@ -482,9 +445,10 @@ static void launch_fmt(const GemmParams& p, int rows, long long tiles, hipStream
     // FP8 weights are the dense projections only: 64-row tiles
     launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, tiles, s);
   } else {
-    constexpr bool F4 = FMT == WF_FP4;
-    constexpr int P16 = F4 ? LMOE_ST_PAIRS16_FP4 : LMOE_ST_PAIRS16;
-    constexpr int P = (F4 && LMOE_ST_PAIRS_FP4) ? LMOE_ST_PAIRS_FP4 : DUAL ? 2 : 4;
+    // 16-row tiles take 4 pairs (256 k) per chunk; 32- and 64-row tiles 2 with a
+    // hi + lo activation, 4 with one part
+    constexpr int P16 = 4;
+    constexpr int P = DUAL ? 2 : 4;
     if (rows == 16)
       launch_rows<16, P16, FMT, DUAL>(p, tiles, s);
     else if (rows == 32)

@@ -95,9 +95,12 @@ void launch_reduce(const GemmParams& p, hipStream_t s);
 void launch_router_split(const float* w, uint16_t* pieces, long long n, hipStream_t s);
 
 // per-token top-K + softmax over logits [T, N] (+ bias); builds per-16-token expert masks
-// (masks_hi, if not null: the routed rows whose gate is at least hi_tau)
+// (masks_hi, if not null: the routed rows that carry a bf16 hi + lo pair -- each
+// token's largest gates until the rows left out hold at most tail_frac of its
+// sum_k g_k^2 -- and paired[t*K + k] = 1 for them, 0 for the others)
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
-                 float* gates, uint32_t* masks, float hi_tau, uint32_t* masks_hi, hipStream_t s);
+                 float* gates, uint32_t* masks, float tail_frac, uint32_t* masks_hi, uint8_t* paired,
+                 hipStream_t s);
 // counts, offsets, per-block prefixes and the expert tile list (tile_rows_max rows per tile);
 // with masks_hi the rows of each expert are split into the hi class (first) and the rest,
 // hi tiles first in the list: n_tiles[0] hi tiles, then n_tiles[1] others.  With place_idx
@@ -117,9 +120,9 @@ void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
                   float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s);
 // y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo.  With og16,
-// rows whose gate is below tau are read from og16 (bf16) instead; z32 / z16 are
+// rows with paired[t*K+k] == 0 are read from og16 (bf16) instead; z32 / z16 are
 // zero rows of L elements.
-void launch_combine(const float* og, const uint16_t* og16, const float* row_gate, float tau,
+void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
                     const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
                     uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s);
 // FP4 blocks (8 code bytes + 1 scale byte each) -> exact bf16 with the in-register

@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -30,61 +31,33 @@ using namespace lmoe;
 
 namespace {
 
-#ifndef LMOE_SHARED_FORK_AT
-#define LMOE_SHARED_FORK_AT 1  // 0: at the start, 1: after the router GEMM, 2: after bucketing
-#endif
-
 constexpr int STREAM_ROWS_BIG = 64;
 constexpr int STREAM_ROWS_SMALL = 16;  // decode expert tiles
 constexpr int STREAM_ROWS_MID = 32;
-#ifndef LMOE_ROWS16_MAX_AVG
-#define LMOE_ROWS16_MAX_AVG 12.0  // up to this many rows per expert on average: 16-row tiles
-#endif
-#ifndef LMOE_ROWS32_MAX_AVG
-#define LMOE_ROWS32_MAX_AVG 24.0  // then up to this many: 32-row tiles, above: 64
-#endif
-constexpr int TILE_ROWS = 256;          // rows per tile of the large-tile kernel
-#ifndef LMOE_HI_TAU
-// Large-tile path (prefill): routed rows whose gate is at least this carry
-// their activations as bf16 hi + lo; the others as bf16.  A row's rounding
-// reaches the output multiplied by its gate, so the small-gate rows add little
-// error (fp64 emulation of the rounding points: max |y - y_exact| rises from
-// 1e-5 to 2.6e-3 rms with a uniform router, stays 1e-5 with the skewed one).
-#define LMOE_HI_TAU 0.1
-#endif
-#ifndef LMOE_SERIAL
-#define LMOE_SERIAL 0  // 1: no side streams
-#endif
-#ifndef LMOE_MID_FP4
-#define LMOE_MID_FP4 1  // FP4 experts with 64-row tiles use the mid kernel
-#endif
+constexpr double ROWS16_MAX_AVG = 12.0;  // up to this many rows per expert on average: 16-row tiles
+constexpr double ROWS32_MAX_AVG = 24.0;  // then up to this many: 32-row tiles, above: 64
+constexpr int TILE_ROWS = 256;           // rows per tile of the large-tile kernel
+// Large-tile path (prefill): a token's routed rows with the largest gates carry
+// their activations (z, h, the gated output) as bf16 hi + lo pairs, the others as
+// bf16 -- as many rows as it takes for the rows left as bf16 to hold at most
+// PAIR_TAIL_FRAC of the token's gate energy sum_k g_k^2.  A row's bf16 rounding
+// reaches the latent sum scaled by its gate; an fp64 emulation of the rounding
+// points keeps the latent sum within 4e-3 of its rms with flat gates (K = 8 of
+// 32, 22 of 512, 40 of 1024: 78-98 % of rows paired) and with skewed ones (one
+// gate near 1: only that row paired), where a fixed gate threshold of 0.1
+// reached 1.6-1.8e-2 with flat gates.
+constexpr float PAIR_TAIL_FRAC = 1.0f / 32.0f;
 // Activations of GEMMs whose weights are stored in FP4 or FP8 are single bf16
 // values: weight-only quantisation with 16-bit activations, the W4A16 mode in
 // which Hopper GPUs serve the NVFP4 checkpoint ("Nemotron 3.5 Super and
 // Lightning", limitations; "Nemotron 3 Ultra", contributions).  bf16 weights keep
 // the hi + lo pairs.  The bf16 rounding of an activation (2^-9 relative) is far
 // below the weight formats' own step.
-#ifndef LMOE_LOWP_A16
-#define LMOE_LOWP_A16 1
-#endif
-
-#ifndef LMOE_BIG_KGRAN
-#define LMOE_BIG_KGRAN 512
-#endif
-#ifndef LMOE_OG16
-#define LMOE_OG16 1  // bf16-class expert-down rows stored as bf16 (two row classes)
-#endif
-#ifndef LMOE_HI_DOWN_SIDE
-#define LMOE_HI_DOWN_SIDE 1  // hi-class expert down on side stream 2 beside the bf16-class expert up
-#endif
-#ifndef LMOE_BUCKET_MIN_CHUNKS
-#define LMOE_BUCKET_MIN_CHUNKS 4  // chunks of 16 mask blocks (256 tokens) from which the count is split
-#endif
-#ifndef LMOE_TARGET_BLOCKS
-#define LMOE_TARGET_BLOCKS 256
-#endif
-constexpr int TARGET_BLOCKS = LMOE_TARGET_BLOCKS;  // streaming kernel: 8-wave blocks, several per CU
-constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 4-wave block per CU
+// smallest k range of a split for large-tile GEMMs with four or more row tiles
+constexpr int BIG_KGRAN = 512;
+constexpr int BUCKET_MIN_CHUNKS = 4;  // chunks of 16 mask blocks (256 tokens) from which the count is split
+constexpr int TARGET_BLOCKS = 256;      // streaming kernel: 8-wave blocks, several per CU
+constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 8-wave block per CU
 
 struct Plan {
   bool stream;  // weight-streaming kernel (true) or LDS-tiled kernel
@@ -102,7 +75,7 @@ Plan plan_dense(int M, int N, int K) {
                                  : ceil_div(N, 256) * ceil_div(M, TILE_ROWS);
   // smallest k range of a split: with four or more row tiles the large-tile GEMMs
   // have blocks enough, and halving their splits halves the partial sums' traffic
-  const int gran = !p.stream && M >= 4 * TILE_ROWS ? LMOE_BIG_KGRAN : 256;
+  const int gran = !p.stream && M >= 4 * TILE_ROWS ? BIG_KGRAN : 256;
   int want = std::max(1, ceil_div(p.stream ? TARGET_BLOCKS : TARGET_BLOCKS_BIG, per_split));
   want = std::min(want, std::max(1, K / gran));
   int ks = ceil_div(ceil_div(K, want), gran) * gran;
@@ -121,7 +94,8 @@ struct Buffers {
   int* idx = nullptr;
   float* gates = nullptr;
   uint32_t* masks = nullptr;
-  uint32_t* masks_hi = nullptr;  // rows whose gate reaches LMOE_HI_TAU (large-tile path)
+  uint32_t* masks_hi = nullptr;  // rows carried as hi + lo pairs (large-tile path)
+  uint8_t* paired = nullptr;     // [T*K]: 1 for those rows, 0 for the bf16 class
   int* block_prefix = nullptr;   // per (block, expert) prefix of the (hi-class) rows
   int* prefix_lo = nullptr;      // the same for the other rows
   int* chunk_hi = nullptr;       // per (chunk of mask blocks, expert) counts -> offsets (large T)
@@ -184,6 +158,12 @@ int check_config(const latentmoe_config* c) {
     return LATENTMOE_ERR_UNSUPPORTED;
   if (c->n_experts % 16 || c->n_experts > 1024) return LATENTMOE_ERR_UNSUPPORTED;
   if (c->top_k > c->n_experts || c->top_k > 64) return LATENTMOE_ERR_UNSUPPORTED;
+  // the large-tile and FP4 kernels address activation rows with 32-bit byte offsets
+  // (bf16 elements): h [T K, m], the gathered z [T, l], x [T, d], h_s [T, m_s]
+  const long long lim = 1ll << 31;
+  if ((long long)c->max_tokens * c->top_k * std::max(c->latent, c->expert_hidden) >= lim ||
+      (long long)c->max_tokens * std::max(c->d, c->shared_hidden) >= lim)
+    return LATENTMOE_ERR_UNSUPPORTED;
   return LATENTMOE_OK;
 }
 
@@ -241,6 +221,7 @@ Layout make_layout(const latentmoe_config& c, Buffers& b) {
   L.add((void**)&b.row_src, TK * 4);
   L.add((void**)&b.row_gate, TK * 4);
   L.add((void**)&b.inv, TK * 4);
+  L.add((void**)&b.paired, TK);
   L.add((void**)&b.z, Tm * c.latent * 2);
   L.add((void**)&b.z_lo, Tm * c.latent * 2);
   L.add((void**)&b.h, TK * c.expert_hidden * 2);
@@ -292,6 +273,10 @@ struct latentmoe_handle_s {
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
   int last_T = 0;
+  // LATENTMOE_SERIAL=1 in the environment at init: every kernel on the caller's
+  // stream in program order (no side streams), so a kernel trace shows each
+  // kernel's own duration
+  bool serial = false;
   // the shared expert runs on a side stream forked from the caller's stream
   hipStream_t side = nullptr;
   hipStream_t side2 = nullptr;  // W_down, concurrent with routing
@@ -428,6 +413,10 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
   if (!h) return LATENTMOE_ERR_OUT_OF_MEMORY;
   h->cfg = *cfg;
   h->w = *w;
+  {
+    const char* ser = std::getenv("LATENTMOE_SERIAL");
+    h->serial = ser && ser[0] == '1';
+  }
   Layout L = make_layout(*cfg, h->b);
   if (hipMalloc(&h->workspace, L.total) != hipSuccess) {
     (void)hipGetLastError();
@@ -485,7 +474,9 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     launch_fp8_dequant(static_cast<const uint8_t*>(w->w_down), n_proj / 16, h->b.wd_bf16, stream);
     launch_fp8_dequant(static_cast<const uint8_t*>(w->w_up), n_proj / 16, h->b.wu_bf16, stream);
   }
-  if (hipGetLastError() != hipSuccess) {
+  // the derived copies are complete before the handle is used on any stream
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
     latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
   }
@@ -527,8 +518,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const bool fp4 = c.expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
   const int shared_fmt = c.shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 ? WF_FP4 : WF_BF16;
   const int proj_fmt = c.proj_format == LATENTMOE_FORMAT_FP8_E4M3 ? WF_FP8 : WF_BF16;
-  const bool shared_a16 = shared_fmt != WF_BF16 && LMOE_LOWP_A16;  // single bf16 h_s
-  const bool expert_a16 = fp4 && LMOE_LOWP_A16;                   // single bf16 z, h
+  const bool shared_a16 = shared_fmt != WF_BF16;  // single bf16 h_s
+  const bool expert_a16 = fp4;                    // single bf16 z, h
   const long long TK = (long long)T * K;
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
@@ -540,9 +531,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // weight stream fills the latency-bound top-K / bucketing chain.
   hipStream_t side = h->side;
   hipStream_t side2 = h->side2;
-#if LMOE_SERIAL
-  side = side2 = s;  // everything in one stream, in program order (per-stage profiling)
-#endif
+  if (h->serial) side = side2 = s;  // everything in one stream, in program order (per-kernel profiling)
   auto fork_to = [&](hipStream_t to, hipEvent_t ev) {
     (void)hipEventRecord(ev, s);
     (void)hipStreamWaitEvent(to, ev, 0);
@@ -607,10 +596,6 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   };
   fork_to(side2, h->ev_fork);
   down_proj();
-#if LMOE_SHARED_FORK_AT == 0
-  fork_to(side, h->ev_fork2);
-  shared_expert();
-#endif
 
   // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
   tm.start(LATENTMOE_STAGE_ROUTER);
@@ -625,36 +610,34 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   pr.C = b.logits;
   run_dense(h, pr, T, s, false);
   tm.stop(LATENTMOE_STAGE_ROUTER);
-#if LMOE_SHARED_FORK_AT == 1
   fork_to(side, h->ev_fork2);
   shared_expert();
-#endif
 
-  // ---- 2. top-K + softmax (sums the router's split partials, adds the bias) ----
+  // ---- 2. top-K + softmax over the logits (plus the bias, when given) ----
   tm.start(LATENTMOE_STAGE_TOPK);
   int* idx_buf = topk_idx ? topk_idx : b.idx;  // written in place when the caller asks
   float* gate_buf = topk_gate ? topk_gate : b.gates;
   const double avg_rows = (double)TK / N;
   const bool expert_stream = fp4 || avg_rows <= 48.0;
-  // large-tile path: rows split by gate into a hi + lo class and a bf16 class
-  const bool split_rows = !expert_stream && LMOE_HI_TAU > 0;
+  // large-tile path: rows split by gate energy into a hi + lo class and a bf16 class
+  const bool split_rows = !expert_stream;
   uint32_t* masks_hi = split_rows ? b.masks_hi : nullptr;
-  launch_topk(b.logits, w.router_bias, T, N, K, idx_buf, gate_buf, b.masks, (float)LMOE_HI_TAU,
-              masks_hi, s);
+  launch_topk(b.logits, w.router_bias, T, N, K, idx_buf, gate_buf, b.masks, PAIR_TAIL_FRAC,
+              masks_hi, b.paired, s);
   tm.stop(LATENTMOE_STAGE_TOPK);
 
   // ---- 3. bucketing ----
   const int rows_per_tile =
       !expert_stream                   ? TILE_ROWS
-      : avg_rows <= LMOE_ROWS16_MAX_AVG ? STREAM_ROWS_SMALL
-      : avg_rows <= LMOE_ROWS32_MAX_AVG ? STREAM_ROWS_MID
+      : avg_rows <= ROWS16_MAX_AVG ? STREAM_ROWS_SMALL
+      : avg_rows <= ROWS32_MAX_AVG ? STREAM_ROWS_MID
                                         : STREAM_ROWS_BIG;
   const int max_tiles =
       ceil_div(TK, rows_per_tile) + (split_rows ? 2 : 1) * (int)std::min<long long>(N, TK);
   tm.start(LATENTMOE_STAGE_BUCKET);
   const bool fuse_place = TK <= 8192;  // one workgroup places a few thousand rows quickly
   // many mask blocks: count them in chunks on many workgroups first
-  const bool chunked = !fuse_place && bucket_chunks(T) >= LMOE_BUCKET_MIN_CHUNKS;
+  const bool chunked = !fuse_place && bucket_chunks(T) >= BUCKET_MIN_CHUNKS;
   int* chunk_hi = chunked ? b.chunk_hi : nullptr;
   int* chunk_lo = chunked ? b.chunk_lo : nullptr;
   launch_bucket_scan(b.masks, masks_hi, T, N, rows_per_tile, b.counts, b.counts_hi, b.offsets,
@@ -665,10 +648,6 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     launch_place(idx_buf, gate_buf, b.masks, masks_hi, b.offsets, b.counts_hi, b.block_prefix,
                  b.prefix_lo, T, N, K, b.row_src, b.row_gate, b.inv, chunk_hi, chunk_lo, s);
   tm.stop(LATENTMOE_STAGE_BUCKET);
-#if LMOE_SHARED_FORK_AT == 2
-  fork_to(side, h->ev_fork2);
-  shared_expert();
-#endif
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
   (void)hipStreamWaitEvent(s, h->ev_join2, 0);
@@ -699,7 +678,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       launch_gemm_big(gl, s);
     } else if (!expert_stream)
       launch_gemm_big(g, s);
-    else if (rows_per_tile == STREAM_ROWS_BIG && LMOE_MID_FP4 && gemm_mid_supports(g, fp4))
+    else if (rows_per_tile == STREAM_ROWS_BIG && gemm_mid_supports(g, fp4))
       launch_gemm_mid(g, fp4, s);
     else
       launch_gemm_stream(g, fp4 ? WF_FP4 : WF_BF16, s);
@@ -743,10 +722,10 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // fill part of the GPU); its expert down needs only its own expert up, so it runs
   // on side stream 2 beside the bf16 class's expert up, and the combine waits for
   // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
-  const bool hi_side = split_rows && LMOE_HI_DOWN_SIDE && !tm.on;
+  const bool hi_side = split_rows && !tm.on && !h->serial;
   // the bf16 class's expert-down rows go out as bf16: their rounding enters y_lat times
   // a gate below the class threshold, like that of their bf16 z and h
-  const bool og_mix = split_rows && LMOE_OG16;
+  const bool og_mix = split_rows;
   if (hi_side) {
     launch_gemm_big(pu, s);  // expert up, hi tiles
     (void)hipEventRecord(h->ev_hi, s);
@@ -776,7 +755,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);
-  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.row_gate, (float)LMOE_HI_TAU, b.zrow32, b.zrow16, b.inv,
+  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.paired, b.zrow32, b.zrow16, b.inv,
                  T, K, L, b.y_lat, b.y_lat_lo, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
@@ -785,7 +764,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_UP_PROJ);
   GemmParams pp = base_params();
   pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
-  pp.a_lo = proj_fmt != WF_BF16 && LMOE_LOWP_A16 ? nullptr : b.y_lat_lo;
+  pp.a_lo = proj_fmt != WF_BF16 ? nullptr : b.y_lat_lo;
   pp.nseg = 1;
   pp.lda = L;
   pp.ldb = L;
@@ -876,6 +855,7 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
     case LATENTMOE_INTER_Y_LAT_LO: src = h->b.y_lat_lo; have = T * c.latent * 2; break;
     case LATENTMOE_INTER_Z_LO: src = h->b.z_lo; have = T * c.latent * 2; break;
     case LATENTMOE_INTER_H_LO: src = h->b.h_lo; have = T * K * c.expert_hidden * 2; break;
+    case LATENTMOE_INTER_PAIRED: src = h->b.paired; have = T * K; break;
     default: return LATENTMOE_ERR_INVALID_ARG;
   }
   if (bytes > have) return LATENTMOE_ERR_INVALID_ARG;

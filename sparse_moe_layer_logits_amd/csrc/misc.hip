@@ -42,15 +42,15 @@ void launch_reduce(const GemmParams& p, hipStream_t s) {
 // scheduling.  The fp32 sum leaves as a bf16 pair (hi, lo = sum - hi) so the
 // up-projection sees it to about 16 significant bits.
 //
-// MIX (large-tile path with two row classes): a row whose gate is below tau (the
-// bf16 class) was written to og16 as bf16, the others to og as fp32.  Every k
+// MIX (large-tile path with two row classes): a row of the bf16 class (paired = 0)
+// was written to og16 as bf16, the others to og as fp32.  Every k
 // loads one fp32 and one bf16 row, one of them the zero row z32 / z16, and adds
 // both: the sum and its order are those of a single format, and a bf16-class row
 // costs half the bytes from memory (the zero rows stay cached).
 template <bool MIX>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ og,
                                                      const uint16_t* __restrict__ og16,
-                                                     const float* __restrict__ row_gate, float tau,
+                                                     const uint8_t* __restrict__ paired,
                                                      const float* __restrict__ z32,
                                                      const uint16_t* __restrict__ z16,
                                                      const int* __restrict__ inv, int K, int L,
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   if (threadIdx.x < K) {
     const int q = inv[(long long)t * K + threadIdx.x];
     pos[threadIdx.x] = q;
-    wide[threadIdx.x] = !MIX || row_gate[q] >= tau;  // the class top-K assigned (same fp32 test)
+    wide[threadIdx.x] = !MIX || paired[(long long)t * K + threadIdx.x];  // the class top-K assigned
   }
   __syncthreads();
   const int c = (blockIdx.y * 64 + threadIdx.x) * 4;
@@ -106,15 +106,15 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   store_bf16x4(y_lat_lo, (long long)t * L + c, lo[0], lo[1], lo[2], lo[3]);
 }
 
-void launch_combine(const float* og, const uint16_t* og16, const float* row_gate, float tau,
+void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
                     const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
                     uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s) {
   if (T <= 0) return;
   dim3 grid(T, (L / 4 + 63) / 64);
   if (og16)
-    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, row_gate, tau, z32, z16, inv, K, L, y_lat, y_lat_lo);
+    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, paired, z32, z16, inv, K, L, y_lat, y_lat_lo);
   else
-    combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, 0.f, nullptr, nullptr, inv, K, L, y_lat,
+    combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, nullptr, nullptr, inv, K, L, y_lat,
                                               y_lat_lo);
 }
 

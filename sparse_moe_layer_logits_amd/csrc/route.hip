@@ -80,11 +80,13 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __re
                                                     const float* __restrict__ bias, int T, int N,
                                                     int K, int* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
-                                                    uint32_t* __restrict__ masks, float hi_tau,
-                                                    uint32_t* __restrict__ masks_hi) {
+                                                    uint32_t* __restrict__ masks, float tail_frac,
+                                                    uint32_t* __restrict__ masks_hi,
+                                                    uint8_t* __restrict__ paired_out) {
   __shared__ uint32_t smask[1024];
   __shared__ uint32_t smask_hi[1024];
   __shared__ unsigned long long cand[TOPK_WAVES][64];
+  __shared__ float esq[TOPK_WAVES][64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int t = blockIdx.x * TOPK_WAVES + w;  // workgroups past T only write zero bytes
@@ -142,13 +144,36 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __re
     const float vmax = from_orderable((uint32_t)(top >> 32));
     const float ex = lane < K ? expf(v - vmax) : 0.0f;
     const float tot = wave_sum(ex);
+    const float gate = lane < K ? ex / tot : 0.0f;
+    // Rows that carry a bf16 hi + lo pair on the large-tile path: the largest gates
+    // of the token, until the rows left out hold at most tail_frac of its gate
+    // energy sum_k g_k^2 (a row's bf16 rounding reaches the latent sum scaled by
+    // its gate).  Row i is left out iff the energy of the rows ranked at or after
+    // it is at most tail_frac times the total; both sums run over the candidates
+    // in index order, so every lane sees the same total.
+    bool paired = true;
+    if (masks_hi) {
+      esq[w][lane] = gate * gate;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float total = 0.0f, tail = 0.0f;
+      for (int c = 0; c < K; ++c) {
+        const float ec = esq[w][c];
+        total += ec;
+        tail += cand[w][c] <= mine ? ec : 0.0f;
+      }
+      paired = tail > tail_frac * total;
+    }
     if (lane < K) {
       const int e = (int)(~(uint32_t)mine);
       idx_out[(long long)t * K + rank] = e;
-      const float gate = ex / tot;
       gate_out[(long long)t * K + rank] = gate;
       atomicOr(&smask[e], 1u << w);
-      if (gate >= hi_tau) atomicOr(&smask_hi[e], 1u << w);
+      if (masks_hi) {
+        if (paired) atomicOr(&smask_hi[e], 1u << w);
+        paired_out[(long long)t * K + rank] = paired ? 1 : 0;
+      }
     }
   }
   __syncthreads();
@@ -164,15 +189,16 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __re
 }
 
 void launch_topk(const float* logits, const float* bias, int T, int N, int K, int* idx,
-                 float* gates, uint32_t* masks, float hi_tau, uint32_t* masks_hi, hipStream_t s) {
+                 float* gates, uint32_t* masks, float tail_frac, uint32_t* masks_hi, uint8_t* paired,
+                 hipStream_t s) {
   // whole mask groups: every byte of every group's words is written
   const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK * (TOPK_TOKENS_PER_BLOCK / TOPK_WAVES);
   if (N <= 512)
-    topk_kernel<8><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, hi_tau,
-                                                      masks_hi);
+    topk_kernel<8><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, tail_frac,
+                                                      masks_hi, paired);
   else
-    topk_kernel<16><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, hi_tau,
-                                                       masks_hi);
+    topk_kernel<16><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, tail_frac,
+                                                       masks_hi, paired);
 }
 
 // ---------------------------------------------------------------------------

@@ -90,6 +90,20 @@ def test_status_strings_and_host_side_validation(lib):
     assert lib.latentmoe_destroy(None) == 0
 
 
+def test_32bit_activation_offsets_bound():
+    """Configs whose activation matrices reach 2^31 elements are rejected (the
+    large-tile kernels address rows with 32-bit offsets): at the Super shapes
+    h = [T K, m] is the widest, 36314 tokens are accepted and 36315 are not."""
+    ok = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 36314, 0)
+    assert binding.latentmoe_workspace_bytes(ok) > 0
+    for cfg in (binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 36315, 0),
+                binding.latentmoe_config(8192, 2048, 512, 22, 5120, 10240, 19066, 0),
+                binding.latentmoe_config(1 << 16, 64, 16, 1, 64, 64, 1 << 15, 0)):
+        with pytest.raises(binding.LatentMoEError) as e:
+            binding.latentmoe_workspace_bytes(cfg)
+        assert e.value.status == binding.LATENTMOE_ERR_UNSUPPORTED
+
+
 def test_workspace_grows_with_max_tokens():
     a = binding.latentmoe_workspace_bytes(binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 64, 0))
     b = binding.latentmoe_workspace_bytes(binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 8192, 0))

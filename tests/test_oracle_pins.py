@@ -336,3 +336,68 @@ def test_released_mix_stays_near_the_bf16_masters():
         np.testing.assert_array_equal(a["idx"], b["idx"])
         rel = np.sqrt(np.mean((a["y"] - b["y"]) ** 2)) / rms
         assert lo < rel < hi, (kw, rel)
+
+
+# ---------------------------------------------------------------------------
+# FP4 experts: exact wiring of codes, block scales and per-expert tensor scales
+# ---------------------------------------------------------------------------
+
+# OCP Microscaling v1.0 E2M1 values by code (sign in bit 3), and a few E4M3FN
+# block-scale codes with their values (bias 7: 0x38 = 2^0, 0x3C = 1.5 * 2^0 ...),
+# written out here so that the expected weights do not come from the oracle's
+# decoder
+E2M1_BY_CODE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+E4M3_SOME = {0x28: 0.25, 0x30: 0.5, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x44: 3.0}
+
+
+def _fp4_on_grid(rng, rows, cols, tscale):
+    """Random codes and block scales (one per 16 consecutive input elements)
+    -> packed bytes [rows, cols/2] (element 2j in the low nibble of byte j),
+    scale bytes [rows, cols/16] and the float64 values code * scale * tscale."""
+    codes = rng.integers(0, 16, size=(rows, cols)).astype(np.uint8)
+    sc_codes = np.array(list(E4M3_SOME), np.uint8)[rng.integers(0, len(E4M3_SOME), size=(rows, cols // 16))]
+    vals = np.empty((rows, cols))
+    for r in range(rows):
+        for c in range(cols):
+            vals[r, c] = E2M1_BY_CODE[codes[r, c]] * E4M3_SOME[int(sc_codes[r, c // 16])] * tscale
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc_codes, vals
+
+
+def test_fp4_experts_match_bf16_storage_of_the_same_values():
+    """FP4-stored experts (m != l, each expert's W1 and W2 with its own power-of-two
+    tensor scale) give exactly the result of bf16 storage of the values the codes
+    encode: the oracle applies expert e's codes, block scales (along the input
+    dimension) and tensor scales to W1_e and W2_e and nothing else.  A swapped
+    W1/W2 tensor scale, another expert's scale or codes, or block scales taken
+    along the output dimension change the result."""
+    N, K, d, l, m, ms, T = 4, 2, 32, 32, 48, 32, 6
+    wl = synth.Workload("t", T=T, d=d, latent=l, n_experts=N, top_k=K, expert_hidden=m,
+                        shared_hidden=ms)
+    x, Wb = synth.make(wl, 5, threads=2)
+    rng = np.random.default_rng(1234)
+    W4 = dict(Wb)
+    w1p, w1s, w2p, w2s, w1v, w2v = [], [], [], [], [], []
+    t1 = np.array([2.0 ** -(4 + e) for e in range(N)], np.float32)       # W1_e
+    t2 = np.array([2.0 ** -(2 + 2 * e) for e in range(N)], np.float32)   # W2_e
+    for e in range(N):
+        p, s, v = _fp4_on_grid(rng, m, l, float(t1[e]))
+        w1p.append(p); w1s.append(s); w1v.append(v)
+        p, s, v = _fp4_on_grid(rng, l, m, float(t2[e]))
+        w2p.append(p); w2s.append(s); w2v.append(v)
+    W4.update(expert_w1=np.stack(w1p), expert_w1_scale=np.stack(w1s), expert_w1_tscale=t1,
+              expert_w2=np.stack(w2p), expert_w2_scale=np.stack(w2s), expert_w2_tscale=t2)
+    assert W4["expert_w1"].shape == (N, m, l // 2) and W4["expert_w2_scale"].shape == (N, l, m // 16)
+    # every value is a bf16 number (E2M1 x E4M3 x 2^-k), so bf16 storage holds it exactly
+    Wb = dict(Wb, expert_w1=bits(np.stack(w1v)), expert_w2=bits(np.stack(w2v)))
+    assert np.array_equal(oracle.bf16_to_f64(Wb["expert_w1"]), np.stack(w1v))
+    a = oracle.forward(x, W4, K, intermediates=True)
+    b = oracle.forward(x, Wb, K, intermediates=True)
+    assert set(a["idx"].ravel().tolist()) == set(range(N))   # every expert's scales matter
+    np.testing.assert_array_equal(a["y_lat"], b["y_lat"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+    assert np.abs(a["y_lat"]).max() > 0
+    # the same bytes with the two tensor scales swapped give another y_lat
+    Ws = dict(W4, expert_w1_tscale=t2, expert_w2_tscale=t1)
+    assert not np.allclose(oracle.forward(x, Ws, K, intermediates=True)["y_lat"], a["y_lat"])
