@@ -46,6 +46,7 @@ extern "C" {
 #define LATENTMOE_ERR_UNSUPPORTED (-2)  /* shape outside what the kernels handle      */
 #define LATENTMOE_ERR_OUT_OF_MEMORY (-3) /* workspace allocation failed               */
 #define LATENTMOE_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
+#define LATENTMOE_ERR_SCRATCH (-5)      /* workspace larger than the static scratch array */
 
 /* ---- weight storage formats ----
  * BF16: raw bf16 patterns.
@@ -155,6 +156,33 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
  * to graph replays. */
 int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y,
                             int32_t* topk_idx, float* topk_gate, hipStream_t stream);
+
+/* Entry point that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same layer and results as latentmoe_init + latentmoe_forward
+ * (the same kernels, all of them on `stream` in program order) without a handle:
+ * the workspace for T tokens is laid out in a file-scope device array of
+ * LATENTMOE_STATIC_SCRATCH_BYTES bytes (64 MiB, enough for T = 64 at the Super
+ * decode shapes), which each GPU the library runs on holds until the process
+ * ends.  Each call derives the router's split weights into that array, clears
+ * what must start at zero (with kernels, no memset nodes) and enqueues the
+ * forward; it calls no hipMalloc, hipFree or other allocating routine.  The
+ * first call on a device looks up that device's address of the array
+ * (hipGetSymbolAddress, not a stream operation) and sets kernel attributes.
+ *   cfg, w     host pointers, read during the call; every format must be
+ *              FORMAT_BF16 (the FP4 / FP8 paths need derived copies larger
+ *              than the array); cfg->max_tokens bounds T
+ *   x, T, y, topk_idx, topk_gate, stream: as latentmoe_forward
+ * All calls on one GPU share its array and the array keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, two threads) race and
+ * must not be made.  Errors (before anything is enqueued): INVALID_ARG (null
+ * pointers, T < 0, T > cfg->max_tokens), UNSUPPORTED (shape checks of
+ * latentmoe_init, a format other than bf16), SCRATCH (the workspace for T
+ * tokens exceeds LATENTMOE_STATIC_SCRATCH_BYTES), HIP. */
+#define LATENTMOE_STATIC_SCRATCH_BYTES (64u << 20)
+int latentmoe_forward_static(const latentmoe_config* cfg, const latentmoe_weights* w,
+                             const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
+                             float* topk_gate, hipStream_t stream);
 
 /* Free the handle and its workspace.  Work still queued on a stream that uses
  * the handle must have completed.  NULL is accepted (returns OK). */

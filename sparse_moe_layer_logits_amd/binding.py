@@ -20,6 +20,8 @@ LATENTMOE_ERR_INVALID_ARG = -1
 LATENTMOE_ERR_UNSUPPORTED = -2
 LATENTMOE_ERR_OUT_OF_MEMORY = -3
 LATENTMOE_ERR_HIP = -4
+LATENTMOE_ERR_SCRATCH = -5
+LATENTMOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 LATENTMOE_FORMAT_BF16 = 0
 LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 = 1
@@ -36,7 +38,7 @@ EXPORTED = [
     "latentmoe_init", "latentmoe_forward", "latentmoe_forward_graph", "latentmoe_destroy",
     "latentmoe_status_string",
     "latentmoe_workspace_bytes", "latentmoe_debug_copy", "latentmoe_profile_begin",
-    "latentmoe_profile_end", "latentmoe_fp4_decode", "latentmoe_fp8_decode",
+    "latentmoe_profile_end", "latentmoe_fp4_decode", "latentmoe_fp8_decode", "latentmoe_forward_static",
 ]
 # include/ssm_replay.h: Mamba-2 checkpoint + replay verification
 SSM_EXPORTED = ["ssm_check_shape", "ssm_replay_verify", "ssm_replay_commit", "ssm_replay_flush",
@@ -98,6 +100,8 @@ def load(path: str = LIB_PATH):
                                           ctypes.POINTER(ctypes.c_int)]
     lib.latentmoe_fp4_decode.argtypes = [vp, vp, ctypes.c_int64, vp, vp]
     lib.latentmoe_fp8_decode.argtypes = [vp, ctypes.c_int64, vp, vp]
+    lib.latentmoe_forward_static.argtypes = [ctypes.POINTER(latentmoe_config), ctypes.POINTER(latentmoe_weights),
+                                             vp, i32, vp, vp, vp, vp]
     sp = ctypes.POINTER(ssm_shape)
     lib.ssm_check_shape.argtypes = [sp]
     lib.ssm_replay_verify.argtypes = [sp, i32, i32] + [vp] * 11  # 10 pointers + stream
@@ -146,6 +150,13 @@ def latentmoe_forward_graph(h: int, x_ptr: int, T: int, y_ptr: int, idx_ptr: int
                             stream: int) -> None:
     _check("latentmoe_forward_graph", load().latentmoe_forward_graph(
         ctypes.c_void_p(h), ctypes.c_void_p(x_ptr), int(T), ctypes.c_void_p(y_ptr),
+        ctypes.c_void_p(idx_ptr or None), ctypes.c_void_p(gate_ptr or None), ctypes.c_void_p(stream)))
+
+
+def latentmoe_forward_static(cfg: latentmoe_config, w: latentmoe_weights, x_ptr: int, T: int, y_ptr: int,
+                             idx_ptr: int, gate_ptr: int, stream: int) -> None:
+    _check("latentmoe_forward_static", load().latentmoe_forward_static(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(x_ptr), int(T), ctypes.c_void_p(y_ptr),
         ctypes.c_void_p(idx_ptr or None), ctypes.c_void_p(gate_ptr or None), ctypes.c_void_p(stream)))
 
 

@@ -129,6 +129,8 @@ void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired
 // decoder (tensor scale not applied): decode check and the bf16 expansion at init
 void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n_blocks16,
                         uint16_t* out, hipStream_t s);
+// zero `bytes` bytes (a multiple of 4) at device address p with a kernel
+void launch_zero(void* p, size_t bytes, hipStream_t s);
 // groups of 16 E4M3 bytes -> exact bf16 with the in-register decoder (tensor scale not applied)
 void launch_fp8_dequant(const uint8_t* codes, long long n_groups16, uint16_t* out, hipStream_t s);
 

@@ -21,6 +21,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -376,6 +377,7 @@ const char* latentmoe_status_string(int status) {
     case LATENTMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
     case LATENTMOE_ERR_OUT_OF_MEMORY: return "out of device memory";
     case LATENTMOE_ERR_HIP: return "HIP runtime error";
+    case LATENTMOE_ERR_SCRATCH: return "workspace exceeds the static scratch array";
     default: return "unknown status";
   }
 }
@@ -532,9 +534,16 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   hipStream_t side = h->side;
   hipStream_t side2 = h->side2;
   if (h->serial) side = side2 = s;  // everything in one stream, in program order (per-kernel profiling)
+  // event edges between the streams (none in serial mode: one stream)
+  auto record = [&](hipEvent_t ev, hipStream_t on) {
+    if (!h->serial) (void)hipEventRecord(ev, on);
+  };
+  auto wait = [&](hipStream_t on, hipEvent_t ev) {
+    if (!h->serial) (void)hipStreamWaitEvent(on, ev, 0);
+  };
   auto fork_to = [&](hipStream_t to, hipEvent_t ev) {
-    (void)hipEventRecord(ev, s);
-    (void)hipStreamWaitEvent(to, ev, 0);
+    record(ev, s);
+    wait(to, ev);
   };
   auto shared_expert = [&]() {
     // ---- shared expert (side stream): h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
@@ -574,7 +583,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     run_dense(h, p2, T, side, false, b.partial2, shared_fmt, b.s2_bf16);
     tm.stop(LATENTMOE_STAGE_SHARED_DOWN, side);
 
-    (void)hipEventRecord(h->ev_join, side);
+    record(h->ev_join, side);
   };
   auto down_proj = [&]() {
     // ---- z = W_down x (side stream 2, concurrent with routing) ----
@@ -592,7 +601,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     pd.ldc = L;
     run_dense(h, pd, T, side2, false, b.partial3, proj_fmt, b.wd_bf16);
     tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
-    (void)hipEventRecord(h->ev_join2, side2);
+    record(h->ev_join2, side2);
   };
   fork_to(side2, h->ev_fork);
   down_proj();
@@ -650,7 +659,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_BUCKET);
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
-  (void)hipStreamWaitEvent(s, h->ev_join2, 0);
+  wait(s, h->ev_join2);
 
   // ---- 5/6. grouped expert GEMMs ----
   GemmParams pe = base_params();
@@ -760,7 +769,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
   // ---- 8. y += W_up y_lat (after the shared expert wrote y) ----
-  (void)hipStreamWaitEvent(s, h->ev_join, 0);
+  wait(s, h->ev_join);
   tm.start(LATENTMOE_STAGE_UP_PROJ);
   GemmParams pp = base_params();
   pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
@@ -914,3 +923,77 @@ int latentmoe_fp8_decode(const uint8_t* codes, int64_t n_groups, uint16_t* out, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// latentmoe_forward_static: the forward without a handle, its workspace in a
+// file-scope device array.  In host code `scratch` names a host-side stand-in,
+// not device memory: the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[LATENTMOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int STATIC_MAX_DEVICES = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[STATIC_MAX_DEVICES];  // device address of `scratch` per device
+
+// the array's address on the current device (looked up on the first call there,
+// with the large-tile kernel's attributes set at the same time)
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LATENTMOE_ERR_HIP;
+  if (dev < 0 || dev >= STATIC_MAX_DEVICES) return LATENTMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p || gemm_big_setup() != 0) {
+      (void)hipGetLastError();
+      return LATENTMOE_ERR_HIP;
+    }
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return LATENTMOE_OK;
+}
+
+}  // namespace
+
+extern "C" int latentmoe_forward_static(const latentmoe_config* cfg, const latentmoe_weights* w,
+                                        const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
+                                        float* topk_gate, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != LATENTMOE_OK) return st;
+  if (cfg->expert_format != LATENTMOE_FORMAT_BF16 || cfg->shared_format != LATENTMOE_FORMAT_BF16 ||
+      cfg->proj_format != LATENTMOE_FORMAT_BF16)
+    return LATENTMOE_ERR_UNSUPPORTED;
+  if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
+      !w->shared_w1 || !w->shared_w2 || T < 0)
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (T == 0) return LATENTMOE_OK;
+  if (!x || !y || T > cfg->max_tokens) return LATENTMOE_ERR_INVALID_ARG;
+  // the workspace laid out for this call's T
+  latentmoe_handle_s h;
+  h.cfg = *cfg;
+  h.cfg.max_tokens = T;
+  h.w = *w;
+  h.serial = true;  // one stream, no events
+  const Layout L = make_layout(h.cfg, h.b);
+  if (L.total > (size_t)LATENTMOE_STATIC_SCRATCH_BYTES) return LATENTMOE_ERR_SCRATCH;
+  void* base = nullptr;
+  st = static_scratch(&base);
+  if (st != LATENTMOE_OK) return st;
+  char* at = static_cast<char*>(base);
+  for (const auto& it : L.items) {
+    *it.first = at;
+    at += (it.second + 255) & ~size_t(255);
+  }
+  (void)hipGetLastError();
+  // what the handle path derives once at init, here on every call: the router's
+  // split weights and the combine's zero rows
+  launch_router_split(w->router_w, h.b.pieces, (long long)cfg->n_experts * cfg->d, stream);
+  launch_zero(h.b.zrow32, (size_t)cfg->latent * 4, stream);
+  launch_zero(h.b.zrow16, (size_t)cfg->latent * 2, stream);
+  forward_impl(&h, x, T, y, topk_idx, topk_gate, stream, false);
+  return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
+}

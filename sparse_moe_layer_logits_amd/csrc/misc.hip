@@ -118,6 +118,19 @@ void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired
                                               y_lat_lo);
 }
 
+// zero n 32-bit words (a kernel rather than a memset node, so that a captured
+// graph replays it as an ordinary kernel)
+__global__ void zero_kernel(uint32_t* __restrict__ p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+void launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const long long n = (long long)(bytes / 4);
+  if (n <= 0) return;
+  zero_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<uint32_t*>(p), n);
+}
+
 // decode n_blocks16 FP4 blocks (8 code bytes + 1 scale byte each) to bf16
 __global__ void fp4_dequant_kernel(const uint8_t* __restrict__ codes,
                                    const uint8_t* __restrict__ scales, long long nb,

@@ -1,0 +1,89 @@
+"""latentmoe_forward_static, the entry point that allocates nothing: its workspace
+lives in the library's static device array.  Checked against latentmoe_forward on
+the same inputs (same kernels: the outputs are equal bit for bit) and against the
+oracle, on two calls in a row, the second with a smaller T."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_moe_layer_logits_amd import binding, synth
+
+from gpu_common import log
+from test_gpu_parity import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(wl, seed, name=None):
+    if name is not None:
+        return synth.make(wl, seed, redraws=synth.load_redraws(name, seed))
+    return gen(wl, seed)
+
+
+def _static(layer, xd, T):
+    import torch
+    wl = layer.dims
+    y = torch.full((T, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((T, wl.top_k), -1, dtype=torch.int32, device="cuda")
+    g = torch.full((T, wl.top_k), float("nan"), dtype=torch.float32, device="cuda")
+    binding.latentmoe_forward_static(layer.cfg, layer.w, xd.data_ptr(), T, y.data_ptr(), idx.data_ptr(),
+                                     g.data_ptr(), layer.stream.cuda_stream)
+    return y, idx, g
+
+
+@pytest.mark.parametrize("name,Ts", [
+    ("super_decode", (64, 23)),                 # Super decode shapes: 60 MiB of the 64 MiB array
+    ("tiny", (8, 3)),
+    ("large_tiles", (1100, 700)),               # > 48 rows per expert: large tiles, two row classes
+])
+def test_static_entry_matches_forward(name, Ts):
+    import torch
+    if name == "large_tiles":
+        wl = synth.Workload("large_tiles", T=1100, d=256, latent=64, n_experts=32, top_k=8,
+                            expert_hidden=128, shared_hidden=256)
+        x, W = _inputs(wl, 41)
+    else:
+        wl = synth.WORKLOADS[name]
+        x, W = _inputs(wl, 0, name)
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    ref = oracle.forward(x, W, wl.top_k)
+    for T in Ts:                                 # two calls in a row, the second smaller
+        ys, idxs, gs = _static(layer, xd[:T], T)
+        yf, idxf, gf = layer.forward(xd[:T])
+        torch.cuda.synchronize()
+        assert torch.equal(ys, yf) and torch.equal(idxs, idxf) and torch.equal(gs, gf), (name, T)
+        rms = np.sqrt(np.mean(ref["y"][:T] ** 2))
+        err = np.max(np.abs(ys.cpu().numpy() - ref["y"][:T]))
+        assert err <= 1e-2 * rms
+        assert [sorted(r) for r in idxs.cpu().numpy().tolist()] == [sorted(r) for r in ref["idx"][:T].tolist()]
+        log("static entry %s T=%d: equal to latentmoe_forward, max|gpu-oracle|/rms = %.2e" % (name, T, err / rms))
+    layer.close()
+
+
+def test_static_entry_rejects_before_work():
+    import torch
+    wl = synth.WORKLOADS["tiny"]
+    x, W = _inputs(wl, 0, "tiny")
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    y = torch.full((wl.T, wl.d), 5.0, device="cuda")
+    s = layer.stream.cuda_stream
+    fits = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 64, 0)   # 60.3 MiB
+    assert binding.latentmoe_workspace_bytes(fits) <= binding.LATENTMOE_STATIC_SCRATCH_BYTES
+    too_big = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 65, 0)  # 70.6 MiB
+    assert binding.latentmoe_workspace_bytes(too_big) > binding.LATENTMOE_STATIC_SCRATCH_BYTES
+    cases = [(too_big, 65, binding.LATENTMOE_ERR_SCRATCH),
+             (layer.cfg, wl.T + 1, binding.LATENTMOE_ERR_INVALID_ARG)]
+    fp4 = binding.latentmoe_config(*[getattr(layer.cfg, f) for f, _ in binding.latentmoe_config._fields_])
+    fp4.expert_format = binding.LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16
+    cases.append((fp4, wl.T, binding.LATENTMOE_ERR_UNSUPPORTED))
+    for cfg, T, status in cases:
+        with pytest.raises(binding.LatentMoEError) as e:
+            binding.latentmoe_forward_static(cfg, layer.w, xd.data_ptr(), T, y.data_ptr(), 0, 0, s)
+        assert e.value.status == status
+    torch.cuda.synchronize()
+    assert float(y.min()) == 5.0 and float(y.max()) == 5.0     # nothing was enqueued
+    layer.close()
