@@ -8,7 +8,10 @@ expert GEMMs, combine, shared expert, W_up) over one batch of seeded synthetic
 tokens already resident in HBM.  Prints one JSON line with the throughput, the
 roofline of the dominant kernel (timed with HIP events on the forward's stream
 during the timed steps) and the fp64 oracle timed on the host cores over a
-bounded sample of the same workload.
+bounded sample of the same workload.  The headline is the Super decode step;
+with the default workload the line also carries a "workloads" object with the
+same measurements for the Super prefill chunk (MFMA-bound), the Ultra shape
+and FP4 experts.
 """
 import argparse
 import hashlib
@@ -75,40 +78,76 @@ def expert_kernel_units(wl, touched, stage):
 
 
 def expert_kernel(wl):
-    """The kernel the library runs the grouped expert GEMMs with (the same
-    choice as the host code: rows per expert and weight format)."""
+    """The kernel the library runs the grouped expert GEMMs with: the host's choice
+    by weight format and average routed rows per expert (T K / N): bf16 experts
+    above 48 rows take the large-tile kernel; otherwise streaming tiles of 16 rows
+    (up to 12 rows), 32 (up to 24) or 64, and FP4 experts with 64-row tiles the
+    LDS-staged FP4 kernel."""
     avg_rows = wl.T * wl.top_k / wl.n_experts
-    if wl.experts == "fp4":
-        mid_ok = avg_rows > 8 and wl.latent % 128 == 0 and wl.expert_hidden % 128 == 0
-        return "gemm_mid_kernel" if mid_ok else "gemm_stream_kernel"
-    return "gemm_stream_kernel" if avg_rows <= 48 else "gemm_big_kernel"
+    if wl.experts == "bf16" and avg_rows > 48:
+        return "gemm_big_kernel"
+    if wl.experts == "fp4" and avg_rows > 24 and wl.latent % 128 == 0 and wl.expert_hidden % 128 == 0:
+        return "gemm_mid_kernel"
+    return "gemm_stream_kernel"
 
 
-def cpu_baseline(wl, x, W, budget_s=15.0):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, x, W, budget_s=15.0, threads=None):
     """The fp64 oracle on the host cores over a bounded sample of tokens: the
     first n tokens of the batch (n sized for about budget_s of work, at most
-    the whole batch), repeated until at least budget_s / 1.5 has passed."""
+    the whole batch), repeated until at least budget_s / 1.5 has passed.
+    threads: cap numpy's BLAS threads (None: all host cores)."""
+    import contextlib
+
     import oracle
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:
-        cores = os.cpu_count() or 1
-    n = 2
-    t0 = time.time()
-    oracle.forward(x[:n], W, wl.top_k)
-    dt = time.time() - t0
-    n = int(min(wl.T, max(n, n * budget_s / max(dt, 1e-3))))
-    passes, tokens = 0, 0
-    t0 = time.time()
-    while passes == 0 or time.time() - t0 < budget_s / 1.5:
+        threadpool_info = threadpool_limits = None
+    ctx = threadpool_limits(threads) if (threads and threadpool_limits) else contextlib.nullcontext()
+    with ctx:
+        if threadpool_info:
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        else:
+            cores = threads or os.cpu_count() or 1
+        n = 2
+        t0 = time.time()
         oracle.forward(x[:n], W, wl.top_k)
-        passes += 1
-        tokens += n
-    dt = time.time() - t0
+        dt = time.time() - t0
+        n = int(min(wl.T, max(n, n * budget_s / max(dt, 1e-3))))
+        passes, tokens = 0, 0
+        t0 = time.time()
+        while passes == 0 or time.time() - t0 < budget_s / 1.5:
+            oracle.forward(x[:n], W, wl.top_k)
+            passes += 1
+            tokens += n
+        dt = time.time() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "first %d of the %d tokens of the %s batch x %d passes, fp64 numpy, %.1f s"
                       % (n, wl.T, wl.name, passes, dt)}
+
+
+def stored_mfma(kernel, workload):
+    """MFMA counters of the expert GEMMs stored for this workload (profiles/),
+    while the kernel's sources are those the counters were taken on."""
+    path = os.path.join(PROFILES, "mfma_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != source_sha(kernel):
+        return None
+    return {k: d[k] for k in ("mfma_busy_frac", "executed_over_algorithmic", "executed_tflop_per_launch",
+                              "algorithmic_tflop_per_launch") if k in d}
 
 
 def stored_traffic(kernel, workload):
@@ -121,43 +160,29 @@ def stored_traffic(kernel, workload):
     return d
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="super_decode")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="batch size T instead of the workload's (e.g. speculative-verify sweeps)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a plain fp32 copy kernel of this size (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: there is no multi-GPU path (expert-parallel "
-              "sharding is not built); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    from sparse_moe_layer_logits_amd import synth as _synth
-    if args.workload in _synth.SSM_WORKLOADS:
-        return bench_ssm(args)
+EXTRA_WORKLOADS = ("super_prefill", "ultra", "super_fp4")   # reported beside the headline
 
+
+def measure(name, args, steps, warmup, tokens=0, cpu_budget=15.0, cpu_1thread=False):
+    """One workload: graph-replayed timed steps (per-step HIP events for the
+    spread), eager steps with stage events for the roofline, and the oracle on
+    the host.  Returns the JSON fields of that workload."""
     import torch
 
     from sparse_moe_layer_logits_amd import binding, synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[name]
     redraw_from = wl.name
-    if args.tokens:
+    if tokens:
         # the same layer at another batch size: token rows are drawn per row, so
         # a smaller T is a prefix of the batch; super_verify's redraw table
         # covers the decode router up to 512 rows
         import dataclasses
-        if args.tokens > wl.T and wl.name == "super_decode":
+        if tokens > wl.T and wl.name == "super_decode":
             redraw_from = "super_verify"
-        elif args.tokens > wl.T:
+        elif tokens > wl.T:
             raise SystemExit("--tokens above %d needs a workload whose batch has that many rows" % wl.T)
-        wl = dataclasses.replace(wl, T=args.tokens)
+        wl = dataclasses.replace(wl, T=tokens)
     t0 = time.time()
     redraws = {t: a for t, a in synth.load_redraws(redraw_from, args.seed).items() if t < wl.T}
     x, W = synth.make(wl, args.seed, redraws=redraws)
@@ -171,37 +196,43 @@ def main():
     idx = torch.empty((wl.T, wl.top_k), dtype=torch.int32, device="cuda")
     gates = torch.empty((wl.T, wl.top_k), dtype=torch.float32, device="cuda")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.forward(xd, y, idx, gates)
     torch.cuda.synchronize()
     counts = layer.intermediate("counts", (wl.n_experts,), torch.int32).cpu().numpy()
     touched = int((counts > 0).sum())
-    log("warmup done; %d experts touched" % touched)
+    log("%s: warmup done; %d experts touched" % (wl.name, touched))
 
-    # timed region 1: the step as a serving loop runs it (graph replay of the forward)
+    # timed region 1: the step as a serving loop runs it (graph replay of the
+    # forward), with an event on the stream between steps for the per-step spread
     for _ in range(3):
         layer.forward(xd, y, idx, gates, graph=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(steps):
         layer.forward(xd, y, idx, gates, graph=True)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    tokens_per_s = wl.T * args.steps / elapsed
-    log("timed %d graph-replayed steps: %.4f ms/step" % (args.steps, ms_per_step))
+    per_step = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    ms_per_step = 1e3 * elapsed / steps
+    tokens_per_s = wl.T * steps / elapsed
+    log("%s: timed %d graph-replayed steps: %.4f ms/step (p10 %.4f, median %.4f, p90 %.4f)"
+        % (wl.name, steps, ms_per_step, *np.percentile(per_step, [10, 50, 90])))
 
     # timed region 2: the same steps launched eagerly, with HIP events on the
     # forward's streams around each stage (per-kernel durations for the roofline)
-    layer.profile_begin(args.steps)
+    layer.profile_begin(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         layer.forward(xd, y, idx, gates)
     torch.cuda.synchronize()
-    eager_ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    eager_ms = 1e3 * (time.perf_counter() - t0) / steps
     stage_ms, calls = layer.profile_end()
-    log("timed %d eager steps with stage events: %.4f ms/step" % (args.steps, eager_ms))
+    log("%s: timed %d eager steps with stage events: %.4f ms/step" % (wl.name, steps, eager_ms))
     for k, v in stage_ms.items():
         log("  stage %-12s %.4f ms" % (k, v / max(calls, 1)))
 
@@ -217,18 +248,21 @@ def main():
     else:
         achieved, peak, unit, bound = kf / dom_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     # counter data is stored for the workloads' own batch sizes only
-    tr = None if args.tokens else stored_traffic(kernel, wl.name)
+    tr = None if tokens else stored_traffic(kernel, wl.name)
     traffic = None if tr is None else tr["hbm_bytes_per_launch"]
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "%s (%s)" % (kernel, dom), "launch_ms": round(dom_s * 1e3, 5),
                 "source_sha": source_sha(kernel),
                 "alg_bytes_per_launch": int(kb), "alg_flops_per_launch": kf}
-    result = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded normal weights and tokens, N(0, 1/fan_in))",
+    mf = None if tokens else stored_mfma(kernel, wl.name)
+    if mf is not None:
+        roofline["mfma_counters"] = mf
+    res = {
+        "value": round(tokens_per_s, 1), "ms_per_step": round(ms_per_step, 5),
+        "step_ms_p10": round(float(np.percentile(per_step, 10)), 5),
+        "step_ms_median": round(float(np.median(per_step)), 5),
+        "step_ms_p90": round(float(np.percentile(per_step, 90)), 5),
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "latent": wl.latent,
                    "n_experts": wl.n_experts, "top_k": wl.top_k, "expert_hidden": wl.expert_hidden,
                    "shared_hidden": wl.shared_hidden, "experts": wl.experts, "shared": wl.shared,
@@ -236,19 +270,71 @@ def main():
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": roofline,
         "layer": {"alg_bytes": int(alg_bytes), "alg_flops": alg_flops, "experts_touched": touched,
+                  "bound": "hbm" if hbm_bound else "mfma",
                   "eager_ms_per_step_with_events": round(eager_ms, 5),
                   "hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(alg_flops / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "stage_ms": {k: round(v / max(calls, 1), 5) for k, v in stage_ms.items()}},
     }
     layer.close()
-    del Wd, xd
+    del Wd, xd, y, idx, gates
     torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        log("%s: timing the fp64 oracle on the host" % wl.name)
+        res["cpu_baseline"] = cpu_baseline(wl, x, W, budget_s=cpu_budget)
+        if cpu_1thread:
+            res["cpu_baseline_1thread"] = cpu_baseline(wl, x, W, budget_s=cpu_budget / 2, threads=1)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="super_decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch size T instead of the workload's (e.g. speculative-verify sweeps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure the headline workload only (no prefill / Ultra / FP4 entries)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain fp32 copy kernel of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: there is no multi-GPU path (expert-parallel "
+              "sharding is not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from sparse_moe_layer_logits_amd import synth as _synth
+    if args.workload in _synth.SSM_WORKLOADS:
+        return bench_ssm(args)
+
+    cpu = 0.0 if args.no_cpu_baseline else 15.0
+    # the headline: the decode step (one 1-thread oracle run beside it, as for tiny and Ultra)
+    head = measure(args.workload, args, args.steps, args.warmup, tokens=args.tokens, cpu_budget=cpu,
+                   cpu_1thread=bool(cpu) and args.workload in ("tiny", "super_decode", "ultra"))
+    result = {
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal weights and tokens, N(0, 1/fan_in))",
+    }
+    result.update({k: v for k, v in head.items() if k not in ("value", "ms_per_step")})
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
-    if not args.no_cpu_baseline:
-        log("timing the fp64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(wl, x, W)
+    if not args.no_workloads and not args.tokens and args.workload == "super_decode":
+        # the other configurations the metric names, each with its own roofline: the
+        # prefill chunk (MFMA-bound), the Ultra shape and FP4 experts (HBM-bound)
+        result["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            result["workloads"][name] = measure(name, args, args.steps, args.warmup,
+                                                cpu_budget=cpu / 2, cpu_1thread=bool(cpu) and name == "ultra")
+        if cpu:
+            from sparse_moe_layer_logits_amd import synth
+            wl = synth.WORKLOADS["tiny"]
+            x, W = synth.make(wl, args.seed, redraws=synth.load_redraws("tiny", args.seed))
+            result["cpu_baseline_tiny_1thread"] = cpu_baseline(wl, x, W, budget_s=4.0, threads=1)
     print(json.dumps(result), flush=True)
 
 

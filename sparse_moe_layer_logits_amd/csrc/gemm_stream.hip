@@ -445,8 +445,10 @@ static void launch_fmt(const GemmParams& p, int rows, long long tiles, hipStream
     // FP8 weights are the dense projections only: 64-row tiles
     launch_rows<64, DUAL ? 2 : 4, FMT, DUAL>(p, tiles, s);
   } else {
-    // 16-row tiles take 4 pairs (256 k) per chunk; 32- and 64-row tiles 2 with a
-    // hi + lo activation, 4 with one part
+    // 16-row tiles take 4 pairs (256 k) per chunk; 32-row tiles 2 with a hi + lo
+    // activation, 4 with one part; 64-row bf16 tiles 2 (with 4, one-part tiles took
+    // 146 VGPRs: one 8-wave block per CU, whose load latency the dense decode GEMMs
+    // could not hide; with 2, 90 VGPRs and two blocks per CU)
     constexpr int P16 = 4;
     constexpr int P = DUAL ? 2 : 4;
     if (rows == 16)
@@ -454,7 +456,7 @@ static void launch_fmt(const GemmParams& p, int rows, long long tiles, hipStream
     else if (rows == 32)
       launch_rows<32, P, FMT, DUAL>(p, tiles, s);
     else
-      launch_rows<64, P, FMT, DUAL>(p, tiles, s);
+      launch_rows<64, FMT == WF_BF16 ? 2 : P, FMT, DUAL>(p, tiles, s);
   }
 }
 

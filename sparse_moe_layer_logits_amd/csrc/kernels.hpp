@@ -119,12 +119,18 @@ void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const uint32_t* masks_hi, const int* offsets, const int* counts_hi,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
                   float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s);
-// y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo.  With og16,
-// rows with paired[t*K+k] == 0 are read from og16 (bf16) instead; z32 / z16 are
-// zero rows of L elements.
+// y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo (rows of stride
+// ldy).  With og16, rows with paired[t*K+k] == 0 are read from og16 (bf16) instead;
+// z32 / z16 are zero rows of L elements.
 void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
                     const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
-                    uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s);
+                    uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s);
+// split-K partials [splits][T][3N + L + MS] of the GEMM over x with the stacked rows
+// [router pieces 1-3; W_down; S1] -> fp32 logits [T, N] (the three piece columns
+// summed), z (bf16 hi + lo, [T, L]) and h_s = relu(.)^2 (bf16 hi + lo, rows of stride ldh)
+void launch_xreduce(const float* partial, int splits, long long pstride, int T, int N, int L, int MS,
+                    float* logits, uint16_t* z, uint16_t* z_lo, uint16_t* hs, uint16_t* hs_lo, int ldh,
+                    hipStream_t s);
 // FP4 blocks (8 code bytes + 1 scale byte each) -> exact bf16 with the in-register
 // decoder (tensor scale not applied): decode check and the bf16 expansion at init
 void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n_blocks16,

@@ -58,6 +58,9 @@ constexpr float PAIR_TAIL_FRAC = 1.0f / 32.0f;
 constexpr int BIG_KGRAN = 512;
 constexpr int BUCKET_MIN_CHUNKS = 4;  // chunks of 16 mask blocks (256 tokens) from which the count is split
 constexpr int TARGET_BLOCKS = 256;      // streaming kernel: 8-wave blocks, several per CU
+// the two stacked GEMMs of the decode-sized path (one block per CU at 256 blocks: the
+// blocks' load latency left HBM idle; 512 put two on each CU, -9 us per forward)
+constexpr int TARGET_BLOCKS_STACKED = 512;
 constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 8-wave block per CU
 
 struct Plan {
@@ -68,8 +71,9 @@ struct Plan {
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// split-K plan for a dense GEMM of M rows, N columns, K reduction
-Plan plan_dense(int M, int N, int K) {
+// split-K plan for a dense GEMM of M rows, N columns, K reduction (target: blocks the
+// streaming kernel aims at)
+Plan plan_dense(int M, int N, int K, int target = TARGET_BLOCKS) {
   Plan p;
   p.stream = M <= STREAM_ROWS_BIG;
   const int per_split = p.stream ? ceil_div(N, 128) * ceil_div(M, STREAM_ROWS_BIG)
@@ -77,7 +81,7 @@ Plan plan_dense(int M, int N, int K) {
   // smallest k range of a split: with four or more row tiles the large-tile GEMMs
   // have blocks enough, and halving their splits halves the partial sums' traffic
   const int gran = !p.stream && M >= 4 * TILE_ROWS ? BIG_KGRAN : 256;
-  int want = std::max(1, ceil_div(p.stream ? TARGET_BLOCKS : TARGET_BLOCKS_BIG, per_split));
+  int want = std::max(1, ceil_div(p.stream ? target : TARGET_BLOCKS_BIG, per_split));
   want = std::min(want, std::max(1, K / gran));
   int ks = ceil_div(ceil_div(K, want), gran) * gran;
   p.k_split = ks;
@@ -131,6 +135,11 @@ struct Buffers {
   uint16_t* s2_bf16 = nullptr;
   uint16_t* wd_bf16 = nullptr;
   uint16_t* wu_bf16 = nullptr;
+  // decode-sized forwards with bf16 projections and shared expert (see `linear` below):
+  uint16_t* wx = nullptr;     // stacked rows [router pieces 1-3; W_down; S1], [3N + l + m_s, d]
+  uint16_t* wy = nullptr;     // [W_up | S2], [d, l + m_s]
+  uint16_t* ay = nullptr;     // [min(T, 64), l + m_s]: y_lat then h_s, bf16 high parts
+  uint16_t* ay_lo = nullptr;  // the remainders
 };
 
 struct Layout {
@@ -168,7 +177,7 @@ int check_config(const latentmoe_config* c) {
   return LATENTMOE_OK;
 }
 
-size_t max_partial_floats(const latentmoe_config& c) {
+size_t max_partial_floats(const latentmoe_config& c, bool linear) {
   // every T a forward may see: the plans only change with the tile counts
   std::vector<int> Ts;
   for (int t = 1; t <= std::min(c.max_tokens, STREAM_ROWS_BIG); t = t < 16 ? t + 1 : t + 16) Ts.push_back(t);
@@ -187,19 +196,44 @@ size_t max_partial_floats(const latentmoe_config& c) {
       Plan p = plan_dense(T, g.N, g.K);
       if (p.splits > 1 || g.always) best = std::max(best, (size_t)p.splits * T * g.N);
     }
+    if (linear && T <= STREAM_ROWS_BIG) {  // the stacked GEMMs always leave partials
+      const G lg[] = {{3 * c.n_experts + c.latent + c.shared_hidden, c.d, true},
+                      {c.d, c.latent + c.shared_hidden, true}};
+      for (const G& g : lg)
+        best = std::max(best, (size_t)plan_dense(T, g.N, g.K, TARGET_BLOCKS_STACKED).splits * T * g.N);
+    }
   }
   return best;
 }
 
-Layout make_layout(const latentmoe_config& c, Buffers& b) {
+// Decode-sized forwards (T <= 64) with bf16 projections and shared expert run on
+// one stream with no events: every GEMM over x is one launch over the stacked
+// rows [router pieces; W_down; S1] (one reduce splits logits, z and h_s), and
+// y = W_up y_lat + S2 h_s is one dual GEMM over [W_up | S2] with y_lat and h_s side
+// by side in one row.  On a multi-queue graph replay every cross-queue edge left
+// the waiting queue idle for 6-12 us; this path has none.
+bool linear_formats(const latentmoe_config& c) {
+  return c.shared_format == LATENTMOE_FORMAT_BF16 && c.proj_format == LATENTMOE_FORMAT_BF16;
+}
+
+// linear: lay out the stacked weights and rows of the decode-sized single-stream forward
+Layout make_layout(const latentmoe_config& c, Buffers& b, bool linear) {
   Layout L;
   const size_t Tm = c.max_tokens, N = c.n_experts, K = c.top_k;
   const size_t TK = Tm * K;
   const size_t nblk = (Tm + 15) / 16;
-  b.partial_cap = max_partial_floats(c);
+  b.partial_cap = max_partial_floats(c, linear);
   // every expert may end in one partial tile per row class
   b.max_tiles_cap = (int)(ceil_div(TK, STREAM_ROWS_SMALL) + 2 * std::min(N, TK));
-  L.add((void**)&b.pieces, 3 * N * c.d * 2);
+  if (linear) {  // the router pieces are the first 3N rows of the stacked x weights
+    L.add((void**)&b.wx, (3 * N + c.latent + c.shared_hidden) * (size_t)c.d * 2);
+    L.add((void**)&b.wy, (size_t)c.d * (c.latent + c.shared_hidden) * 2);
+    const size_t Tl = std::min<size_t>(Tm, STREAM_ROWS_BIG);
+    L.add((void**)&b.ay, Tl * (c.latent + c.shared_hidden) * 2);
+    L.add((void**)&b.ay_lo, Tl * (c.latent + c.shared_hidden) * 2);
+  } else {
+    L.add((void**)&b.pieces, 3 * N * c.d * 2);
+  }
   L.add((void**)&b.logits, Tm * N * 4);
   L.add((void**)&b.partial, b.partial_cap * 4);
   L.add((void**)&b.partial2, b.partial_cap * 4);
@@ -278,6 +312,8 @@ struct latentmoe_handle_s {
   // stream in program order (no side streams), so a kernel trace shows each
   // kernel's own duration
   bool serial = false;
+  bool linear = false;       // stacked weights present: decode-sized forwards run on one stream
+  bool last_linear = false;  // the last forward took that path (y_lat, h_s in the stacked rows)
   // the shared expert runs on a side stream forked from the caller's stream
   hipStream_t side = nullptr;
   hipStream_t side2 = nullptr;  // W_down, concurrent with routing
@@ -330,10 +366,11 @@ GemmParams base_params() {
 // seg[0].B's stored format; the LDS-tiled kernel reads bf16_B (its exact bf16 values)
 // instead when fmt is not bf16.
 int run_dense(latentmoe_handle_s* h, GemmParams p, int T, hipStream_t s, bool force_partial,
-              float* partial = nullptr, int fmt = WF_BF16, const uint16_t* bf16_B = nullptr) {
+              float* partial = nullptr, int fmt = WF_BF16, const uint16_t* bf16_B = nullptr,
+              int target = TARGET_BLOCKS) {
   int Ktot = 0;
   for (int i = 0; i < p.nseg; ++i) Ktot += p.seg[i].K;
-  Plan pl = plan_dense(T, p.N, Ktot);
+  Plan pl = plan_dense(T, p.N, Ktot, target);
   // keep within the partial buffer (it is sized for every T at init)
   while (pl.splits > 1 && (size_t)pl.splits * T * p.N > h->b.partial_cap) {
     pl.k_split *= 2;
@@ -387,7 +424,7 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes) {
   if (st != LATENTMOE_OK) return st;
   if (!bytes) return LATENTMOE_ERR_INVALID_ARG;
   Buffers b;
-  *bytes = make_layout(*cfg, b).total;
+  *bytes = make_layout(*cfg, b, linear_formats(*cfg)).total;
   return LATENTMOE_OK;
 }
 
@@ -419,7 +456,8 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     const char* ser = std::getenv("LATENTMOE_SERIAL");
     h->serial = ser && ser[0] == '1';
   }
-  Layout L = make_layout(*cfg, h->b);
+  h->linear = linear_formats(*cfg);
+  Layout L = make_layout(*cfg, h->b, h->linear);
   if (hipMalloc(&h->workspace, L.total) != hipSuccess) {
     (void)hipGetLastError();
     delete h;
@@ -438,6 +476,7 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     *it.first = base;
     base += (it.second + 255) & ~size_t(255);
   }
+  if (h->linear) h->b.pieces = h->b.wx;
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&h->side2, hipStreamNonBlocking) != hipSuccess ||
       hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking) != hipSuccess ||
@@ -457,6 +496,22 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     (void)hipGetLastError();
     latentmoe_destroy(h);
     return LATENTMOE_ERR_HIP;
+  }
+  if (h->linear) {
+    // stacked copies: wx rows [3N, 3N + l) = W_down, then S1; wy = [W_up | S2] row by row
+    const size_t N = cfg->n_experts, d = cfg->d, l = cfg->latent, ms = cfg->shared_hidden;
+    uint16_t* wx = h->b.wx;
+    if (hipMemcpyAsync(wx + 3 * N * d, w->w_down, l * d * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(wx + (3 * N + l) * d, w->shared_w1, ms * d * 2, hipMemcpyDeviceToDevice, stream) !=
+            hipSuccess ||
+        hipMemcpy2DAsync(h->b.wy, (l + ms) * 2, w->w_up, l * 2, l * 2, d, hipMemcpyDeviceToDevice, stream) !=
+            hipSuccess ||
+        hipMemcpy2DAsync(h->b.wy + l, (l + ms) * 2, w->shared_w2, ms * 2, ms * 2, d, hipMemcpyDeviceToDevice,
+                         stream) != hipSuccess) {
+      (void)hipGetLastError();
+      latentmoe_destroy(h);
+      return LATENTMOE_ERR_HIP;
+    }
   }
   if (h->b.w1_scale_sm) {
     launch_scale_stage_major(w->expert_w1_scale, h->b.w1_scale_sm, cfg->n_experts,
@@ -603,24 +658,50 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     tm.stop(LATENTMOE_STAGE_DOWN_PROJ, side2);
     record(h->ev_join2, side2);
   };
-  fork_to(side2, h->ev_fork);
-  down_proj();
+  // decode-sized forward on one stream (the stacked GEMMs); otherwise W_down and the
+  // shared expert run on the side streams
+  const bool linear = h->linear && T <= STREAM_ROWS_BIG;
+  h->last_linear = linear;
+  const int LS = L + ms;  // row length of the stacked activations [y_lat | h_s]
+  if (linear) {
+    // ---- 1. router logits, z = W_down x and the shared hidden in one GEMM over x ----
+    tm.start(LATENTMOE_STAGE_ROUTER);
+    GemmParams px = base_params();
+    px.seg[0] = GemmSeg{x, b.wx, d};
+    px.nseg = 1;
+    px.lda = d;
+    px.ldb = d;
+    px.N = 3 * N + LS;
+    px.ldc = px.N;
+    const int splits = run_dense(h, px, T, s, true, b.partial, WF_BF16, nullptr, TARGET_BLOCKS_STACKED);
+    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, ms, b.logits, b.z, b.z_lo, b.ay + L,
+                   b.ay_lo + L, LS, s);
+    tm.stop(LATENTMOE_STAGE_ROUTER);
+    // stages without a launch of their own here are recorded empty
+    for (int st : {LATENTMOE_STAGE_DOWN_PROJ, LATENTMOE_STAGE_SHARED_UP, LATENTMOE_STAGE_SHARED_DOWN}) {
+      tm.start(st);
+      tm.stop(st);
+    }
+  } else {
+    fork_to(side2, h->ev_fork);
+    down_proj();
 
-  // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
-  tm.start(LATENTMOE_STAGE_ROUTER);
-  GemmParams pr = base_params();
-  for (int i = 0; i < 3; ++i) pr.seg[i] = GemmSeg{x, b.pieces + (size_t)i * N * d, d};
-  pr.nseg = 3;
-  pr.lda = d;
-  pr.ldb = d;
-  pr.N = N;
-  pr.ldc = N;
-  pr.epi = EPI_F32;
-  pr.C = b.logits;
-  run_dense(h, pr, T, s, false);
-  tm.stop(LATENTMOE_STAGE_ROUTER);
-  fork_to(side, h->ev_fork2);
-  shared_expert();
+    // ---- 1. router logits: x [T, d] times the three exact bf16 pieces of W_r ----
+    tm.start(LATENTMOE_STAGE_ROUTER);
+    GemmParams pr = base_params();
+    for (int i = 0; i < 3; ++i) pr.seg[i] = GemmSeg{x, b.pieces + (size_t)i * N * d, d};
+    pr.nseg = 3;
+    pr.lda = d;
+    pr.ldb = d;
+    pr.N = N;
+    pr.ldc = N;
+    pr.epi = EPI_F32;
+    pr.C = b.logits;
+    run_dense(h, pr, T, s, false);
+    tm.stop(LATENTMOE_STAGE_ROUTER);
+    fork_to(side, h->ev_fork2);
+    shared_expert();
+  }
 
   // ---- 2. top-K + softmax over the logits (plus the bias, when given) ----
   tm.start(LATENTMOE_STAGE_TOPK);
@@ -659,7 +740,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_BUCKET);
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
-  wait(s, h->ev_join2);
+  if (!linear) wait(s, h->ev_join2);
 
   // ---- 5/6. grouped expert GEMMs ----
   GemmParams pe = base_params();
@@ -731,7 +812,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // fill part of the GPU); its expert down needs only its own expert up, so it runs
   // on side stream 2 beside the bf16 class's expert up, and the combine waits for
   // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
-  const bool hi_side = split_rows && !tm.on && !h->serial;
+  const bool hi_side = split_rows && !tm.on && !h->serial && !linear;
   // the bf16 class's expert-down rows go out as bf16: their rounding enters y_lat times
   // a gate below the class threshold, like that of their bf16 z and h
   const bool og_mix = split_rows;
@@ -765,8 +846,28 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);
   launch_combine(b.og, og_mix ? b.og16 : nullptr, b.paired, b.zrow32, b.zrow16, b.inv,
-                 T, K, L, b.y_lat, b.y_lat_lo, s);
+                 T, K, L, linear ? b.ay : b.y_lat, linear ? b.ay_lo : b.y_lat_lo, linear ? LS : L, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
+
+  if (linear) {
+    // ---- 8. y = [W_up | S2] [y_lat ; h_s], both as bf16 hi + lo ----
+    tm.start(LATENTMOE_STAGE_UP_PROJ);
+    GemmParams pq = base_params();
+    pq.seg[0] = GemmSeg{b.ay, b.wy, LS};
+    pq.a_lo = b.ay_lo;
+    pq.nseg = 1;
+    pq.lda = LS;
+    pq.ldb = LS;
+    pq.N = d;
+    pq.epi = EPI_F32;
+    pq.C = y;
+    pq.ldc = d;
+    run_dense(h, pq, T, s, false, nullptr, WF_BF16, nullptr, TARGET_BLOCKS_STACKED);
+    tm.stop(LATENTMOE_STAGE_UP_PROJ);
+    tm.done();
+    h->last_T = T;
+    return;
+  }
 
   // ---- 8. y += W_up y_lat (after the shared expert wrote y) ----
   wait(s, h->ev_join);
@@ -869,6 +970,21 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
   }
   if (bytes > have) return LATENTMOE_ERR_INVALID_ARG;
   if (bytes == 0) return LATENTMOE_OK;
+  if (h->last_linear && (which == LATENTMOE_INTER_Y_LAT || which == LATENTMOE_INTER_Y_LAT_LO ||
+                         which == LATENTMOE_INTER_HS_HI || which == LATENTMOE_INTER_HS_LO)) {
+    // decode-sized forwards keep y_lat and h_s side by side in rows of l + m_s
+    const bool lo = which == LATENTMOE_INTER_Y_LAT_LO || which == LATENTMOE_INTER_HS_LO;
+    const bool hs = which == LATENTMOE_INTER_HS_HI || which == LATENTMOE_INTER_HS_LO;
+    const size_t w = (hs ? c.shared_hidden : c.latent) * 2, pitch = (size_t)(c.latent + c.shared_hidden) * 2;
+    const uint16_t* base = (lo ? h->b.ay_lo : h->b.ay) + (hs ? c.latent : 0);
+    const size_t rows = bytes / w, rest = bytes % w;
+    if (rows && hipMemcpy2DAsync(dst, w, base, pitch, w, rows, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return LATENTMOE_ERR_HIP;
+    if (rest && hipMemcpyAsync(static_cast<char*>(dst) + rows * w, reinterpret_cast<const char*>(base) + rows * pitch,
+                               rest, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return LATENTMOE_ERR_HIP;
+    return LATENTMOE_OK;
+  }
   return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess
              ? LATENTMOE_OK
              : LATENTMOE_ERR_HIP;
@@ -978,7 +1094,7 @@ extern "C" int latentmoe_forward_static(const latentmoe_config* cfg, const laten
   h.cfg.max_tokens = T;
   h.w = *w;
   h.serial = true;  // one stream, no events
-  const Layout L = make_layout(h.cfg, h.b);
+  const Layout L = make_layout(h.cfg, h.b, false);
   if (L.total > (size_t)LATENTMOE_STATIC_SCRATCH_BYTES) return LATENTMOE_ERR_SCRATCH;
   void* base = nullptr;
   st = static_scratch(&base);

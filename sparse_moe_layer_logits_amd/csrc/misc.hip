@@ -35,6 +35,66 @@ void launch_reduce(const GemmParams& p, hipStream_t s) {
   reduce_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, s>>>(p);
 }
 
+// Decode-sized forward: one GEMM over x with the stacked weight rows
+// [router piece 1; piece 2; piece 3; W_down; S1] leaves split-K partials
+// [splits][T][NS], NS = 3N + L + MS.  This sums them and splits the columns: the
+// three piece columns of expert e add up to its fp32 logit (the pieces sum to the
+// fp32 router weight exactly); then z = W_down x leaves as a bf16 pair; then
+// h_s = relu(S1 x)^2 leaves as a bf16 pair into columns [L, L + MS) of the rows
+// (stride ldh) that the final GEMM [W_up | S2] reads.  One thread per 4 columns
+// of logits, z or h_s; splits are summed in order.
+__global__ void xreduce_kernel(const float* __restrict__ partial, int splits, long long pstride, int T,
+                               int N, int L, int MS, float* __restrict__ logits, uint16_t* __restrict__ z,
+                               uint16_t* __restrict__ z_lo, uint16_t* __restrict__ hs,
+                               uint16_t* __restrict__ hs_lo, int ldh) {
+  const int G = (N + L + MS) / 4;  // output groups per row
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)T * G) return;
+  const int t = (int)(i / G);
+  const int c = (int)(i % G) * 4;  // output column in [0, N + L + MS)
+  const int NS = 3 * N + L + MS;
+  const float* row = partial + (long long)t * NS;
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  if (c < N) {
+    for (int s = 0; s < splits; ++s) {
+      const float* q = row + s * pstride + c;
+      v += *reinterpret_cast<const f32x4_t*>(q) + *reinterpret_cast<const f32x4_t*>(q + N) +
+           *reinterpret_cast<const f32x4_t*>(q + 2 * N);
+    }
+    *reinterpret_cast<f32x4_t*>(logits + (long long)t * N + c) = v;
+    return;
+  }
+  const int cc = c + 2 * N;  // partial column of z or h_s
+  for (int s = 0; s < splits; ++s) v += *reinterpret_cast<const f32x4_t*>(row + s * pstride + cc);
+  u32x2_t hi, lo;
+  if (c < N + L) {
+    epi_pack<EPI_BF16_HILO>(v, hi, lo);
+    const long long off = (long long)t * L + (c - N);
+    *reinterpret_cast<u32x2_t*>(z + off) = hi;
+    *reinterpret_cast<u32x2_t*>(z_lo + off) = lo;
+  } else {
+    f32x4_t u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float r = fmaxf(v[j], 0.0f);
+      u[j] = r * r;
+    }
+    epi_pack<EPI_SQRELU_HILO>(u, hi, lo);
+    const long long off = (long long)t * ldh + (c - N - L);
+    *reinterpret_cast<u32x2_t*>(hs + off) = hi;
+    *reinterpret_cast<u32x2_t*>(hs_lo + off) = lo;
+  }
+}
+
+void launch_xreduce(const float* partial, int splits, long long pstride, int T, int N, int L, int MS,
+                    float* logits, uint16_t* z, uint16_t* z_lo, uint16_t* hs, uint16_t* hs_lo, int ldh,
+                    hipStream_t s) {
+  const long long n = (long long)T * ((N + L + MS) / 4);
+  if (n <= 0) return;
+  xreduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(partial, splits, pstride, T, N, L, MS, logits, z,
+                                                             z_lo, hs, hs_lo, ldh);
+}
+
 // Gated sum over each token's K expert outputs, in the order of its top-K list
 // ("Nemotron 3 Super", section 3.2: the experts' outputs are combined in the
 // latent space before the up-projection).  og rows are already multiplied by
@@ -55,7 +115,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
                                                      const uint16_t* __restrict__ z16,
                                                      const int* __restrict__ inv, int K, int L,
                                                      uint16_t* __restrict__ y_lat,
-                                                     uint16_t* __restrict__ y_lat_lo) {
+                                                     uint16_t* __restrict__ y_lat_lo, int ldy) {
   __shared__ int pos[64];
   __shared__ int wide[64];
   const int t = blockIdx.x;
@@ -102,20 +162,20 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
     hi[i] = bf16_bits_to_f32(f32_to_bf16_bits(acc[i]));
     lo[i] = acc[i] - hi[i];
   }
-  store_bf16x4(y_lat, (long long)t * L + c, hi[0], hi[1], hi[2], hi[3]);
-  store_bf16x4(y_lat_lo, (long long)t * L + c, lo[0], lo[1], lo[2], lo[3]);
+  store_bf16x4(y_lat, (long long)t * ldy + c, hi[0], hi[1], hi[2], hi[3]);
+  store_bf16x4(y_lat_lo, (long long)t * ldy + c, lo[0], lo[1], lo[2], lo[3]);
 }
 
 void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
                     const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
-                    uint16_t* y_lat, uint16_t* y_lat_lo, hipStream_t s) {
+                    uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s) {
   if (T <= 0) return;
   dim3 grid(T, (L / 4 + 63) / 64);
   if (og16)
-    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, paired, z32, z16, inv, K, L, y_lat, y_lat_lo);
+    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, paired, z32, z16, inv, K, L, y_lat, y_lat_lo, ldy);
   else
     combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, nullptr, nullptr, inv, K, L, y_lat,
-                                              y_lat_lo);
+                                              y_lat_lo, ldy);
 }
 
 // zero n 32-bit words (a kernel rather than a memset node, so that a captured

@@ -1,14 +1,17 @@
 """latentmoe_forward_static, the entry point that allocates nothing: its workspace
 lives in the library's static device array.  Checked against latentmoe_forward on
-the same inputs (same kernels: the outputs are equal bit for bit) and against the
-oracle, on two calls in a row, the second with a smaller T."""
+the same inputs and against the oracle, on two calls in a row, the second with a
+smaller T.  Above 64 tokens both run the same launches (outputs equal bit for bit);
+up to 64 tokens latentmoe_forward runs the stacked single-stream GEMMs, which sum
+in another order: top-K sets equal, gates within 1e-6, outputs within 1e-4 of
+each other's rms and 1e-2 of the oracle's."""
 import numpy as np
 import pytest
 
 import oracle
 from sparse_moe_layer_logits_amd import binding, synth
 
-from gpu_common import log
+from gpu_common import check_topk, log
 from test_gpu_parity import gen
 
 pytestmark = pytest.mark.gpu
@@ -53,12 +56,17 @@ def test_static_entry_matches_forward(name, Ts):
         ys, idxs, gs = _static(layer, xd[:T], T)
         yf, idxf, gf = layer.forward(xd[:T])
         torch.cuda.synchronize()
-        assert torch.equal(ys, yf) and torch.equal(idxs, idxf) and torch.equal(gs, gf), (name, T)
+        if T > 64:
+            assert torch.equal(ys, yf) and torch.equal(idxs, idxf) and torch.equal(gs, gf), (name, T)
+        else:
+            check_topk(idxs.cpu().numpy(), gs.cpu().numpy(), idxf.cpu().numpy(), gf.cpu().numpy())
+            a, b = ys.cpu().numpy().astype(np.float64), yf.cpu().numpy().astype(np.float64)
+            assert np.max(np.abs(a - b)) <= 1e-4 * np.sqrt(np.mean(b ** 2)), (name, T)
         rms = np.sqrt(np.mean(ref["y"][:T] ** 2))
         err = np.max(np.abs(ys.cpu().numpy() - ref["y"][:T]))
         assert err <= 1e-2 * rms
         assert [sorted(r) for r in idxs.cpu().numpy().tolist()] == [sorted(r) for r in ref["idx"][:T].tolist()]
-        log("static entry %s T=%d: equal to latentmoe_forward, max|gpu-oracle|/rms = %.2e" % (name, T, err / rms))
+        log("static entry %s T=%d: matches latentmoe_forward, max|gpu-oracle|/rms = %.2e" % (name, T, err / rms))
     layer.close()
 
 
@@ -71,10 +79,8 @@ def test_static_entry_rejects_before_work():
     xd = binding.to_device(x)
     y = torch.full((wl.T, wl.d), 5.0, device="cuda")
     s = layer.stream.cuda_stream
-    fits = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 64, 0)   # 60.3 MiB
-    assert binding.latentmoe_workspace_bytes(fits) <= binding.LATENTMOE_STATIC_SCRATCH_BYTES
-    too_big = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 65, 0)  # 70.6 MiB
-    assert binding.latentmoe_workspace_bytes(too_big) > binding.LATENTMOE_STATIC_SCRATCH_BYTES
+    # Super decode shapes: 64 tokens fit the array (60.3 MiB of workspace), 65 need 70.6 MiB
+    too_big = binding.latentmoe_config(4096, 1024, 512, 22, 2688, 5376, 65, 0)
     cases = [(too_big, 65, binding.LATENTMOE_ERR_SCRATCH),
              (layer.cfg, wl.T + 1, binding.LATENTMOE_ERR_INVALID_ARG)]
     fp4 = binding.latentmoe_config(*[getattr(layer.cfg, f) for f, _ in binding.latentmoe_config._fields_])
