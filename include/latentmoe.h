@@ -127,7 +127,11 @@ typedef struct {
  * receives the handle (set to NULL on failure).
  * Errors: INVALID_ARG (null pointer, including a scale pointer that the
  * chosen format needs), UNSUPPORTED (shape requirements above, a format not
- * offered for that matrix), OUT_OF_MEMORY, HIP. */
+ * offered for that matrix), OUT_OF_MEMORY (the workspace allocation failed;
+ * LATENTMOE_FAIL_ALLOC=1 in the environment forces this, for tests), HIP.
+ * With bf16 projections and shared expert the workspace also holds stacked
+ * copies of [router pieces; W_down; S1] and [W_up | S2] for forwards of at most
+ * 64 tokens, which run on `stream` alone. */
 int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
                    latentmoe_handle_t* out);
 

@@ -73,6 +73,13 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 #undef VMCNT_WAIT
 }
 
+// the same with a compile-time count (one wait instruction, no selection)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_c() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Output tile through LDS.  A lane's accumulators hold 4 columns of one row, so
 // direct stores write 32 (bf16) or 64 (fp32) bytes of each of 16 rows per
 // instruction; L2 reads every line written that way before merging (measured:
@@ -202,7 +209,10 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
   }
 }
 
-template <bool DUAL, int EPI>
+// ONESEG: the reduction runs over one segment (every GEMM but the router's three
+// weight pieces): a stage's load addresses are a base plus the stage's k offset,
+// with no segment selection in the loop
+template <bool DUAL, int EPI, bool ONESEG>
 __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int STAGES = bg_stages<DUAL>();
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS chunk bases stay scalar
   const int wn = wave & 1, wm = wave >> 1;  // 128 weight rows x BG_MB * 16 activation rows
   const int r16 = lane & 15, g = lane >> 4;
 
@@ -305,14 +315,16 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     int k = kbeg + kt * BG_BK;
     const uint16_t* A = A0;
     const uint16_t* B = B0;
-    if (k >= K0 && p.nseg > 1) {
-      k -= K0;
-      A = A1;
-      B = B1;
-      if (k >= K1 && p.nseg > 2) {
-        k -= K1;
-        A = A2;
-        B = B2;
+    if constexpr (!ONESEG) {
+      if (k >= K0 && p.nseg > 1) {
+        k -= K0;
+        A = A1;
+        B = B1;
+        if (k >= K1 && p.nseg > 2) {
+          k -= K1;
+          A = A2;
+          B = B2;
+        }
       }
     }
     uint8_t* st = smem + (kt % STAGES) * STAGEB;
@@ -388,11 +400,18 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     // a step with a next one; every such step has the same shape, so the compiler's
     // wait insertion sees the current set complete (the explicit wait) and the next
     // set's reads as the only ones outstanding.  The last step runs on its own.
-    auto step = [&](int kt, const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB]) {
+    // FAST: a steady-state step (kt + STAGES < KT): stages up to kt - 1 + STAGES were
+    // all issued, so STAGES - 2 stages follow stage kt + 1 (a compile-time wait), and
+    // stage kt + STAGES exists (its loads are issued without a test)
+    auto step = [&](int kt, const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB], auto fast) {
+      constexpr bool FAST = decltype(fast)::value;
       // this wave's reads of step kt are in registers; after the barrier no wave
       // reads slot kt % STAGES any more
       __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-      wait_vmcnt(min(STAGES - 2, KT - 2 - kt) * LOADS);
+      if constexpr (FAST)
+        wait_vmcnt_c<(STAGES - 2) * LOADS>();
+      else
+        wait_vmcnt(min(STAGES - 2, KT - 2 - kt) * LOADS);
       asm volatile("s_barrier" ::: "memory");
       const uint8_t* base = smem + ((kt + 1) % STAGES) * STAGEB;
 #pragma unroll
@@ -409,7 +428,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
         // wave's MFMAs wait behind its own loads
 #pragma unroll
         for (int u = a * LOADS / 8; u < (a + 1) * LOADS / 8; ++u)
-          if (kt + STAGES < KT) issue_one(kt + STAGES, u);
+          if (FAST || kt + STAGES < KT) issue_one(kt + STAGES, u);
       }
       // keep the interleave: the activation reads, then 4 MFMAs and one read per a
       __builtin_amdgcn_sched_group_barrier(0x100, BG_MB, 0);
@@ -419,13 +438,19 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     };
+    const std::integral_constant<bool, true> fast{};
+    const std::integral_constant<bool, false> checked{};
     int kt = 0;
+    for (; kt + 1 + STAGES < KT; kt += 2) {
+      step(kt, xa, xb, fast);
+      step(kt + 1, xb, xa, fast);
+    }
     for (; kt + 2 < KT; kt += 2) {
-      step(kt, xa, xb);
-      step(kt + 1, xb, xa);
+      step(kt, xa, xb, checked);
+      step(kt + 1, xb, xa, checked);
     }
     if (kt + 1 < KT) {  // two steps left: one more with a next step, ending in xb
-      step(kt, xa, xb);
+      step(kt, xa, xb, checked);
 #pragma unroll
       for (int b = 0; b < BG_MB; ++b) xa[0][b] = xb[0][b];
     }
@@ -437,10 +462,15 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < KT) issue(s);
-    for (int kt = 0; kt < KT; ++kt) {
+    // FAST: a steady-state step (kt + STAGES - 1 < KT): STAGES - 2 later stages are in
+    // flight (a compile-time wait) and stage kt + STAGES - 1 exists
+    auto dstep = [&](int kt, auto fast) {
+      constexpr bool FAST = decltype(fast)::value;
       // stages issued after step kt: min(STAGES - 2, KT - 1 - kt)
-      const int later = min(STAGES - 2, KT - 1 - kt);
-      wait_vmcnt(later * LOADS);
+      if constexpr (FAST)
+        wait_vmcnt_c<(STAGES - 2) * LOADS>();
+      else
+        wait_vmcnt(min(STAGES - 2, KT - 1 - kt) * LOADS);
       // a plain barrier: the step's own loads were waited for above; a fenced
       // __syncthreads would wait for every load in flight, draining the ring
       asm volatile("s_barrier" ::: "memory");
@@ -449,7 +479,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
       // stage kt + STAGES - 1 goes to the slot every wave finished reading before
       // this barrier; its loads are spread over the MFMAs (see the pipelined path)
-      const bool more = kt + STAGES - 1 < KT;
+      const bool more = FAST || kt + STAGES - 1 < KT;
 #pragma unroll
       for (int part = 0; part < NPART; ++part)
 #pragma unroll
@@ -461,7 +491,10 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
           for (int u = grp * LOADS / (8 * NPART); u < (grp + 1) * LOADS / (8 * NPART); ++u)
             if (more) issue_one(kt + STAGES - 1, u);
         }
-    }
+    };
+    int kt = 0;
+    for (; kt + STAGES - 1 < KT; ++kt) dstep(kt, std::integral_constant<bool, true>{});
+    for (; kt < KT; ++kt) dstep(kt, std::integral_constant<bool, false>{});
   }
 
   big_epilogue<EPI>(p, smem, acc, expert, split, row0, rows, n0, wn, wm, r16, g, tid);
@@ -472,7 +505,10 @@ constexpr int big_lds_bytes() { return bg_stages<DUAL>() * BG_TILEB * (1 + (DUAL
 
 template <bool DUAL, int EPI>
 static hipError_t big_attr() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<DUAL, EPI>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<DUAL, EPI, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes<DUAL>());
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_kernel<DUAL, EPI, false>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, big_lds_bytes<DUAL>());
 }
 
@@ -517,13 +553,22 @@ void launch_gemm_big(const GemmParams& p, hipStream_t s) {
   if (p.splits == 1) tiles = (tiles + 7) / 8 * 8;  // whole groups of 8 tiles
   const long long blocks = tiles * NQ * p.splits;
   if (blocks <= 0) return;
+  const bool one = p.nseg == 1;
   if (p.a_lo)
     big_for_each_epi(p.epi, [&](auto E) {
-      gemm_big_kernel<true, decltype(E)::value><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<true>(), s>>>(p);
+      constexpr int EPI = decltype(E)::value;
+      if (one)
+        gemm_big_kernel<true, EPI, true><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<true>(), s>>>(p);
+      else
+        gemm_big_kernel<true, EPI, false><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<true>(), s>>>(p);
     });
   else
     big_for_each_epi(p.epi, [&](auto E) {
-      gemm_big_kernel<false, decltype(E)::value><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<false>(), s>>>(p);
+      constexpr int EPI = decltype(E)::value;
+      if (one)
+        gemm_big_kernel<false, EPI, true><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<false>(), s>>>(p);
+      else
+        gemm_big_kernel<false, EPI, false><<<(unsigned)blocks, BG_THREADS, big_lds_bytes<false>(), s>>>(p);
     });
 }
 

@@ -458,7 +458,12 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
   }
   h->linear = linear_formats(*cfg);
   Layout L = make_layout(*cfg, h->b, h->linear);
-  if (hipMalloc(&h->workspace, L.total) != hipSuccess) {
+  // LATENTMOE_FAIL_ALLOC=1 in the environment makes the workspace allocation fail
+  // (tests of the out-of-memory path)
+  const char* fail = std::getenv("LATENTMOE_FAIL_ALLOC");
+  const bool force_fail = fail && fail[0] == '1';
+  if (force_fail || hipMalloc(&h->workspace, L.total) != hipSuccess) {
+    h->workspace = nullptr;
     (void)hipGetLastError();
     delete h;
     return LATENTMOE_ERR_OUT_OF_MEMORY;

@@ -234,6 +234,27 @@ def test_chunked_bucketing(n_experts):
     full_check(wl, x, W)
 
 
+def test_workspace_allocation_failure(monkeypatch):
+    """LATENTMOE_FAIL_ALLOC=1 makes init's workspace allocation fail: init returns
+    OUT_OF_MEMORY and hands out no handle; without it the same weights initialise
+    and the layer runs."""
+    import torch
+    wl = synth.WORKLOADS["tiny"]
+    x, W = gen(wl, 0)
+    Wd = binding.upload_weights(W)
+    monkeypatch.setenv("LATENTMOE_FAIL_ALLOC", "1")
+    with pytest.raises(binding.LatentMoEError) as e:
+        binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    assert e.value.status == binding.LATENTMOE_ERR_OUT_OF_MEMORY
+    monkeypatch.delenv("LATENTMOE_FAIL_ALLOC")
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    y, idx, g = layer.forward(binding.to_device(x))
+    torch.cuda.synchronize()
+    ref = oracle.forward(x, W, wl.top_k)
+    assert np.max(np.abs(y.cpu().numpy() - ref["y"])) <= 1e-2 * np.sqrt(np.mean(ref["y"] ** 2))
+    layer.close()
+
+
 def test_edge_token_counts_and_reuse():
     import torch
     wl = small_wl(T=33, d=256, latent=64, n_experts=16, top_k=4)
