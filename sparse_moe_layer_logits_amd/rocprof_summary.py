@@ -10,6 +10,15 @@
         copy launches of the same run (bench.py --copy-probe-mib M: M MiB read
         and M MiB written per launch).
 
+    python -m sparse_moe_layer_logits_amd.rocprof_summary mfma PMC_DIR --group SUBSTR@GRID [...] \\
+            --alg-flops F --source-sha SHA --out FILE.json
+        MFMA work of a stage (its kernel groups, one launch each) from a run with
+        SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE:
+        executed flops (512 per MOPS unit) against the stage's algorithmic flops,
+        and MFMA-busy cycles against the SIMD cycles of the launches' duration
+        (GRBM_GUI_ACTIVE counts every XCC; SIMD and XCC counts come from the run's
+        agent information).
+
 DIR is the rocprofv3 output directory (-d) of a run with --output-format csv.
 """
 import argparse
@@ -95,6 +104,57 @@ def cmd_traffic(a):
     print(json.dumps(res, indent=1))
 
 
+def gpu_agent(dir_):
+    for r in csv.DictReader(open(_one(dir_, "*agent_info.csv"))):
+        if int(r.get("Simd_Count") or 0) > 0:
+            return r
+    raise SystemExit("no GPU agent in %s" % dir_)
+
+
+def cmd_mfma(a):
+    agent = gpu_agent(a.dir)
+    simds, xcc = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    max_ghz = int(agent["Max_Engine_Clk_Fcompute"]) / 1e3
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    n = collections.Counter()
+    dur = collections.defaultdict(float)
+    seen = set()
+    for r in csv.DictReader(open(_one(a.dir, "*counter_collection.csv"))):
+        key = (r["Kernel_Name"], int(r["Grid_Size"]))
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        if (r["Dispatch_Id"], key) not in seen:
+            seen.add((r["Dispatch_Id"], key))
+            n[key] += 1
+            dur[key] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    mops = busy = cycles = seconds = 0.0
+    names = []
+    for kernel, grid in [(g.rsplit("@", 1)[0], int(g.rsplit("@", 1)[1])) for g in a.group]:
+        (name, g), v = _pick(per, kernel, grid)
+        c = n[(name, g)]
+        mops += v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / c
+        busy += v["SQ_VALU_MFMA_BUSY_CYCLES"] / c
+        cycles += v["GRBM_GUI_ACTIVE"] / c / xcc
+        seconds += dur[(name, g)] / c
+        names.append("%s @%d (%d launches)" % (name, g, c))
+    executed = mops * 512
+    res = {
+        "groups": names,
+        "executed_tflop_per_launch": executed / 1e12,
+        "algorithmic_tflop_per_launch": a.alg_flops / 1e12,
+        "executed_over_algorithmic": executed / a.alg_flops,
+        "mfma_busy_frac": busy / (simds * cycles),
+        "launch_ms": seconds * 1e3,
+        "clock_ghz": cycles / seconds / 1e9,
+        "executed_tflops": executed / seconds / 1e12,
+        "algorithmic_tflops": a.alg_flops / seconds / 1e12,
+        "peak_at_max_clock_tflops": simds * 1024 * max_ghz / 1e3,
+        "source_sha": a.source_sha,
+        "command": a.command,
+    }
+    json.dump(res, open(a.out, "w"), indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -110,8 +170,16 @@ def main(argv=None):
     t.add_argument("--source-sha", required=True)
     t.add_argument("--command", default="")
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--group", action="append", required=True,
+                   help="kernel name substring @ grid size (threads); repeat for a stage of several launches")
+    m.add_argument("--alg-flops", type=float, required=True, help="algorithmic flops of one launch of the stage")
+    m.add_argument("--source-sha", required=True)
+    m.add_argument("--command", default="")
+    m.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"kt": cmd_kt, "traffic": cmd_traffic}[a.cmd](a)
+    {"kt": cmd_kt, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
