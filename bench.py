@@ -32,6 +32,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "sparse_moe_layer_logits_amd/csrc/"
 KERNEL_SOURCES = {  # kernel -> the files (source and included headers) whose hash pins stored counter data
     "gemm_stream_kernel": ("gemm_stream.hip", "common.hpp", "epilogue.hpp", "fp4.hpp", "fp8.hpp", "kernels.hpp"),
+    "gemm_stream_pair_kernel": ("gemm_stream.hip", "common.hpp", "epilogue.hpp", "fp4.hpp", "fp8.hpp",
+                                "kernels.hpp"),
     "gemm_mid_kernel": ("gemm_mid.hip", "common.hpp", "epilogue.hpp", "fp4.hpp", "fp8.hpp", "kernels.hpp"),
     "gemm_big_kernel": ("gemm_big.hip", "common.hpp", "epilogue.hpp", "kernels.hpp"),
     "ssm_verify_kernel": ("ssm_replay.hip", "common.hpp", "../../include/ssm_replay.h"),
@@ -64,17 +66,32 @@ def algorithmic(wl, touched):
     return bytes_, flops
 
 
+def shared_rides(wl):
+    """Whether the library runs the shared expert's two GEMMs inside the expert
+    launches (S1 with expert up, S2 with expert down): decode-sized forwards
+    (T <= 64) with bf16 experts, shared expert and projections whose experts take
+    the streaming kernel."""
+    return (wl.T <= 64 and wl.experts == "bf16" and wl.shared == "bf16" and wl.proj == "bf16"
+            and wl.T * wl.top_k / wl.n_experts <= 48)
+
+
 def expert_kernel_units(wl, touched, stage):
     """Algorithmic bytes and flops of one launch of a grouped expert GEMM:
     the touched experts' weight matrix, the T*K routed input rows, the T*K
-    output rows (bf16 rows for the method's activations)."""
+    output rows (bf16 rows for the method's activations); plus, when the shared
+    expert rides in that launch, its matrix, its T input and T output rows."""
     l, m, TK = wl.latent, wl.expert_hidden, wl.T * wl.top_k
     wbytes = l * m * (2.0 if wl.experts == "bf16" else 0.5 + 1.0 / 16)
     if stage == "expert_up":
         io = TK * l * 2 + TK * m * 2
     else:
         io = TK * m * 2 + TK * l * 2
-    return touched * wbytes + io, 2.0 * TK * l * m
+    b, f = touched * wbytes + io, 2.0 * TK * l * m
+    if shared_rides(wl):
+        d, ms, T = wl.d, wl.shared_hidden, wl.T
+        b += d * ms * 2 + T * ms * 2 + (T * d * 2 if stage == "expert_up" else T * d * 4)  # x or y (fp32)
+        f += 2.0 * T * d * ms
+    return b, f
 
 
 def expert_kernel(wl):
@@ -88,7 +105,7 @@ def expert_kernel(wl):
         return "gemm_big_kernel"
     if wl.experts == "fp4" and avg_rows > 24 and wl.latent % 128 == 0 and wl.expert_hidden % 128 == 0:
         return "gemm_mid_kernel"
-    return "gemm_stream_kernel"
+    return "gemm_stream_pair_kernel" if shared_rides(wl) else "gemm_stream_kernel"
 
 
 def cpu_model():
@@ -222,8 +239,9 @@ def measure(name, args, steps, warmup, tokens=0, cpu_budget=15.0, cpu_1thread=Fa
     log("%s: timed %d graph-replayed steps: %.4f ms/step (p10 %.4f, median %.4f, p90 %.4f)"
         % (wl.name, steps, ms_per_step, *np.percentile(per_step, [10, 50, 90])))
 
-    # timed region 2: the same steps launched eagerly, with HIP events on the
-    # forward's streams around each stage (per-kernel durations for the roofline)
+    # timed region 2: the same steps launched eagerly with HIP events around
+    # each stage; stage-timed forwards run every stage in program order on one
+    # stream, so each stage's time is its own kernels' (durations for the roofline)
     layer.profile_begin(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()

@@ -131,7 +131,10 @@ typedef struct {
  * LATENTMOE_FAIL_ALLOC=1 in the environment forces this, for tests), HIP.
  * With bf16 projections and shared expert the workspace also holds stacked
  * copies of [router pieces; W_down; S1] and [W_up | S2] for forwards of at most
- * 64 tokens, which run on `stream` alone. */
+ * 64 tokens, which run on `stream` alone.  Larger forwards fork two side
+ * streams of the default priority from `stream` (W_down; the shared expert);
+ * LATENTMOE_SERIAL=1 in the environment at init keeps every stage of this
+ * handle on `stream` in program order (per-kernel profiling). */
 int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
                    latentmoe_handle_t* out);
 
@@ -250,7 +253,10 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
  * latentmoe_profile_begin reserves events for up to max_calls forward calls
  * (host allocation of HIP events; call it outside any timed or captured
  * region); every later latentmoe_forward records one start/stop pair for each
- * stage whose bit (1 << LATENTMOE_STAGE_*) is set in stage_mask.
+ * stage whose bit (1 << LATENTMOE_STAGE_*) is set in stage_mask.  While
+ * recording, a forward runs every stage in program order on the caller's
+ * stream (no side streams), so a stage's time is that of its own kernels; its
+ * outputs are the same as those of an untimed call.
  * latentmoe_profile_end synchronises those events, writes the summed
  * milliseconds of each stage to stage_ms (host, n_stages entries, order of
  * LATENTMOE_STAGE_*), the number of recorded calls to *calls (host), and

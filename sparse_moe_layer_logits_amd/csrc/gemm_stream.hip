@@ -93,8 +93,15 @@ struct BFrag<WF_FP8> {
   u32x4_t codes;   // 16 E4M3 bytes: step 0 in words 0-1, step 1 in words 2-3
 };
 
+// LDS bytes of one block: two chunk buffers of the tile's activation rows
+template <int ROWS, int PAIRS, bool DUAL>
+constexpr int stream_lds_bytes() {
+  return 2 * (DUAL ? 2 : 1) * ROWS * (64 * PAIRS * 2);
+}
+
+// One block's work item `block` of GEMM p; smem holds stream_lds_bytes() bytes.
 template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) void gemm_stream_kernel(GemmParams p) {
+__device__ __forceinline__ void stream_tile(const GemmParams& p, const int block, uint8_t* smem) {
   constexpr int MTMAX = ROWS / 16;
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int KC = 64 * PAIRS;                           // k per chunk
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) voi
   constexpr int THREADS = W * 64;
   constexpr int APT = (PIECES + THREADS - 1) / THREADS;    // A pieces per thread
   constexpr int PPR = 8 * PAIRS;                           // pieces per row and part
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][NPART * ROWS * ROWB];
+  auto As = reinterpret_cast<uint8_t (*)[NPART * ROWS * ROWB]>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) voi
 
   // ---- work item ----
   const int NQ = (p.N + W * NT * 16 - 1) / (W * NT * 16);
-  int item = blockIdx.x;
+  int item = block;
   const int split = item % p.splits;
   item /= p.splits;
   const int q = item % NQ;
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) voi
 
   if constexpr (FMT == WF_FP4) {
     // FP4 fragments are small (3 registers per pair): rings of R chunks of weights and
-    // activation pieces (registers) keep R - 2 chunks of loads in flight while a chunk
+    // activation pieces (registers) keep R - 1 chunks of loads in flight while a chunk
     // is computed.  Step cc loads chunk cc + R - 1 (activations first, then weights) and
     // moves chunk cc + 1's activations to LDS; loads complete in order, so that wait
     // leaves the younger chunks in flight.  Every step issues the same loads (clamped
@@ -427,6 +434,32 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) voi
   });
 }
 
+template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) void gemm_stream_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[stream_lds_bytes<ROWS, PAIRS, DUAL>()];
+  stream_tile<W, NT, ROWS, PAIRS, FMT, DUAL>(p, blockIdx.x, smem);
+}
+
+// Two GEMMs in one launch: blocks [0, q_blocks) run q, a dense GEMM of at most 64
+// rows over its whole k range (bf16 weights, 128-k chunks; QDUAL: hi + lo
+// activations), the rest run the grouped expert GEMM p.  A dense GEMM of a few
+// tokens on its own is a short launch whose blocks wait on memory latency
+// (a few chunks each, then split-K partial sums); inside a long weight-streaming
+// launch its blocks start first, read their weights at the launch's rate and
+// finish long before it ends.
+template <int W, int NT, int ROWS, int PAIRS, int FMT, bool DUAL, bool QDUAL>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(1))) void gemm_stream_pair_kernel(
+    GemmParams p, GemmParams q, int q_blocks) {
+  constexpr int LP = stream_lds_bytes<ROWS, PAIRS, DUAL>();
+  constexpr int LQ = stream_lds_bytes<64, 2, QDUAL>();
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LP > LQ ? LP : LQ];
+  const int b = blockIdx.x;
+  if (b < q_blocks)
+    stream_tile<W, NT, 64, 2, WF_BF16, QDUAL>(q, b, smem);
+  else
+    stream_tile<W, NT, ROWS, PAIRS, FMT, DUAL>(p, b - q_blocks, smem);
+}
+
 // block shape: 8 waves of one 16-row weight tile each
 constexpr int ST_W = 8, ST_NT = 1;
 
@@ -481,6 +514,43 @@ void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s) {
     launch_dual<WF_FP8>(p, rows, tiles, s);
   else
     launch_dual<WF_BF16>(p, rows, tiles, s);
+}
+
+template <int ROWS, int PAIRS, bool QDUAL>
+static void launch_pair_rows(const GemmParams& p, const GemmParams& q, hipStream_t s) {
+  constexpr int W = ST_W, NT = ST_NT;
+  const long long q_blocks = (long long)(q.N + W * NT * 16 - 1) / (W * NT * 16) * ((q.M + 63) / 64);
+  const long long p_blocks = (long long)p.max_tiles * ((p.N + W * NT * 16 - 1) / (W * NT * 16)) * p.splits;
+  if (q_blocks + p_blocks <= 0) return;
+  gemm_stream_pair_kernel<W, NT, ROWS, PAIRS, WF_BF16, true, QDUAL>
+      <<<(unsigned)(q_blocks + p_blocks), W * 64, 0, s>>>(p, q, (int)q_blocks);
+}
+
+template <bool QDUAL>
+static void launch_pair_q(const GemmParams& p, const GemmParams& q, int rows, hipStream_t s) {
+  if (rows == 16)
+    launch_pair_rows<16, 4, QDUAL>(p, q, s);
+  else if (rows == 32)
+    launch_pair_rows<32, 2, QDUAL>(p, q, s);
+  else
+    launch_pair_rows<64, 2, QDUAL>(p, q, s);
+}
+
+void launch_gemm_stream_pair(const GemmParams& p, const GemmParams& q, hipStream_t s) {
+  // the pair covers bf16 experts with hi + lo activations and a one-segment dense
+  // bf16 GEMM of at most one 64-row tile in one split; anything else runs as two launches
+  const bool ok = p.tile_expert && p.a_lo && p.nseg == 1 && !q.tile_expert && q.nseg == 1 &&
+                  q.splits == 1 && q.M <= 64;
+  if (!ok) {
+    launch_gemm_stream(q, WF_BF16, s);
+    launch_gemm_stream(p, WF_BF16, s);
+    return;
+  }
+  const int rows = p.rows_per_tile <= 16 ? 16 : p.rows_per_tile <= 32 ? 32 : 64;
+  if (q.a_lo)
+    launch_pair_q<true>(p, q, rows, s);
+  else
+    launch_pair_q<false>(p, q, rows, s);
 }
 
 }  // namespace lmoe

@@ -74,6 +74,9 @@ struct GemmParams {
 // weight-streaming MFMA GEMM for <= 64 rows per tile (decode-like shapes); fmt is a
 // WFmt (FP8 with 64-row tiles only)
 void launch_gemm_stream(const GemmParams& p, int fmt, hipStream_t s);
+// one launch of a grouped bf16 expert GEMM p (hi + lo activations) and a dense bf16
+// GEMM q of at most 64 rows over its whole k range (q.splits == 1, q's blocks first)
+void launch_gemm_stream_pair(const GemmParams& p, const GemmParams& q, hipStream_t s);
 // grouped MFMA GEMM for 64-row expert tiles of block-scaled FP4 weights with dual
 // activations (tens of rows per expert): activations staged in LDS, weights read once
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s);

@@ -61,6 +61,8 @@ constexpr int TARGET_BLOCKS = 256;      // streaming kernel: 8-wave blocks, seve
 // the two stacked GEMMs of the decode-sized path (one block per CU at 256 blocks: the
 // blocks' load latency left HBM idle; 512 put two on each CU, -9 us per forward)
 constexpr int TARGET_BLOCKS_STACKED = 512;
+// the decode-sized up-projection alone (the shared expert's S2 ran with expert down)
+constexpr int TARGET_BLOCKS_UP = 256;
 constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 8-wave block per CU
 
 struct Plan {
@@ -198,9 +200,11 @@ size_t max_partial_floats(const latentmoe_config& c, bool linear) {
     }
     if (linear && T <= STREAM_ROWS_BIG) {  // the stacked GEMMs always leave partials
       const G lg[] = {{3 * c.n_experts + c.latent + c.shared_hidden, c.d, true},
+                      {3 * c.n_experts + c.latent, c.d, true},
                       {c.d, c.latent + c.shared_hidden, true}};
       for (const G& g : lg)
         best = std::max(best, (size_t)plan_dense(T, g.N, g.K, TARGET_BLOCKS_STACKED).splits * T * g.N);
+      best = std::max(best, (size_t)plan_dense(T, c.d, c.latent, TARGET_BLOCKS_UP).splits * T * c.d);
     }
   }
   return best;
@@ -211,7 +215,9 @@ size_t max_partial_floats(const latentmoe_config& c, bool linear) {
 // rows [router pieces; W_down; S1] (one reduce splits logits, z and h_s), and
 // y = W_up y_lat + S2 h_s is one dual GEMM over [W_up | S2] with y_lat and h_s side
 // by side in one row.  On a multi-queue graph replay every cross-queue edge left
-// the waiting queue idle for 6-12 us; this path has none.
+// the waiting queue idle for 6-12 us; this path has none.  With bf16 experts on the
+// streaming kernel, S1 and S2 instead run inside the expert-up and expert-down
+// launches, and the second stacked GEMM keeps W_up only (it adds onto the y S2 wrote).
 bool linear_formats(const latentmoe_config& c) {
   return c.shared_format == LATENTMOE_FORMAT_BF16 && c.proj_format == LATENTMOE_FORMAT_BF16;
 }
@@ -591,15 +597,18 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // its consumer.  W_down is forked at the start; the shared expert after the
   // router GEMM, so the router runs at full speed and the shared expert's
   // weight stream fills the latency-bound top-K / bucketing chain.
+  // Stage-timed calls run in program order on the caller's stream as well, so
+  // each stage's events bracket its own kernels with nothing beside them.
+  const bool one_stream = h->serial || tm.on;
   hipStream_t side = h->side;
   hipStream_t side2 = h->side2;
-  if (h->serial) side = side2 = s;  // everything in one stream, in program order (per-kernel profiling)
-  // event edges between the streams (none in serial mode: one stream)
+  if (one_stream) side = side2 = s;
+  // event edges between the streams (none on one stream)
   auto record = [&](hipEvent_t ev, hipStream_t on) {
-    if (!h->serial) (void)hipEventRecord(ev, on);
+    if (!one_stream) (void)hipEventRecord(ev, on);
   };
   auto wait = [&](hipStream_t on, hipEvent_t ev) {
-    if (!h->serial) (void)hipStreamWaitEvent(on, ev, 0);
+    if (!one_stream) (void)hipStreamWaitEvent(on, ev, 0);
   };
   auto fork_to = [&](hipStream_t to, hipEvent_t ev) {
     record(ev, s);
@@ -668,18 +677,23 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const bool linear = h->linear && T <= STREAM_ROWS_BIG;
   h->last_linear = linear;
   const int LS = L + ms;  // row length of the stacked activations [y_lat | h_s]
+  // bf16 experts on the streaming kernel: the shared expert's GEMMs run inside the
+  // expert launches (S1 with expert up, S2 with expert down) instead of in the
+  // stacked GEMMs, where a few tokens' dense GEMM is a latency-bound launch
+  const bool shared_rides = linear && !fp4 && (double)TK / N <= 48.0;
+  const int MSX = shared_rides ? 0 : ms;  // shared-hidden rows of the stacked x GEMM
   if (linear) {
-    // ---- 1. router logits, z = W_down x and the shared hidden in one GEMM over x ----
+    // ---- 1. router logits, z = W_down x (and the shared hidden) in one GEMM over x ----
     tm.start(LATENTMOE_STAGE_ROUTER);
     GemmParams px = base_params();
     px.seg[0] = GemmSeg{x, b.wx, d};
     px.nseg = 1;
     px.lda = d;
     px.ldb = d;
-    px.N = 3 * N + LS;
+    px.N = 3 * N + L + MSX;
     px.ldc = px.N;
     const int splits = run_dense(h, px, T, s, true, b.partial, WF_BF16, nullptr, TARGET_BLOCKS_STACKED);
-    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, ms, b.logits, b.z, b.z_lo, b.ay + L,
+    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, MSX, b.logits, b.z, b.z_lo, b.ay + L,
                    b.ay_lo + L, LS, s);
     tm.stop(LATENTMOE_STAGE_ROUTER);
     // stages without a launch of their own here are recorded empty
@@ -817,7 +831,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // fill part of the GPU); its expert down needs only its own expert up, so it runs
   // on side stream 2 beside the bf16 class's expert up, and the combine waits for
   // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
-  const bool hi_side = split_rows && !tm.on && !h->serial && !linear;
+  const bool hi_side = split_rows && !one_stream && !linear;
   // the bf16 class's expert-down rows go out as bf16: their rounding enters y_lat times
   // a gate below the class threshold, like that of their bf16 z and h
   const bool og_mix = split_rows;
@@ -839,6 +853,41 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     lo(pu, EPI_SQRELU_BF16, b.h);
     lo(pw, og_mix ? EPI_GATE_BF16 : EPI_GATE_F32, og_mix ? (void*)b.og16 : (void*)b.og);
     (void)hipStreamWaitEvent(s, h->ev_hi_done, 0);
+  } else if (shared_rides) {
+    // S1: h_s = relu(S1 x)^2 as bf16 hi + lo into the stacked rows [y_lat | h_s]
+    GemmParams q1 = base_params();
+    q1.seg[0] = GemmSeg{x, w.shared_w1, d};
+    q1.nseg = 1;
+    q1.lda = d;
+    q1.ldb = d;
+    q1.M = T;
+    q1.N = ms;
+    q1.splits = 1;
+    q1.k_split = d;
+    q1.epi = EPI_SQRELU_HILO;
+    q1.C = b.ay + L;
+    q1.C2 = b.ay_lo + L;
+    q1.ldc = LS;
+    // S2: y = S2 h_s (the up-projection adds onto it)
+    GemmParams q2 = base_params();
+    q2.seg[0] = GemmSeg{b.ay + L, w.shared_w2, ms};
+    q2.a_lo = b.ay_lo + L;
+    q2.nseg = 1;
+    q2.lda = LS;
+    q2.ldb = ms;
+    q2.M = T;
+    q2.N = d;
+    q2.splits = 1;
+    q2.k_split = ms;
+    q2.epi = EPI_F32;
+    q2.C = y;
+    q2.ldc = d;
+    tm.start(LATENTMOE_STAGE_EXPERT_UP);
+    launch_gemm_stream_pair(pu, q1, s);
+    tm.stop(LATENTMOE_STAGE_EXPERT_UP);
+    tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
+    launch_gemm_stream_pair(pw, q2, s);
+    tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
   } else {
     tm.start(LATENTMOE_STAGE_EXPERT_UP);
     launch_expert(pu, EPI_SQRELU_BF16, b.h);
@@ -855,19 +904,20 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
   if (linear) {
-    // ---- 8. y = [W_up | S2] [y_lat ; h_s], both as bf16 hi + lo ----
+    // ---- 8. y = [W_up | S2] [y_lat ; h_s], both as bf16 hi + lo; or, when S2 ran
+    // with expert down, y += W_up y_lat (the first L columns of the stacked rows) ----
     tm.start(LATENTMOE_STAGE_UP_PROJ);
     GemmParams pq = base_params();
-    pq.seg[0] = GemmSeg{b.ay, b.wy, LS};
+    pq.seg[0] = GemmSeg{b.ay, b.wy, shared_rides ? L : LS};
     pq.a_lo = b.ay_lo;
     pq.nseg = 1;
     pq.lda = LS;
     pq.ldb = LS;
     pq.N = d;
-    pq.epi = EPI_F32;
+    pq.epi = shared_rides ? EPI_F32_ADD : EPI_F32;
     pq.C = y;
     pq.ldc = d;
-    run_dense(h, pq, T, s, false, nullptr, WF_BF16, nullptr, TARGET_BLOCKS_STACKED);
+    run_dense(h, pq, T, s, false, nullptr, WF_BF16, nullptr, shared_rides ? TARGET_BLOCKS_UP : TARGET_BLOCKS_STACKED);
     tm.stop(LATENTMOE_STAGE_UP_PROJ);
     tm.done();
     h->last_T = T;
