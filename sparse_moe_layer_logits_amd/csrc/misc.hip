@@ -56,7 +56,17 @@ __global__ void xreduce_kernel(const float* __restrict__ partial, int splits, lo
   const float* row = partial + (long long)t * NS;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   if (c < N) {
-    for (int s = 0; s < splits; ++s) {
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {  // twelve loads in flight; the sum order is fixed
+      f32x4_t u[4][3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) u[i][j] = *reinterpret_cast<const f32x4_t*>(row + (s + i) * pstride + c + j * N);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v += u[i][0] + u[i][1] + u[i][2];
+    }
+    for (; s < splits; ++s) {
       const float* q = row + s * pstride + c;
       v += *reinterpret_cast<const f32x4_t*>(q) + *reinterpret_cast<const f32x4_t*>(q + N) +
            *reinterpret_cast<const f32x4_t*>(q + 2 * N);
@@ -65,7 +75,15 @@ __global__ void xreduce_kernel(const float* __restrict__ partial, int splits, lo
     return;
   }
   const int cc = c + 2 * N;  // partial column of z or h_s
-  for (int s = 0; s < splits; ++s) v += *reinterpret_cast<const f32x4_t*>(row + s * pstride + cc);
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {  // eight loads in flight; the sum order is fixed
+    f32x4_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = *reinterpret_cast<const f32x4_t*>(row + (s + i) * pstride + cc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += u[i];
+  }
+  for (; s < splits; ++s) v += *reinterpret_cast<const f32x4_t*>(row + s * pstride + cc);
   u32x2_t hi, lo;
   if (c < N + L) {
     epi_pack<EPI_BF16_HILO>(v, hi, lo);
@@ -137,19 +155,39 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int k = 0;
-  for (; k + 8 <= K; k += 8) {  // eight rows in flight, summed in k order
-    f32x4_t v[8];
-    u32x2_t w[8];
+  for (; k + 24 <= K; k += 24) {  // 24 rows in flight (every row of a top-22 token), summed in k order
+    f32x4_t v[24];
+    u32x2_t w[24];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 24; ++i) {
       v[i] = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k + i) : og + (long long)pos[k + i] * L + c);
       if constexpr (MIX) w[i] = *reinterpret_cast<const u32x2_t*>(p16(k + i));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 24; ++i) {
       if constexpr (MIX) v[i] += widen(w[i]);
       acc += v[i];
     }
+  }
+  if (k + 8 <= K) {  // the rest: up to 23 rows, loads first, in k order
+    f32x4_t v[23];
+    u32x2_t w[23];
+    const int r = K - k;
+#pragma unroll
+    for (int i = 0; i < 23; ++i) {
+      if (i < r) {
+        v[i] = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k + i) : og + (long long)pos[k + i] * L + c);
+        if constexpr (MIX) w[i] = *reinterpret_cast<const u32x2_t*>(p16(k + i));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 23; ++i) {
+      if (i < r) {
+        if constexpr (MIX) v[i] += widen(w[i]);
+        acc += v[i];
+      }
+    }
+    k = K;
   }
   for (; k < K; ++k) {
     f32x4_t v = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k) : og + (long long)pos[k] * L + c);

@@ -314,9 +314,9 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     int* __restrict__ offsets, int* __restrict__ tile_expert, int* __restrict__ tile_row0,
     int* __restrict__ tile_rows, int* __restrict__ n_tiles, int max_tiles, PlaceArgs pa,
     int nchunk, int* __restrict__ chunk_hi, int* __restrict__ chunk_lo) {
-  __shared__ int scan_a[1024];
-  __shared__ int scan_b[1024];
-  __shared__ int scan_c[1024];
+  __shared__ int scan_a[16];  // wave totals
+  __shared__ int scan_b[16];
+  __shared__ int scan_c[16];
   const int e = threadIdx.x;
   int run_hi = 0, run_lo = 0;
   if (e < N && nchunk > 0) {
@@ -379,30 +379,43 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
   const int run = run_hi + run_lo;
   const int nt_hi = (e < N) ? (run_hi + tile_rows_max - 1) / tile_rows_max : 0;
   const int nt_lo = (e < N) ? (run_lo + tile_rows_max - 1) / tile_rows_max : 0;
-  // inclusive scans at once (rows, hi tiles, other tiles), Hillis-Steele
-  scan_a[e] = run;
-  scan_b[e] = nt_hi;
-  if constexpr (HI) scan_c[e] = nt_lo;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int a = scan_a[e], bb = scan_b[e], c = 0;
-    if constexpr (HI) c = scan_c[e];
-    if (e >= off) {
-      a += scan_a[e - off];
-      bb += scan_b[e - off];
-      if constexpr (HI) c += scan_c[e - off];
+  // inclusive scans at once (rows, hi tiles, other tiles): inside each wave by
+  // cross-lane shifts, then the exclusive prefix of the 16 wave totals
+  const int lane = e & 63, wv = e >> 6;
+  int a = run, bb = nt_hi, cs = HI ? nt_lo : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ua = __shfl_up(a, off), ub = __shfl_up(bb, off);
+    const int uc = HI ? __shfl_up(cs, off) : 0;
+    if (lane >= off) {
+      a += ua;
+      bb += ub;
+      cs += uc;
     }
-    __syncthreads();
-    scan_a[e] = a;
-    scan_b[e] = bb;
-    if constexpr (HI) scan_c[e] = c;
-    __syncthreads();
   }
-  const int row_start = scan_a[e] - run;
-  const int total_hi = scan_b[1023];
-  const int hi_start = scan_b[e] - nt_hi;
-  const int lo_start = HI ? total_hi + scan_c[e] - nt_lo : 0;
-  const int total_lo = HI ? scan_c[1023] : 0;
+  if (lane == 63) {
+    scan_a[wv] = a;
+    scan_b[wv] = bb;
+    scan_c[wv] = cs;
+  }
+  __syncthreads();
+  int tot_a = 0, tot_b = 0, tot_c = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w == wv) {
+      a += tot_a;
+      bb += tot_b;
+      cs += tot_c;
+    }
+    tot_a += scan_a[w];
+    tot_b += scan_b[w];
+    tot_c += scan_c[w];
+  }
+  const int row_start = a - run;
+  const int total_hi = tot_b;
+  const int hi_start = bb - nt_hi;
+  const int lo_start = HI ? total_hi + cs - nt_lo : 0;
+  const int total_lo = HI ? tot_c : 0;
   if (e < N) {
     offsets[e] = row_start;
     for (int i = 0; i < nt_hi; ++i) {
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     }
   }
   if (e == 0) {
-    offsets[N] = scan_a[1023];
+    offsets[N] = tot_a;
     const int nh = min(total_hi, max_tiles);
     n_tiles[0] = nh;                                        // hi tiles: [0, n_tiles[0])
     n_tiles[1] = min(total_hi + total_lo, max_tiles) - nh;  // then n_tiles[1] others
