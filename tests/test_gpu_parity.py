@@ -137,6 +137,17 @@ def test_fp4_mid_kernel_small():
     full_check(wl, x, W, tol=3e-2)
 
 
+def test_fp4_mid_kernel_chunks():
+    # the FP4 kernel over many k stages: expert up K = 896 (seven stages of 128, not a
+    # multiple of its three register sets), N = 1536 in 8-wave blocks; expert down
+    # K = 1536 (twelve stages), N = 896 in 7-wave blocks; 30 rows per expert
+    wl = small_wl(T=240, d=256, latent=896, n_experts=32, top_k=4, expert_hidden=1536,
+                  shared_hidden=256, experts="fp4")
+    x, W = gen(wl, 16)
+    log("FP4 kernel, several chunks", wl)
+    full_check(wl, x, W, tol=3e-2)
+
+
 def test_k_equals_n():
     wl = small_wl(T=9, n_experts=16, top_k=16)
     x, W = gen(wl, 6)
@@ -371,9 +382,10 @@ def test_graph_replay_large_tiles():
 
 
 def test_stage_timing_keeps_outputs():
-    """Stage-timed forwards (latentmoe_profile_begin) keep the plain launch order on
-    the large-tile path, where untimed ones run the hi class's expert down beside
-    the other class's expert up: both give the same outputs bit for bit, and every
+    """Stage-timed forwards (latentmoe_profile_begin) run every stage in program
+    order on the caller's stream, where untimed ones fork side streams (W_down, the
+    shared expert, and on the large-tile path the hi class's expert down beside the
+    other class's expert up): both give the same outputs bit for bit, and every
     stage reports a time."""
     import torch
     wl = small_wl(T=1100, d=256, latent=64, n_experts=32, top_k=8, expert_hidden=128, shared_hidden=256)
