@@ -44,7 +44,7 @@ constexpr int TILE_ROWS = 256;           // rows per tile of the large-tile kern
 // PAIR_TAIL_FRAC of the token's gate energy sum_k g_k^2.  A row's bf16 rounding
 // reaches the latent sum scaled by its gate; an fp64 emulation of the rounding
 // points keeps the latent sum within 4e-3 of its rms with flat gates (K = 8 of
-// 32, 22 of 512, 40 of 1024: 78-98 % of rows paired) and with skewed ones (one
+// 32, 22 of 512, 40 of 1024: 90-93 % of rows paired) and with skewed ones (one
 // gate near 1: only that row paired), where a fixed gate threshold of 0.1
 // reached 1.6-1.8e-2 with flat gates.
 constexpr float PAIR_TAIL_FRAC = 1.0f / 32.0f;
