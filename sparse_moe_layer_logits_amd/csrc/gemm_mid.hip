@@ -1,9 +1,10 @@
 // Grouped MFMA GEMM for block-scaled FP4 expert weights and tiles of up to 64
 // activation rows (experts that see tens of tokens); NP activation parts: bf16
-// (1) or a bf16 hi + lo pair (2).
+// (1; the one launched: FP4 experts take bf16 activations) or a bf16 hi + lo
+// pair (2).
 //
-// Block: W waves (W = 8, 7 or 4, the largest that divides N into 64-row wave
-// slabs); wave w owns four 16-row MFMA tiles of weight rows (n0 + 64w ..)
+// Block: W waves (W = 8, 7 or 4, the largest that divides N into 32-row wave
+// slabs); wave w owns two 16-row MFMA tiles of weight rows (n0 + 32w ..)
 // against the tile's activation rows in 16-row groups (a tile of r rows runs
 // ceil(r/16) groups, no more).  The k loop runs in stages of 128.  Stage s is
 // loaded into register set s % NS, NS - 1 stages ahead: the activation stage
@@ -34,7 +35,10 @@
 namespace lmoe {
 
 constexpr int MD_ROWS = 64;                 // activation rows per tile
-constexpr int MD_NT = 4;                    // 16-row weight tiles per wave
+// 16-row weight tiles per wave: two (32 weight rows) keep a wave at 126 VGPRs, so
+// two 7- or 8-wave blocks share a CU; four (the earlier form, ~230 VGPRs, one block
+// per CU) ran 7 % slower, the activations re-read by half as many blocks
+constexpr int MD_NT = 2;
 constexpr int MD_KS = 128;                  // k per stage
 constexpr int MD_ROWB = MD_KS * 2;          // bytes of one activation row per stage and part
 constexpr int MD_PARTB = MD_ROWS * MD_ROWB; // 16 KB
@@ -64,11 +68,15 @@ template <int W, int EPI, int MT, int NP>
 __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int expert, int row0,
                                          int rows, int n0, int nbase, bool active) {
   constexpr int NTH = 64 * W;
-  constexpr int BN = 64 * W;
+  constexpr int BN = 16 * MD_NT * W;  // weight rows per block
   constexpr int XP = (MD_PIECES + NTH - 1) / NTH;
-  // register sets: three fit next to two activation pieces per thread
-  constexpr int NS = XP <= 2 ? 3 : 2;  // loads run NS - 1 stages ahead
-  constexpr int SLOTB = NP * MD_PARTB + BN * 8;  // activation parts + scales
+  // register sets: three fit next to two activation pieces per thread in 128 VGPRs
+  // with 7 waves; 8-wave blocks (one activation piece fewer per thread, but the
+  // same budget) take two
+  constexpr int NS = XP <= 2 && W < 8 ? 3 : 2;  // loads run NS - 1 stages ahead
+  // activation parts + scales: every thread stages one weight row's 8 scale bytes
+  // (rows past the block's BN are never read)
+  constexpr int SLOTB = NP * MD_PARTB + NTH * 8;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -207,15 +215,18 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
                 [&](int mt) { return mt * 16 + r16; }, acc);
 }
 
+// two slots of the activation parts and one 8-byte scale row per thread (SLOTB)
 template <int W, int NP>
 constexpr int mid_lds_bytes() {
   return 2 * (NP * MD_PARTB + 64 * W * 8);
 }
 
 template <int W, int EPI, int NP>
-__global__ __launch_bounds__(64 * W) void gemm_mid_kernel(GemmParams p) {
+// 7- and 8-wave blocks: two per CU (four waves per SIMD, 128 VGPRs); 4-wave blocks
+// (narrow N) keep 256 VGPRs
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 4) void gemm_mid_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int BN = 64 * W;
+  constexpr int BN = 16 * MD_NT * W;
   const int NQ = (p.N + BN - 1) / BN;
   const int b = blockIdx.x;
   if (b >= p.n_tiles[0] * NQ) return;
@@ -237,13 +248,13 @@ __global__ __launch_bounds__(64 * W) void gemm_mid_kernel(GemmParams p) {
 
 template <int W, int EPI, int NP>
 static void mid_launch(const GemmParams& p, hipStream_t s) {
-  const long long blocks = (long long)p.max_tiles * ((p.N + 64 * W - 1) / (64 * W));
+  const long long blocks = (long long)p.max_tiles * ((p.N + 16 * MD_NT * W - 1) / (16 * MD_NT * W));
   if (blocks <= 0) return;
   gemm_mid_kernel<W, EPI, NP><<<(unsigned)blocks, 64 * W, mid_lds_bytes<W, NP>(), s>>>(p);
 }
 
 // waves per block: the largest of 8, 7 that splits N into whole blocks, else 4
-static int mid_waves(int N) { return N % 512 == 0 ? 8 : N % 448 == 0 ? 7 : 4; }
+static int mid_waves(int N) { return N % 256 == 0 ? 8 : N % 224 == 0 ? 7 : 4; }
 
 template <int EPI, int NP>
 static void mid_launch_w(const GemmParams& p, hipStream_t s) {
@@ -257,8 +268,8 @@ static void mid_launch_w(const GemmParams& p, hipStream_t s) {
 // epilogues offered: with a hi + lo activation, relu^2 to a pair or the gated fp32
 // rows; with a bf16 activation, relu^2 to bf16 or the gated fp32 rows
 bool gemm_mid_supports(const GemmParams& p, bool fp4) {
-  const bool epi_ok = p.a_lo ? (p.epi == EPI_SQRELU_HILO || p.epi == EPI_GATE_F32)
-                             : (p.epi == EPI_SQRELU_BF16 || p.epi == EPI_GATE_F32);
+  // FP4 experts take bf16 activations (no hi + lo pair)
+  const bool epi_ok = !p.a_lo && (p.epi == EPI_SQRELU_BF16 || p.epi == EPI_GATE_F32);
   return fp4 && p.tile_expert && p.rows_per_tile <= MD_ROWS && p.nseg == 1 && epi_ok &&
          p.b_scale_sm && p.N % 64 == 0 && p.seg[0].K % MD_KS == 0 && p.seg[0].K >= MD_KS;
 }
@@ -271,9 +282,7 @@ static hipError_t mid_attr() {
 
 template <int W>
 static hipError_t mid_attr_w() {
-  hipError_t e = mid_attr<W, EPI_SQRELU_HILO, 2>();
-  if (e == hipSuccess) e = mid_attr<W, EPI_GATE_F32, 2>();
-  if (e == hipSuccess) e = mid_attr<W, EPI_SQRELU_BF16, 1>();
+  hipError_t e = mid_attr<W, EPI_SQRELU_BF16, 1>();
   if (e == hipSuccess) e = mid_attr<W, EPI_GATE_F32, 1>();
   return e;
 }
@@ -287,17 +296,10 @@ int gemm_mid_setup() {
 
 void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s) {
   (void)fp4;
-  if (p.a_lo) {
-    if (p.epi == EPI_SQRELU_HILO)
-      mid_launch_w<EPI_SQRELU_HILO, 2>(p, s);
-    else
-      mid_launch_w<EPI_GATE_F32, 2>(p, s);
-  } else {
-    if (p.epi == EPI_SQRELU_BF16)
-      mid_launch_w<EPI_SQRELU_BF16, 1>(p, s);
-    else
-      mid_launch_w<EPI_GATE_F32, 1>(p, s);
-  }
+  if (p.epi == EPI_SQRELU_BF16)
+    mid_launch_w<EPI_SQRELU_BF16, 1>(p, s);
+  else
+    mid_launch_w<EPI_GATE_F32, 1>(p, s);
 }
 
 // [E][N][K/16] -> [E][K/128][N][8]: one thread per 8-byte group

@@ -275,11 +275,10 @@ Layout make_layout(const latentmoe_config& c, Buffers& b, bool linear) {
   L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
   L.add((void**)&b.hs_hi, Tm * c.shared_hidden * 2);
   L.add((void**)&b.hs_lo, Tm * c.shared_hidden * 2);
-  if (c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16 && c.latent % 128 == 0 &&
-      c.expert_hidden % 128 == 0) {
-    const size_t sc_bytes = N * (size_t)c.expert_hidden * (c.latent / 16);  // same for both
-    L.add((void**)&b.w1_scale_sm, sc_bytes);
-    L.add((void**)&b.w2_scale_sm, sc_bytes);
+  if (c.expert_format == LATENTMOE_EXPERTS_FP4_E2M1_E4M3_B16) {  // the mid kernel's K is a multiple of 128
+    const size_t sc_bytes = N * (size_t)c.expert_hidden * (c.latent / 16);  // either matrix
+    if (c.latent % 128 == 0) L.add((void**)&b.w1_scale_sm, sc_bytes);
+    if (c.expert_hidden % 128 == 0) L.add((void**)&b.w2_scale_sm, sc_bytes);
   }
   if (c.max_tokens > STREAM_ROWS_BIG) {  // some dense GEMMs run on the LDS-tiled kernel
     if (c.shared_format != LATENTMOE_FORMAT_BF16) {
@@ -524,12 +523,12 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
       return LATENTMOE_ERR_HIP;
     }
   }
-  if (h->b.w1_scale_sm) {
+  if (h->b.w1_scale_sm)
     launch_scale_stage_major(w->expert_w1_scale, h->b.w1_scale_sm, cfg->n_experts,
                              cfg->expert_hidden, cfg->latent, stream);
+  if (h->b.w2_scale_sm)
     launch_scale_stage_major(w->expert_w2_scale, h->b.w2_scale_sm, cfg->n_experts, cfg->latent,
                              cfg->expert_hidden, stream);
-  }
   const long long n_shared = (long long)cfg->shared_hidden * cfg->d;  // elements per matrix
   const long long n_proj = (long long)cfg->latent * cfg->d;
   if (h->b.s1_bf16) {

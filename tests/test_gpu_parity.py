@@ -128,12 +128,22 @@ def test_rows32_stream_path():
 
 def test_fp4_mid_kernel_small():
     # FP4 experts, 24 < rows per expert <= 48: the LDS-staged FP4 kernel; up-proj
-    # N = 512 runs 8-wave blocks, down-proj N = 128 4-wave blocks with two waves
-    # past N; K = 128 is a single stage
+    # N = 512 runs two 8-wave blocks of 256 rows, down-proj N = 128 one 4-wave
+    # block; K = 128 is a single stage
     wl = small_wl(T=240, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=512,
                   shared_hidden=256, experts="fp4")
     x, W = gen(wl, 15)
     log("FP4 mid kernel", wl)
+    full_check(wl, x, W, tol=3e-2)
+
+
+def test_fp4_mid_kernel_waves_past_n():
+    # down-proj N = latent = 192 in 4-wave blocks of 128 rows: the second block has
+    # two waves past N (they stage activations and skip their products); K = 512
+    wl = small_wl(T=240, d=256, latent=192, n_experts=32, top_k=4, expert_hidden=512,
+                  shared_hidden=256, experts="fp4")
+    x, W = gen(wl, 17)
+    log("FP4 kernel, waves past N", wl)
     full_check(wl, x, W, tol=3e-2)
 
 
