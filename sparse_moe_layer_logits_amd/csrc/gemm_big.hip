@@ -5,7 +5,11 @@
 // 16x16x32 tiles (128 fp32 accumulators per lane), two waves per SIMD so that
 // one wave's LDS reads and waits overlap the other's MFMAs (one wave per SIMD
 // with 128 x 128 wave tiles ran 11 % slower at prefill).  Per k step a wave
-// reads 12 (16 in dual mode) 16-byte fragments for 32 (64) MFMAs.
+// reads 12 (16 in dual mode) 16-byte fragments for 32 (64) MFMAs.  A wave's 64
+// activation rows are the 16-row groups wm, wm + 4, wm + 8, wm + 12 of the tile:
+// in a partly filled expert tile the groups past its rows are skipped (no reads,
+// no MFMAs), and the interleave spreads them evenly over the four SIMDs (at the
+// Zipf-routed prefill this cut the expert GEMMs by 2-4 %).
 //
 // Operand tiles go from global memory straight into a ring of STAGES LDS
 // buffers (global_load_lds, 16 bytes per lane, no staging registers): while
@@ -109,12 +113,11 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
   constexpr int SE = ADD ? EPI_F32_ADD : EPI;  // the kind whose values are staged
   constexpr int BATCH = ADD ? 4 : PER;
   static_assert(PER % BATCH == 0, "whole batches");
-  const int wrow = wm * (BG_MB * 16);      // first tile row of this wave
   const float ts = epi_tscale(p, expert);
   float rf[BG_MB];
 #pragma unroll
   for (int b = 0; b < BG_MB; ++b) {
-    const int m = wrow + b * 16 + r16;
+    const int m = (4 * b + wm) * 16 + r16;  // the wave's 16-row group b
     rf[b] = m < rows ? epi_rowf<EPI>(p, row0 + m) : 1.0f;
   }
   epi_wait_all();
@@ -139,20 +142,19 @@ __device__ __forceinline__ void big_epilogue(const GemmParams& p, uint8_t* smem,
 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    if (wrow / HR == half) {
+    // group 4b + wm lies in half b / 2 (wm < 4): every wave stages in both halves
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const int col = wn * 128 + a * 16 + 4 * g;
+    for (int a = 0; a < 8; ++a) {
+      const int col = wn * 128 + a * 16 + 4 * g;
 #pragma unroll
-        for (int b = 0; b < BG_MB; ++b) {
-          const int r = wrow % HR + b * 16 + r16;
-          if constexpr (EB == 4) {
-            *reinterpret_cast<f32x4_t*>(smem + r * RB + (((col >> 2) ^ (r & 7)) << 4)) = sf[a][b];
-          } else {
-            const int at = r * RB + (((col >> 3) ^ (r & 7)) << 4) + ((col >> 2) & 1) * 8;
-            *reinterpret_cast<u32x2_t*>(smem + at) = sb[0][a][b];
-            if constexpr (PL == 2) *reinterpret_cast<u32x2_t*>(smem + PLANEB + at) = sb[PL - 1][a][b];
-          }
+      for (int b = 2 * half; b < 2 * half + 2; ++b) {
+        const int r = (4 * (b % 2) + wm) * 16 + r16;
+        if constexpr (EB == 4) {
+          *reinterpret_cast<f32x4_t*>(smem + r * RB + (((col >> 2) ^ (r & 7)) << 4)) = sf[a][b];
+        } else {
+          const int at = r * RB + (((col >> 3) ^ (r & 7)) << 4) + ((col >> 2) & 1) * 8;
+          *reinterpret_cast<u32x2_t*>(smem + at) = sb[0][a][b];
+          if constexpr (PL == 2) *reinterpret_cast<u32x2_t*>(smem + PLANEB + at) = sb[PL - 1][a][b];
         }
       }
     }
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS chunk bases stay scalar
-  const int wn = wave & 1, wm = wave >> 1;  // 128 weight rows x BG_MB * 16 activation rows
+  const int wn = wave & 1, wm = wave >> 1;  // 128 weight rows x the groups 4b + wm
   const int r16 = lane & 15, g = lane >> 4;
 
   const int NQ = (p.N + BG_BN - 1) / BG_BN;
@@ -353,32 +355,11 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int b = 0; b < BG_MB; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // a step's fragments: activation part 0, the weights, then part 1, so that part
-  // 0's MFMAs can start while the rest arrive
-  auto read_frags = [&](int kt, u32x4_t (&wf)[8], u32x4_t (&xf)[NPART][BG_MB]) {
-    const uint8_t* base = smem + (kt % STAGES) * STAGEB;
-#pragma unroll
-    for (int b = 0; b < BG_MB; ++b)
-      xf[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off(wm * (BG_MB * 16) + b * 16 + r16, g));
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-      wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int b = 0; b < BG_MB; ++b)
-        xf[1][b] = *reinterpret_cast<const u32x4_t*>(base + 2 * BG_TILEB +
-                                                     bg_off(wm * (BG_MB * 16) + b * 16 + r16, g));
-    }
-  };
-  auto mfmas = [&](const u32x4_t (&wf)[8], const u32x4_t (&xf)[NPART][BG_MB]) {
-#pragma unroll
-    for (int part = 0; part < NPART; ++part)
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[part][b], acc[a][b]);
-  };
 
+  // Wave (wn, wm) multiplies the tile's 16-row activation groups 4b + wm: a partly
+  // filled tile's empty groups fall evenly on the four SIMDs, and only the groups
+  // that hold rows (the wave's first nb) are read and multiplied (wave-uniform).
+  const int nb = min(BG_MB, max(0, (((rows + 15) >> 4) - wm + 3) >> 2));
   if constexpr (!DUAL) {
     // Next step's fragments are read while this step's MFMAs run: after step
     // kt + 1's barrier the wave reads that step's activation fragments into a
@@ -395,8 +376,18 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       if (s < KT) issue(s);
     wait_vmcnt((min(STAGES, KT) - 1) * LOADS);
     asm volatile("s_barrier" ::: "memory");
+    auto single = [&](auto nbc) {
+    constexpr int NB = decltype(nbc)::value;
     u32x4_t wf[8], xa[1][BG_MB], xb[1][BG_MB];
-    read_frags(0, wf, xa);
+    {
+      const uint8_t* base = smem;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        xa[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
+#pragma unroll
+      for (int a = 0; a < 8; ++a)
+        if constexpr (NB > 0) wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
+    }
     // a step with a next one; every such step has the same shape, so the compiler's
     // wait insertion sees the current set complete (the explicit wait) and the next
     // set's reads as the only ones outstanding.  The last step runs on its own.
@@ -415,13 +406,13 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       asm volatile("s_barrier" ::: "memory");
       const uint8_t* base = smem + ((kt + 1) % STAGES) * STAGEB;
 #pragma unroll
-      for (int b = 0; b < BG_MB; ++b)
-        xn[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off(wm * (BG_MB * 16) + b * 16 + r16, g));
+      for (int b = 0; b < NB; ++b)
+        xn[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
 #pragma unroll
-        for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xc[0][b], acc[a][b]);
-        wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
+        for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xc[0][b], acc[a][b]);
+        if constexpr (NB > 0) wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
         // stage kt + STAGES (into the slot every wave finished reading before this
         // step's barrier), its loads spread over the step: issued together after
         // the barrier, all waves' loads queue at the memory unit at once and each
@@ -430,12 +421,14 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
         for (int u = a * LOADS / 8; u < (a + 1) * LOADS / 8; ++u)
           if (FAST || kt + STAGES < KT) issue_one(kt + STAGES, u);
       }
-      // keep the interleave: the activation reads, then 4 MFMAs and one read per a
-      __builtin_amdgcn_sched_group_barrier(0x100, BG_MB, 0);
+      // keep the interleave: the activation reads, then NB MFMAs and one read per a
+      if constexpr (NB > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        __builtin_amdgcn_sched_group_barrier(0x008, BG_MB, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int a = 0; a < 8; ++a) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
     };
     const std::integral_constant<bool, true> fast{};
@@ -452,9 +445,20 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     if (kt + 1 < KT) {  // two steps left: one more with a next step, ending in xb
       step(kt, xa, xb, checked);
 #pragma unroll
-      for (int b = 0; b < BG_MB; ++b) xa[0][b] = xb[0][b];
+      for (int b = 0; b < NB; ++b) xa[0][b] = xb[0][b];
     }
-    mfmas(wf, xa);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xa[0][b], acc[a][b]);
+    };
+    switch (nb) {
+      case 4: single(std::integral_constant<int, 4>{}); break;
+      case 3: single(std::integral_constant<int, 3>{}); break;
+      case 2: single(std::integral_constant<int, 2>{}); break;
+      case 1: single(std::integral_constant<int, 1>{}); break;
+      default: single(std::integral_constant<int, 0>{}); break;
+    }
   } else {
     // all of a step's fragments are read before its first MFMA (the scheduler would
     // otherwise reuse one register for the weight fragments and wait for each read
@@ -464,6 +468,8 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       if (s < KT) issue(s);
     // FAST: a steady-state step (kt + STAGES - 1 < KT): STAGES - 2 later stages are in
     // flight (a compile-time wait) and stage kt + STAGES - 1 exists
+    auto dual = [&](auto nbc) {
+    constexpr int NB = decltype(nbc)::value;
     auto dstep = [&](int kt, auto fast) {
       constexpr bool FAST = decltype(fast)::value;
       // stages issued after step kt: min(STAGES - 2, KT - 1 - kt)
@@ -474,8 +480,21 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
       // a plain barrier: the step's own loads were waited for above; a fenced
       // __syncthreads would wait for every load in flight, draining the ring
       asm volatile("s_barrier" ::: "memory");
+      // activation part 0, the weights, then part 1, so that part 0's MFMAs can
+      // start while the rest arrive
       u32x4_t wf[8], xf[NPART][BG_MB];
-      read_frags(kt, wf, xf);
+      {
+        const uint8_t* base = smem + (kt % STAGES) * STAGEB;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          xf[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+          if constexpr (NB > 0) wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          xf[1][b] = *reinterpret_cast<const u32x4_t*>(base + 2 * BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
+      }
       __builtin_amdgcn_sched_barrier(0);
       // stage kt + STAGES - 1 goes to the slot every wave finished reading before
       // this barrier; its loads are spread over the MFMAs (see the pipelined path)
@@ -485,7 +504,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
 #pragma unroll
-          for (int b = 0; b < BG_MB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[part][b], acc[a][b]);
+          for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xf[part][b], acc[a][b]);
           const int grp = part * 8 + a;
 #pragma unroll
           for (int u = grp * LOADS / (8 * NPART); u < (grp + 1) * LOADS / (8 * NPART); ++u)
@@ -495,6 +514,14 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     int kt = 0;
     for (; kt + STAGES - 1 < KT; ++kt) dstep(kt, std::integral_constant<bool, true>{});
     for (; kt < KT; ++kt) dstep(kt, std::integral_constant<bool, false>{});
+    };
+    switch (nb) {
+      case 4: dual(std::integral_constant<int, 4>{}); break;
+      case 3: dual(std::integral_constant<int, 3>{}); break;
+      case 2: dual(std::integral_constant<int, 2>{}); break;
+      case 1: dual(std::integral_constant<int, 1>{}); break;
+      default: dual(std::integral_constant<int, 0>{}); break;
+    }
   }
 
   big_epilogue<EPI>(p, smem, acc, expert, split, row0, rows, n0, wn, wm, r16, g, tid);
