@@ -123,11 +123,9 @@ void launch_place(const int* idx, const float* gates, const uint32_t* masks,
                   const int* prefix_hi, const int* prefix_lo, int T, int N, int K, int* row_src,
                   float* row_gate, int* inv, const int* chunk_hi, const int* chunk_lo, hipStream_t s);
 // y_lat[t] = sum_k og[inv[t*K+k]] (fixed k order) -> bf16 hi + bf16 lo (rows of stride
-// ldy).  With og16, rows with paired[t*K+k] == 0 are read from og16 (bf16) instead;
-// z32 / z16 are zero rows of L elements.
-void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
-                    const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
-                    uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s);
+// ldy).  With og16, rows with paired[t*K+k] == 0 are read from og16 (bf16) instead.
+void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired, const int* inv, int T,
+                    int K, int L, uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s);
 // split-K partials [splits][T][3N + L + MS] of the GEMM over x with the stacked rows
 // [router pieces 1-3; W_down; S1] -> fp32 logits [T, N] (the three piece columns
 // summed), z (bf16 hi + lo, [T, L]) and h_s = relu(.)^2 (bf16 hi + lo, rows of stride ldh)

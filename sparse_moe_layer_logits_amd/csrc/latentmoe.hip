@@ -124,8 +124,6 @@ struct Buffers {
   uint16_t* h_lo = nullptr;
   float* og = nullptr;
   uint16_t* og16 = nullptr;  // bf16-class expert-down rows (large-tile path, two row classes)
-  float* zrow32 = nullptr;   // zero rows of `latent` elements (fp32, bf16) for the combine
-  uint16_t* zrow16 = nullptr;
   uint16_t* y_lat = nullptr;
   uint16_t* y_lat_lo = nullptr;
   uint16_t* hs_hi = nullptr;
@@ -268,9 +266,7 @@ Layout make_layout(const latentmoe_config& c, Buffers& b, bool linear) {
   L.add((void**)&b.h, TK * c.expert_hidden * 2);
   L.add((void**)&b.h_lo, TK * c.expert_hidden * 2);
   L.add((void**)&b.og, TK * c.latent * 4);
-  L.add((void**)&b.og16, TK * c.latent * 2);
-  L.add((void**)&b.zrow32, (size_t)c.latent * 4);
-  L.add((void**)&b.zrow16, (size_t)c.latent * 2);
+  L.add((void**)&b.og16, TK * c.latent * 2 + 16);  // + the combine's 16-byte reads past the last row
   L.add((void**)&b.y_lat, Tm * c.latent * 2);
   L.add((void**)&b.y_lat_lo, Tm * c.latent * 2);
   L.add((void**)&b.hs_hi, Tm * c.shared_hidden * 2);
@@ -501,12 +497,6 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
     return LATENTMOE_ERR_HIP;
   }
   launch_router_split(w->router_w, h->b.pieces, (long long)cfg->n_experts * cfg->d, stream);
-  if (hipMemsetAsync(h->b.zrow32, 0, (size_t)cfg->latent * 4, stream) != hipSuccess ||
-      hipMemsetAsync(h->b.zrow16, 0, (size_t)cfg->latent * 2, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    latentmoe_destroy(h);
-    return LATENTMOE_ERR_HIP;
-  }
   if (h->linear) {
     // stacked copies: wx rows [3N, 3N + l) = W_down, then S1; wy = [W_up | S2] row by row
     const size_t N = cfg->n_experts, d = cfg->d, l = cfg->latent, ms = cfg->shared_hidden;
@@ -898,8 +888,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);
-  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.paired, b.zrow32, b.zrow16, b.inv,
-                 T, K, L, linear ? b.ay : b.y_lat, linear ? b.ay_lo : b.y_lat_lo, linear ? LS : L, s);
+  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.paired, b.inv, T, K, L, linear ? b.ay : b.y_lat,
+                 linear ? b.ay_lo : b.y_lat_lo, linear ? LS : L, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
   if (linear) {
@@ -1160,10 +1150,8 @@ extern "C" int latentmoe_forward_static(const latentmoe_config* cfg, const laten
   }
   (void)hipGetLastError();
   // what the handle path derives once at init, here on every call: the router's
-  // split weights and the combine's zero rows
+  // split weights
   launch_router_split(w->router_w, h.b.pieces, (long long)cfg->n_experts * cfg->d, stream);
-  launch_zero(h.b.zrow32, (size_t)cfg->latent * 4, stream);
-  launch_zero(h.b.zrow16, (size_t)cfg->latent * 2, stream);
   forward_impl(&h, x, T, y, topk_idx, topk_gate, stream, false);
   return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }

@@ -121,16 +121,14 @@ void launch_xreduce(const float* partial, int splits, long long pstride, int T, 
 // up-projection sees it to about 16 significant bits.
 //
 // MIX (large-tile path with two row classes): a row of the bf16 class (paired = 0)
-// was written to og16 as bf16, the others to og as fp32.  Every k
-// loads one fp32 and one bf16 row, one of them the zero row z32 / z16, and adds
-// both: the sum and its order are those of a single format, and a bf16-class row
-// costs half the bytes from memory (the zero rows stay cached).
+// was written to og16 as bf16, the others to og as fp32.  A row costs one 16-byte
+// load per thread from its own format's row (the first 8 bytes of a bf16 row's load
+// are the thread's 4 values, widened exactly before the add; og16 has 16 bytes of
+// slack past its last row): no branches, so the compiler keeps all loads in flight.
 template <bool MIX>
 __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ og,
                                                      const uint16_t* __restrict__ og16,
                                                      const uint8_t* __restrict__ paired,
-                                                     const float* __restrict__ z32,
-                                                     const uint16_t* __restrict__ z16,
                                                      const int* __restrict__ inv, int K, int L,
                                                      uint16_t* __restrict__ y_lat,
                                                      uint16_t* __restrict__ y_lat_lo, int ldy) {
@@ -145,55 +143,40 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   __syncthreads();
   const int c = (blockIdx.y * 64 + threadIdx.x) * 4;
   if (c >= L) return;
-  // row k's two sources, formed from the global arguments (addresses kept in LDS
-  // would be generic and turn the loads into flat ones)
-  auto p32 = [&](int k) { return wide[k] ? og + (long long)pos[k] * L + c : z32 + c; };
-  auto p16 = [&](int k) { return wide[k] ? z16 + c : og16 + (long long)pos[k] * L + c; };
-  auto widen = [](const u32x2_t& w) {
-    return f32x4_t{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+  // row k as four fp32 values (bf16 rows: 4 bf16 in words 0-1, widened at the add)
+  auto load = [&](int k) {
+    const long long off = (long long)pos[k] * L + c;
+    if (!MIX) return *reinterpret_cast<const u32x4_t*>(og + off);
+    const uint8_t* src = wide[k] ? reinterpret_cast<const uint8_t*>(og + off)
+                                 : reinterpret_cast<const uint8_t*>(og16 + off);
+    return *reinterpret_cast<const u32x4_t*>(src);
+  };
+  auto value = [&](int k, const u32x4_t& v) {
+    const f32x4_t bf = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                        __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+    return !MIX || wide[k] ? __builtin_bit_cast(f32x4_t, v) : bf;
   };
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int k = 0;
   for (; k + 24 <= K; k += 24) {  // 24 rows in flight (every row of a top-22 token), summed in k order
-    f32x4_t v[24];
-    u32x2_t w[24];
+    u32x4_t v[24];
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      v[i] = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k + i) : og + (long long)pos[k + i] * L + c);
-      if constexpr (MIX) w[i] = *reinterpret_cast<const u32x2_t*>(p16(k + i));
-    }
+    for (int i = 0; i < 24; ++i) v[i] = load(k + i);
 #pragma unroll
-    for (int i = 0; i < 24; ++i) {
-      if constexpr (MIX) v[i] += widen(w[i]);
-      acc += v[i];
-    }
+    for (int i = 0; i < 24; ++i) acc += value(k + i, v[i]);
   }
   if (k + 8 <= K) {  // the rest: up to 23 rows, loads first, in k order
-    f32x4_t v[23];
-    u32x2_t w[23];
+    u32x4_t v[23];
     const int r = K - k;
 #pragma unroll
-    for (int i = 0; i < 23; ++i) {
-      if (i < r) {
-        v[i] = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k + i) : og + (long long)pos[k + i] * L + c);
-        if constexpr (MIX) w[i] = *reinterpret_cast<const u32x2_t*>(p16(k + i));
-      }
-    }
+    for (int i = 0; i < 23; ++i)
+      if (i < r) v[i] = load(k + i);
 #pragma unroll
-    for (int i = 0; i < 23; ++i) {
-      if (i < r) {
-        if constexpr (MIX) v[i] += widen(w[i]);
-        acc += v[i];
-      }
-    }
+    for (int i = 0; i < 23; ++i)
+      if (i < r) acc += value(k + i, v[i]);
     k = K;
   }
-  for (; k < K; ++k) {
-    f32x4_t v = *reinterpret_cast<const f32x4_t*>(MIX ? p32(k) : og + (long long)pos[k] * L + c);
-    if constexpr (MIX) v += widen(*reinterpret_cast<const u32x2_t*>(p16(k)));
-    acc += v;
-  }
+  for (; k < K; ++k) acc += value(k, load(k));
   float hi[4], lo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -204,16 +187,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   store_bf16x4(y_lat_lo, (long long)t * ldy + c, lo[0], lo[1], lo[2], lo[3]);
 }
 
-void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired,
-                    const float* z32, const uint16_t* z16, const int* inv, int T, int K, int L,
-                    uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s) {
+void launch_combine(const float* og, const uint16_t* og16, const uint8_t* paired, const int* inv, int T,
+                    int K, int L, uint16_t* y_lat, uint16_t* y_lat_lo, int ldy, hipStream_t s) {
   if (T <= 0) return;
   dim3 grid(T, (L / 4 + 63) / 64);
   if (og16)
-    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, paired, z32, z16, inv, K, L, y_lat, y_lat_lo, ldy);
+    combine_kernel<true><<<grid, 64, 0, s>>>(og, og16, paired, inv, K, L, y_lat, y_lat_lo, ldy);
   else
-    combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, nullptr, nullptr, inv, K, L, y_lat,
-                                              y_lat_lo, ldy);
+    combine_kernel<false><<<grid, 64, 0, s>>>(og, nullptr, nullptr, inv, K, L, y_lat, y_lat_lo, ldy);
 }
 
 // zero n 32-bit words (a kernel rather than a memset node, so that a captured
