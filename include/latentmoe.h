@@ -70,10 +70,12 @@ extern "C" {
 typedef struct latentmoe_handle_s* latentmoe_handle_t;
 
 /* Layer shape (host struct).  Requirements, checked by latentmoe_init:
- * d, latent, expert_hidden, shared_hidden multiples of 64; n_experts a
- * multiple of 16 and at most 1024; 1 <= top_k <= min(n_experts, 64);
- * max_tokens >= 1; the activation matrices the kernels address with 32-bit
- * offsets stay below 2^31 elements: max_tokens * top_k * max(latent,
+ * d, latent, expert_hidden, shared_hidden multiples of 16 (the FP4 block; the
+ * kernels run widths in multiples of 64, and other widths run zero-padded to
+ * the next multiple of 64, see latentmoe_init); n_experts a multiple of 16 and
+ * at most 1024; 1 <= top_k <= min(n_experts, 64); max_tokens >= 1; the
+ * activation matrices the kernels address with 32-bit offsets stay below 2^31
+ * elements at the widths the kernels run: max_tokens * top_k * max(latent,
  * expert_hidden) and max_tokens * max(d, shared_hidden) (at the Super shapes,
  * d = 4096, l = 1024, m = 2688, m_s = 5376, K = 22: max_tokens <= 36314). */
 typedef struct {
@@ -90,7 +92,10 @@ typedef struct {
 } latentmoe_config;
 
 /* Weights (host struct holding device pointers).  The library BORROWS every
- * buffer: it must stay allocated and unchanged until latentmoe_destroy.
+ * buffer: it must stay allocated and unchanged until latentmoe_destroy (with a
+ * width that is not a multiple of 64, init copies the matrices and reads the
+ * caller's matrices only during the call; the bias and the per-tensor scales
+ * stay borrowed).
  * Alignment: every pointer 16-byte aligned. */
 typedef struct {
   const float* router_w;          /* [N, d] fp32                                  */
@@ -134,7 +139,15 @@ typedef struct {
  * 64 tokens, which run on `stream` alone.  Larger forwards fork two side
  * streams of the default priority from `stream` (W_down; the shared expert);
  * LATENTMOE_SERIAL=1 in the environment at init keeps every stage of this
- * handle on `stream` in program order (per-kernel profiling). */
+ * handle on `stream` in program order (per-kernel profiling).
+ * Widths that are not multiples of 64 (d, latent, expert_hidden or
+ * shared_hidden): init allocates zero-padded copies of every weight matrix at
+ * the widths rounded up to 64 (D, L, M, M_s; device memory owned by the handle,
+ * about the weights' size again; the padded rows and columns add exact zeros,
+ * so the layer's results are those of the caller's widths) and a [max_tokens, D]
+ * bf16 and a [max_tokens, D] fp32 buffer, and makes the copies on `stream`;
+ * each forward then also copies x into the first buffer and crops y out of the
+ * second (two kernels on the forward's stream). */
 int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
                    latentmoe_handle_t* out);
 
@@ -177,14 +190,16 @@ int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, 
  * first call on a device looks up that device's address of the array
  * (hipGetSymbolAddress, not a stream operation) and sets kernel attributes.
  *   cfg, w     host pointers, read during the call; every format must be
- *              FORMAT_BF16 (the FP4 / FP8 paths need derived copies larger
- *              than the array); cfg->max_tokens bounds T
+ *              FORMAT_BF16 and every width a multiple of 64 (the FP4 / FP8
+ *              paths and the padded widths need derived copies larger than
+ *              the array); cfg->max_tokens bounds T
  *   x, T, y, topk_idx, topk_gate, stream: as latentmoe_forward
  * All calls on one GPU share its array and the array keeps the last call's
  * contents: calls that overlap on one GPU (two streams, two threads) race and
  * must not be made.  Errors (before anything is enqueued): INVALID_ARG (null
  * pointers, T < 0, T > cfg->max_tokens), UNSUPPORTED (shape checks of
- * latentmoe_init, a format other than bf16), SCRATCH (the workspace for T
+ * latentmoe_init, a format other than bf16, a width that is not a multiple of
+ * 64), SCRATCH (the workspace for T
  * tokens exceeds LATENTMOE_STATIC_SCRATCH_BYTES), HIP. */
 #define LATENTMOE_STATIC_SCRATCH_BYTES (64u << 20)
 int latentmoe_forward_static(const latentmoe_config* cfg, const latentmoe_weights* w,
@@ -199,12 +214,14 @@ int latentmoe_destroy(latentmoe_handle_t h);
 const char* latentmoe_status_string(int status);
 
 /* Bytes of device workspace latentmoe_init would allocate for cfg (host
- * pointers).  Errors as latentmoe_init's shape checks. */
+ * pointers), including the padded copies of widths that are not multiples of
+ * 64.  Errors as latentmoe_init's shape checks. */
 int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes);
 
 /* Intermediates of the last forward on this handle, for tests and tools.
  * Copies `bytes` bytes of intermediate `which` into device buffer dst on
- * `stream` (asynchronous).  Layouts for the last call's T:
+ * `stream` (asynchronous).  Layouts for the last call's T, at the caller's
+ * widths (padded widths are cropped):
  *   LATENTMOE_INTER_Z        [T, l] bf16       latent tokens W_down x
  *   LATENTMOE_INTER_Y_LAT    [T, l] bf16       gated expert sum (latent), high part
  *   LATENTMOE_INTER_Y_LAT_LO [T, l] bf16       gated expert sum, remainder

@@ -138,6 +138,10 @@ void launch_fp4_dequant(const uint8_t* codes, const uint8_t* scales, long long n
                         uint16_t* out, hipStream_t s);
 // zero `bytes` bytes (a multiple of 4) at device address p with a kernel
 void launch_zero(void* p, size_t bytes, hipStream_t s);
+// dst[sl][i][j] = src[sl srows + i][j] for i < rows, j < cols, else 0 (bytes; dst rows of
+// dpitch bytes, drows rows per slice; src rows of spitch bytes, srows rows per slice)
+void launch_pad_copy(const void* src, size_t spitch, int srows, void* dst, size_t dpitch, int drows,
+                     long long slices, int rows, size_t cols, hipStream_t s);
 // groups of 16 E4M3 bytes -> exact bf16 with the in-register decoder (tensor scale not applied)
 void launch_fp8_dequant(const uint8_t* codes, long long n_groups16, uint16_t* out, hipStream_t s);
 

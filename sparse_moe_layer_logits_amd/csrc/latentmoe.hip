@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -164,15 +165,19 @@ int check_config(const latentmoe_config* c) {
     return LATENTMOE_ERR_UNSUPPORTED;
   if (c->proj_format != LATENTMOE_FORMAT_BF16 && c->proj_format != LATENTMOE_FORMAT_FP8_E4M3)
     return LATENTMOE_ERR_UNSUPPORTED;
-  if (c->d % 64 || c->latent % 64 || c->expert_hidden % 64 || c->shared_hidden % 64)
+  // the FP4 block (16 elements along the input width) and the kernels' 16-row tiles;
+  // widths that are not multiples of 64 run zero-padded to the next one
+  if (c->d % 16 || c->latent % 16 || c->expert_hidden % 16 || c->shared_hidden % 16)
     return LATENTMOE_ERR_UNSUPPORTED;
   if (c->n_experts % 16 || c->n_experts > 1024) return LATENTMOE_ERR_UNSUPPORTED;
   if (c->top_k > c->n_experts || c->top_k > 64) return LATENTMOE_ERR_UNSUPPORTED;
   // the large-tile and FP4 kernels address activation rows with 32-bit byte offsets
-  // (bf16 elements): h [T K, m], the gathered z [T, l], x [T, d], h_s [T, m_s]
+  // (bf16 elements): h [T K, m], the gathered z [T, l], x [T, d], h_s [T, m_s] (at
+  // the widths the kernels run: rounded up to multiples of 64)
   const long long lim = 1ll << 31;
-  if ((long long)c->max_tokens * c->top_k * std::max(c->latent, c->expert_hidden) >= lim ||
-      (long long)c->max_tokens * std::max(c->d, c->shared_hidden) >= lim)
+  auto r64 = [](int v) { return (long long)(v + 63) / 64 * 64; };
+  if ((long long)c->max_tokens * c->top_k * std::max(r64(c->latent), r64(c->expert_hidden)) >= lim ||
+      (long long)c->max_tokens * std::max(r64(c->d), r64(c->shared_hidden)) >= lim)
     return LATENTMOE_ERR_UNSUPPORTED;
   return LATENTMOE_OK;
 }
@@ -218,6 +223,107 @@ size_t max_partial_floats(const latentmoe_config& c, bool linear) {
 // launches, and the second stacked GEMM keeps W_up only (it adds onto the y S2 wrote).
 bool linear_formats(const latentmoe_config& c) {
   return c.shared_format == LATENTMOE_FORMAT_BF16 && c.proj_format == LATENTMOE_FORMAT_BF16;
+}
+
+// ---- widths that are multiples of 16 but not of 64 ----
+// The kernels take d, l, m, m_s in multiples of 64.  Other widths run at the widths
+// rounded up to 64: init copies every weight into zero-padded matrices (the padded
+// rows and columns add exact zeros to every product, so z, h, h_s, y_lat and the
+// logits keep their values and the padded columns of each activation are zero);
+// each forward copies x into a zero-padded [T, D] buffer and crops y out of a
+// [T, D] one.
+int round64(int v) { return (v + 63) / 64 * 64; }
+
+bool needs_pad(const latentmoe_config& c) {
+  return c.d % 64 || c.latent % 64 || c.expert_hidden % 64 || c.shared_hidden % 64;
+}
+
+latentmoe_config padded_config(const latentmoe_config& c) {
+  latentmoe_config p = c;
+  p.d = round64(c.d);
+  p.latent = round64(c.latent);
+  p.expert_hidden = round64(c.expert_hidden);
+  p.shared_hidden = round64(c.shared_hidden);
+  return p;
+}
+
+// One allocation: every weight matrix at the padded widths, then x_pad [max_tokens, D]
+// bf16 and y_pad [max_tokens, D] fp32.  A matrix is `slices` slices of rows x cols
+// elements of num/den bytes (FP4 codes 1/2, block scales 1/16) padded to prows x pcols.
+struct PadPlan {
+  struct Item {
+    const void* src;
+    size_t field;  // offset of the matrix's pointer in latentmoe_weights
+    long long slices;
+    int rows, prows;
+    size_t row_bytes, prow_bytes;
+  };
+  std::vector<Item> items;
+  size_t total = 0;
+  size_t x_off = 0, y_off = 0;
+  latentmoe_weights w{};  // the padded matrices (pointers set by place_pad_plan)
+
+  void add(const void* src, size_t field, long long slices, int rows, int cols, int prows, int pcols,
+           int num, int den) {
+    Item it{src, field, slices, rows, prows, (size_t)cols * num / den, (size_t)pcols * num / den};
+    items.push_back(it);
+    total += (slices * (size_t)prows * it.prow_bytes + 255) & ~size_t(255);
+  }
+};
+
+// the padded copies of cfg's weights (w may be null: sizes only)
+PadPlan make_pad_plan(const latentmoe_config& c, const latentmoe_weights* w) {
+  static const latentmoe_weights none{};
+  const latentmoe_weights& s = w ? *w : none;
+  const latentmoe_config p = padded_config(c);
+  PadPlan P;
+  P.w = s;
+  const int N = c.n_experts;
+  const int d = c.d, l = c.latent, m = c.expert_hidden, ms = c.shared_hidden;
+  const int D = p.d, L = p.latent, M = p.expert_hidden, MS = p.shared_hidden;
+  const bool fp4 = c.expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
+  const bool sfp4 = c.shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
+  const int pe = c.proj_format == LATENTMOE_FORMAT_FP8_E4M3 ? 1 : 2;  // projection bytes per element
+#define LMOE_F(name) offsetof(latentmoe_weights, name)
+  P.add(s.router_w, LMOE_F(router_w), 1, N, d, N, D, 4, 1);
+  P.add(s.w_down, LMOE_F(w_down), 1, l, d, L, D, pe, 1);
+  P.add(s.w_up, LMOE_F(w_up), 1, d, l, D, L, pe, 1);
+  if (fp4) {  // codes (two per byte) and block scales (one per 16 input elements)
+    P.add(s.expert_w1, LMOE_F(expert_w1), N, m, l, M, L, 1, 2);
+    P.add(s.expert_w2, LMOE_F(expert_w2), N, l, m, L, M, 1, 2);
+    P.add(s.expert_w1_scale, LMOE_F(expert_w1_scale), N, m, l, M, L, 1, 16);
+    P.add(s.expert_w2_scale, LMOE_F(expert_w2_scale), N, l, m, L, M, 1, 16);
+  } else {
+    P.add(s.expert_w1, LMOE_F(expert_w1), N, m, l, M, L, 2, 1);
+    P.add(s.expert_w2, LMOE_F(expert_w2), N, l, m, L, M, 2, 1);
+  }
+  if (sfp4) {
+    P.add(s.shared_w1, LMOE_F(shared_w1), 1, ms, d, MS, D, 1, 2);
+    P.add(s.shared_w2, LMOE_F(shared_w2), 1, d, ms, D, MS, 1, 2);
+    P.add(s.shared_w1_scale, LMOE_F(shared_w1_scale), 1, ms, d, MS, D, 1, 16);
+    P.add(s.shared_w2_scale, LMOE_F(shared_w2_scale), 1, d, ms, D, MS, 1, 16);
+  } else {
+    P.add(s.shared_w1, LMOE_F(shared_w1), 1, ms, d, MS, D, 2, 1);
+    P.add(s.shared_w2, LMOE_F(shared_w2), 1, d, ms, D, MS, 2, 1);
+  }
+#undef LMOE_F
+  P.x_off = P.total;
+  P.total += ((size_t)c.max_tokens * p.d * 2 + 255) & ~size_t(255);
+  P.y_off = P.total;
+  P.total += ((size_t)c.max_tokens * p.d * 4 + 255) & ~size_t(255);
+  return P;
+}
+
+// points the plan's matrices into buf and enqueues the padded copies on s
+void place_pad_plan(PadPlan& P, char* buf, hipStream_t s) {
+  size_t at = 0;
+  for (const PadPlan::Item& it : P.items) {
+    const void* q = buf + at;
+    std::memcpy(reinterpret_cast<char*>(&P.w) + it.field, &q, sizeof(q));
+    launch_pad_copy(it.src, it.row_bytes, it.rows, buf + at, it.prow_bytes, it.prows, it.slices, it.rows,
+                    it.row_bytes, s);
+    at += (it.slices * (size_t)it.prows * it.prow_bytes + 255) & ~size_t(255);
+  }
 }
 
 // linear: lay out the stacked weights and rows of the decode-sized single-stream forward
@@ -303,8 +409,13 @@ struct GraphKey {
 };
 
 struct latentmoe_handle_s {
-  latentmoe_config cfg;
+  latentmoe_config cfg;  // the widths the kernels run (rounded up to multiples of 64)
   latentmoe_weights w;
+  latentmoe_config ucfg;  // the caller's widths
+  // widths that are not multiples of 64: the padded weights, x_pad and y_pad
+  void* pad_buf = nullptr;
+  uint16_t* x_pad = nullptr;
+  float* y_pad = nullptr;
   Buffers b;
   void* workspace = nullptr;
   size_t workspace_bytes = 0;
@@ -425,16 +536,23 @@ int latentmoe_workspace_bytes(const latentmoe_config* cfg, size_t* bytes) {
   if (st != LATENTMOE_OK) return st;
   if (!bytes) return LATENTMOE_ERR_INVALID_ARG;
   Buffers b;
-  *bytes = make_layout(*cfg, b, linear_formats(*cfg)).total;
+  if (needs_pad(*cfg)) {
+    const latentmoe_config p = padded_config(*cfg);
+    *bytes = make_layout(p, b, linear_formats(p)).total + make_pad_plan(*cfg, nullptr).total;
+  } else {
+    *bytes = make_layout(*cfg, b, linear_formats(*cfg)).total;
+  }
   return LATENTMOE_OK;
 }
 
-int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
-                   latentmoe_handle_t* out) {
-  if (!out) return LATENTMOE_ERR_INVALID_ARG;
-  *out = nullptr;
-  int st = check_config(cfg);
-  if (st != LATENTMOE_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// the handle for widths that are multiples of 64 (cfg and w are what the kernels run)
+int init_handle(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
+                latentmoe_handle_t* out) {
+  int st = LATENTMOE_OK;
   if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
       !w->shared_w1 || !w->shared_w2)
     return LATENTMOE_ERR_INVALID_ARG;
@@ -541,6 +659,57 @@ int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipS
   return LATENTMOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int latentmoe_init(const latentmoe_config* cfg, const latentmoe_weights* w, hipStream_t stream,
+                   latentmoe_handle_t* out) {
+  if (!out) return LATENTMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  int st = check_config(cfg);
+  if (st != LATENTMOE_OK) return st;
+  if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
+      !w->shared_w1 || !w->shared_w2)
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (cfg->expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 &&
+      (!w->expert_w1_scale || !w->expert_w2_scale || !w->expert_w1_tscale || !w->expert_w2_tscale))
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (cfg->shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 &&
+      (!w->shared_w1_scale || !w->shared_w2_scale || !w->shared_w1_tscale || !w->shared_w2_tscale))
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (cfg->proj_format == LATENTMOE_FORMAT_FP8_E4M3 && (!w->w_down_tscale || !w->w_up_tscale))
+    return LATENTMOE_ERR_INVALID_ARG;
+  if (!needs_pad(*cfg)) {
+    st = init_handle(cfg, w, stream, out);
+    if (st == LATENTMOE_OK) (*out)->ucfg = *cfg;
+    return st;
+  }
+  // zero-padded copies of the weights (enqueued on `stream`, which init_handle
+  // synchronises before it returns), then the handle at the padded widths
+  PadPlan P = make_pad_plan(*cfg, w);
+  const char* fail = std::getenv("LATENTMOE_FAIL_ALLOC");
+  void* buf = nullptr;
+  if ((fail && fail[0] == '1') || hipMalloc(&buf, P.total) != hipSuccess) {
+    (void)hipGetLastError();
+    return LATENTMOE_ERR_OUT_OF_MEMORY;
+  }
+  place_pad_plan(P, static_cast<char*>(buf), stream);
+  const latentmoe_config pc = padded_config(*cfg);
+  st = init_handle(&pc, &P.w, stream, out);
+  if (st != LATENTMOE_OK) {
+    (void)hipStreamSynchronize(stream);
+    (void)hipFree(buf);
+    return st;
+  }
+  latentmoe_handle_s* h = *out;
+  h->ucfg = *cfg;
+  h->pad_buf = buf;
+  h->x_pad = reinterpret_cast<uint16_t*>(static_cast<char*>(buf) + P.x_off);
+  h->y_pad = reinterpret_cast<float*>(static_cast<char*>(buf) + P.y_off);
+  return LATENTMOE_OK;
+}
+
 int latentmoe_destroy(latentmoe_handle_t h) {
   if (!h) return LATENTMOE_OK;
   for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
@@ -555,6 +724,7 @@ int latentmoe_destroy(latentmoe_handle_t h) {
   drop_graph(h);
   if (h->cap) (void)hipStreamDestroy(h->cap);
   hipError_t e = h->workspace ? hipFree(h->workspace) : hipSuccess;
+  if (h->pad_buf && hipFree(h->pad_buf) != hipSuccess) e = hipErrorUnknown;
   delete h;
   return e == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }
@@ -940,6 +1110,20 @@ int check_forward_args(latentmoe_handle_t h, const uint16_t* x, int32_t T, float
   return 1;  // proceed
 }
 
+// the forward at the caller's widths: padded widths copy x into x_pad (zeros past
+// d) and crop y out of y_pad around the forward
+void forward_outer(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, int32_t* topk_idx,
+                   float* topk_gate, hipStream_t s, bool eager) {
+  if (!h->pad_buf) {
+    forward_impl(h, x, T, y, topk_idx, topk_gate, s, eager);
+    return;
+  }
+  const size_t d = h->ucfg.d, D = h->cfg.d;
+  launch_pad_copy(x, d * 2, T, h->x_pad, D * 2, T, 1, T, d * 2, s);
+  forward_impl(h, h->x_pad, T, h->y_pad, topk_idx, topk_gate, s, eager);
+  launch_pad_copy(h->y_pad, D * 4, T, y, d * 4, T, 1, T, d * 4, s);
+}
+
 void drop_graph(latentmoe_handle_s* h) {
   if (h->gexec) (void)hipGraphExecDestroy(h->gexec);
   if (h->graph) (void)hipGraphDestroy(h->graph);
@@ -956,7 +1140,7 @@ int latentmoe_forward(latentmoe_handle_t h, const uint16_t* x, int32_t T, float*
   const int st = check_forward_args(h, x, T, y);
   if (st != 1) return st;
   (void)hipGetLastError();
-  forward_impl(h, x, T, y, topk_idx, topk_gate, s, true);
+  forward_outer(h, x, T, y, topk_idx, topk_gate, s, true);
   return hipGetLastError() == hipSuccess ? LATENTMOE_OK : LATENTMOE_ERR_HIP;
 }
 
@@ -970,7 +1154,7 @@ int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, 
     drop_graph(h);
     if (hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal) != hipSuccess)
       return LATENTMOE_ERR_HIP;
-    forward_impl(h, x, T, y, topk_idx, topk_gate, h->cap, false);
+    forward_outer(h, x, T, y, topk_idx, topk_gate, h->cap, false);
     hipGraph_t g = nullptr;
     if (hipStreamEndCapture(h->cap, &g) != hipSuccess || !g) {
       (void)hipGetLastError();
@@ -992,46 +1176,51 @@ int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, 
 int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t bytes,
                          hipStream_t s) {
   if (!h || !dst) return LATENTMOE_ERR_INVALID_ARG;
-  const latentmoe_config& c = h->cfg;
+  const latentmoe_config& c = h->cfg;   // the widths the buffers have
+  const latentmoe_config& u = h->ucfg;  // the caller's widths (the copies' rows)
   const size_t T = h->last_T, K = c.top_k;
+  // rows of w bytes, `pitch` bytes apart in the buffer (decode-sized forwards keep
+  // y_lat and h_s side by side in rows of l + m_s)
+  const size_t LS = (size_t)(c.latent + c.shared_hidden) * 2;
+  const bool lin = h->last_linear;
   const void* src = nullptr;
-  size_t have = 0;
+  size_t w = 0, pitch = 0, rows = 1;
   switch (which) {
-    case LATENTMOE_INTER_Z: src = h->b.z; have = T * c.latent * 2; break;
-    case LATENTMOE_INTER_Y_LAT: src = h->b.y_lat; have = T * c.latent * 2; break;
-    case LATENTMOE_INTER_COUNTS: src = h->b.counts; have = (size_t)c.n_experts * 4; break;
-    case LATENTMOE_INTER_OFFSETS: src = h->b.offsets; have = (size_t)(c.n_experts + 1) * 4; break;
-    case LATENTMOE_INTER_ROW_SRC: src = h->b.row_src; have = T * K * 4; break;
-    case LATENTMOE_INTER_INV: src = h->b.inv; have = T * K * 4; break;
-    case LATENTMOE_INTER_H: src = h->b.h; have = T * K * c.expert_hidden * 2; break;
-    case LATENTMOE_INTER_HS_HI: src = h->b.hs_hi; have = T * c.shared_hidden * 2; break;
-    case LATENTMOE_INTER_HS_LO: src = h->b.hs_lo; have = T * c.shared_hidden * 2; break;
-    case LATENTMOE_INTER_Y_LAT_LO: src = h->b.y_lat_lo; have = T * c.latent * 2; break;
-    case LATENTMOE_INTER_Z_LO: src = h->b.z_lo; have = T * c.latent * 2; break;
-    case LATENTMOE_INTER_H_LO: src = h->b.h_lo; have = T * K * c.expert_hidden * 2; break;
-    case LATENTMOE_INTER_PAIRED: src = h->b.paired; have = T * K; break;
+    case LATENTMOE_INTER_Z: src = h->b.z; w = u.latent * 2; pitch = c.latent * 2; rows = T; break;
+    case LATENTMOE_INTER_Z_LO: src = h->b.z_lo; w = u.latent * 2; pitch = c.latent * 2; rows = T; break;
+    case LATENTMOE_INTER_Y_LAT:
+      src = lin ? (const void*)h->b.ay : h->b.y_lat; w = u.latent * 2; pitch = lin ? LS : c.latent * 2; rows = T;
+      break;
+    case LATENTMOE_INTER_Y_LAT_LO:
+      src = lin ? (const void*)h->b.ay_lo : h->b.y_lat_lo; w = u.latent * 2; pitch = lin ? LS : c.latent * 2;
+      rows = T;
+      break;
+    case LATENTMOE_INTER_HS_HI:
+      src = lin ? (const void*)(h->b.ay + c.latent) : h->b.hs_hi; w = u.shared_hidden * 2;
+      pitch = lin ? LS : c.shared_hidden * 2; rows = T;
+      break;
+    case LATENTMOE_INTER_HS_LO:
+      src = lin ? (const void*)(h->b.ay_lo + c.latent) : h->b.hs_lo; w = u.shared_hidden * 2;
+      pitch = lin ? LS : c.shared_hidden * 2; rows = T;
+      break;
+    case LATENTMOE_INTER_H: src = h->b.h; w = u.expert_hidden * 2; pitch = c.expert_hidden * 2; rows = T * K; break;
+    case LATENTMOE_INTER_H_LO: src = h->b.h_lo; w = u.expert_hidden * 2; pitch = c.expert_hidden * 2; rows = T * K; break;
+    case LATENTMOE_INTER_COUNTS: src = h->b.counts; w = pitch = (size_t)c.n_experts * 4; break;
+    case LATENTMOE_INTER_OFFSETS: src = h->b.offsets; w = pitch = (size_t)(c.n_experts + 1) * 4; break;
+    case LATENTMOE_INTER_ROW_SRC: src = h->b.row_src; w = pitch = T * K * 4; break;
+    case LATENTMOE_INTER_INV: src = h->b.inv; w = pitch = T * K * 4; break;
+    case LATENTMOE_INTER_PAIRED: src = h->b.paired; w = pitch = T * K; break;
     default: return LATENTMOE_ERR_INVALID_ARG;
   }
-  if (bytes > have) return LATENTMOE_ERR_INVALID_ARG;
+  if (bytes > w * rows) return LATENTMOE_ERR_INVALID_ARG;
   if (bytes == 0) return LATENTMOE_OK;
-  if (h->last_linear && (which == LATENTMOE_INTER_Y_LAT || which == LATENTMOE_INTER_Y_LAT_LO ||
-                         which == LATENTMOE_INTER_HS_HI || which == LATENTMOE_INTER_HS_LO)) {
-    // decode-sized forwards keep y_lat and h_s side by side in rows of l + m_s
-    const bool lo = which == LATENTMOE_INTER_Y_LAT_LO || which == LATENTMOE_INTER_HS_LO;
-    const bool hs = which == LATENTMOE_INTER_HS_HI || which == LATENTMOE_INTER_HS_LO;
-    const size_t w = (hs ? c.shared_hidden : c.latent) * 2, pitch = (size_t)(c.latent + c.shared_hidden) * 2;
-    const uint16_t* base = (lo ? h->b.ay_lo : h->b.ay) + (hs ? c.latent : 0);
-    const size_t rows = bytes / w, rest = bytes % w;
-    if (rows && hipMemcpy2DAsync(dst, w, base, pitch, w, rows, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return LATENTMOE_ERR_HIP;
-    if (rest && hipMemcpyAsync(static_cast<char*>(dst) + rows * w, reinterpret_cast<const char*>(base) + rows * pitch,
-                               rest, hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return LATENTMOE_ERR_HIP;
-    return LATENTMOE_OK;
-  }
-  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess
-             ? LATENTMOE_OK
-             : LATENTMOE_ERR_HIP;
+  const size_t full = bytes / w, rest = bytes % w;
+  if (full && hipMemcpy2DAsync(dst, w, src, pitch, w, full, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return LATENTMOE_ERR_HIP;
+  if (rest && hipMemcpyAsync(static_cast<char*>(dst) + full * w, static_cast<const char*>(src) + full * pitch,
+                             rest, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return LATENTMOE_ERR_HIP;
+  return LATENTMOE_OK;
 }
 
 int latentmoe_profile_begin(latentmoe_handle_t h, int max_calls, uint32_t stage_mask) {
@@ -1125,7 +1314,7 @@ extern "C" int latentmoe_forward_static(const latentmoe_config* cfg, const laten
   int st = check_config(cfg);
   if (st != LATENTMOE_OK) return st;
   if (cfg->expert_format != LATENTMOE_FORMAT_BF16 || cfg->shared_format != LATENTMOE_FORMAT_BF16 ||
-      cfg->proj_format != LATENTMOE_FORMAT_BF16)
+      cfg->proj_format != LATENTMOE_FORMAT_BF16 || needs_pad(*cfg))
     return LATENTMOE_ERR_UNSUPPORTED;
   if (!w || !w->router_w || !w->w_down || !w->w_up || !w->expert_w1 || !w->expert_w2 ||
       !w->shared_w1 || !w->shared_w2 || T < 0)

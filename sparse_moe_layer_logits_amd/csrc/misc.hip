@@ -5,6 +5,8 @@
 #include "fp8.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace lmoe {
 
 // out[row, n..n+3] = epilogue(sum over splits of partial[s, row, n..n+3])
@@ -242,6 +244,41 @@ __global__ void fp8_dequant_kernel(const uint8_t* __restrict__ codes, long long 
 void launch_fp8_dequant(const uint8_t* codes, long long n_groups16, uint16_t* out, hipStream_t s) {
   if (n_groups16 <= 0) return;
   fp8_dequant_kernel<<<(unsigned)((n_groups16 + 255) / 256), 256, 0, s>>>(codes, n_groups16, out);
+}
+
+// Strided copy with zero fill, in units of U bytes: dst has `slices` slices of
+// drows rows of dcols units; element (s, i, j) is src[(s srows + i) spitch + j] when
+// i < rows and j < cols, else 0.  Widths that are not multiples of 64 run on
+// zero-padded copies (weights once, tokens per call), and the output is cropped.
+template <typename U>
+__global__ void pad_copy_kernel(const U* __restrict__ src, long long spitch, int srows, U* __restrict__ dst,
+                                long long dcols, int drows, int rows, long long cols, long long total) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const long long j = i % dcols;
+    const long long r = i / dcols;
+    const int row = (int)(r % drows);
+    const long long sl = r / drows;
+    dst[i] = row < rows && j < cols ? src[(sl * srows + row) * spitch + j] : U(0);
+  }
+}
+
+void launch_pad_copy(const void* src, size_t spitch, int srows, void* dst, size_t dpitch, int drows,
+                     long long slices, int rows, size_t cols, hipStream_t s) {
+  const bool words = spitch % 4 == 0 && dpitch % 4 == 0 && cols % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(src) % 4 == 0 && reinterpret_cast<uintptr_t>(dst) % 4 == 0;
+  const size_t u = words ? 4 : 1;
+  const long long total = slices * (long long)drows * (long long)(dpitch / u);
+  if (total <= 0) return;
+  const unsigned blocks = (unsigned)std::min<long long>((total + 255) / 256, 65536);
+  if (words)
+    pad_copy_kernel<uint32_t><<<blocks, 256, 0, s>>>(static_cast<const uint32_t*>(src), (long long)(spitch / 4),
+                                                     srows, static_cast<uint32_t*>(dst), (long long)(dpitch / 4),
+                                                     drows, rows, (long long)(cols / 4), total);
+  else
+    pad_copy_kernel<uint8_t><<<blocks, 256, 0, s>>>(static_cast<const uint8_t*>(src), (long long)spitch, srows,
+                                                    static_cast<uint8_t*>(dst), (long long)dpitch, drows, rows,
+                                                    (long long)cols, total);
 }
 
 }  // namespace lmoe

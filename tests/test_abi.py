@@ -69,7 +69,8 @@ def test_status_strings_and_host_side_validation(lib):
     cfg = binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 0)
     n = binding.latentmoe_workspace_bytes(cfg)
     assert n > 0
-    bad = [binding.latentmoe_config(250, 64, 16, 4, 128, 256, 8, 0),   # d not a multiple of 64
+    bad = [binding.latentmoe_config(250, 64, 16, 4, 128, 256, 8, 0),   # d not a multiple of 16
+           binding.latentmoe_config(256, 72, 16, 4, 128, 256, 8, 0),   # l not a multiple of 16
            binding.latentmoe_config(256, 64, 16, 17, 128, 256, 8, 0),  # K > N
            binding.latentmoe_config(256, 64, 20, 4, 128, 256, 8, 0),   # N not a multiple of 16
            binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 7)]   # unknown format
@@ -88,6 +89,25 @@ def test_status_strings_and_host_side_validation(lib):
     # forward / destroy on a null handle
     assert lib.latentmoe_forward(None, None, 1, None, None, None, None) == binding.LATENTMOE_ERR_INVALID_ARG
     assert lib.latentmoe_destroy(None) == 0
+
+
+def test_widths_multiple_of_16_run_padded(lib):
+    """Widths that are multiples of 16 but not of 64 are accepted: the layer runs
+    at the widths rounded up to 64, on zero-padded copies of the weights plus a
+    padded x and y buffer, so its workspace is that of the rounded widths and
+    more.  The entry point that allocates nothing has no room for the copies and
+    rejects such widths before any device work."""
+    odd = binding.latentmoe_config(208, 80, 16, 4, 112, 144, 8, 0)
+    rounded = binding.latentmoe_config(256, 128, 16, 4, 128, 192, 8, 0)
+    assert binding.latentmoe_workspace_bytes(odd) > binding.latentmoe_workspace_bytes(rounded)
+    fp4 = binding.latentmoe_config(208, 80, 16, 4, 112, 144, 8, 1)
+    assert binding.latentmoe_workspace_bytes(fp4) > 0
+    w = binding.latentmoe_weights()
+    for name in ("router_w", "w_down", "w_up", "expert_w1", "expert_w2", "shared_w1", "shared_w2"):
+        setattr(w, name, 4096)   # non-null; never dereferenced: the shape check comes first
+    with pytest.raises(binding.LatentMoEError) as e:
+        binding.latentmoe_forward_static(odd, w, 4096, 1, 4096, 0, 0, 0)
+    assert e.value.status == binding.LATENTMOE_ERR_UNSUPPORTED
 
 
 def test_32bit_activation_offsets_bound():

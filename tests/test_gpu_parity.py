@@ -363,6 +363,34 @@ def test_graph_replay_matches_eager_and_oracle():
     layer.close()
 
 
+@pytest.mark.parametrize("T,experts,shared,proj", [
+    (37, "bf16", "bf16", "bf16"),   # decode-sized path: one stream, stacked GEMMs
+    (600, "bf16", "bf16", "bf16"),  # large-tile path: > 64 tokens, > 48 rows per expert, two row classes
+    (40, "fp4", "fp4", "fp8"),      # the released precision mix on the streaming kernels
+    (300, "fp4", "fp4", "fp8"),     # the mix above 64 tokens: LDS-staged FP4 expert kernel
+])
+def test_widths_multiple_of_16(T, experts, shared, proj):
+    """d, l, m, m_s multiples of 16 (the FP4 block) but not of 64: the layer runs on
+    zero-padded weight copies at the widths rounded up to 64 and crops y; z, y_lat
+    and the bucketing come back at the caller's widths and match the oracle run at
+    the caller's widths.  Graph replay (the padding and cropping copies captured
+    with the forward) equals the eager forward bit for bit."""
+    import torch
+    wl = small_wl(T=T, d=208, latent=80, n_experts=32, top_k=4, expert_hidden=112, shared_hidden=144,
+                  experts=experts, shared=shared, proj=proj)
+    x, W = gen(wl, 21)
+    log("padded widths", wl)
+    full_check(wl, x, W, tol=tolerance(wl))
+    Wd = binding.upload_weights(W)
+    layer = binding.LatentMoE(wl, Wd, max_tokens=wl.T)
+    xd = binding.to_device(x)
+    ye, ie, ge = layer.forward(xd)
+    yg, ig, gg = layer.forward(xd, graph=True)
+    torch.cuda.synchronize()
+    assert torch.equal(yg, ye) and torch.equal(ig, ie) and torch.equal(gg, ge)
+    layer.close()
+
+
 def test_graph_replay_large_tiles():
     """The large-tile path with two row classes in a graph (the hi class's expert
     down runs on a side stream beside the other class's expert up): every replay
