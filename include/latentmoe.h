@@ -73,7 +73,7 @@ typedef struct latentmoe_handle_s* latentmoe_handle_t;
  * d, latent, expert_hidden, shared_hidden multiples of 16 (the FP4 block; the
  * kernels run widths in multiples of 64, and other widths run zero-padded to
  * the next multiple of 64, see latentmoe_init); n_experts a multiple of 16 and
- * at most 1024; 1 <= top_k <= min(n_experts, 64); max_tokens >= 1; the
+ * at most 4096; 1 <= top_k <= min(n_experts, 64); max_tokens >= 1; the
  * activation matrices the kernels address with 32-bit offsets stay below 2^31
  * elements at the widths the kernels run: max_tokens * top_k * max(latent,
  * expert_hidden) and max_tokens * max(d, shared_hidden) (at the Super shapes,

@@ -169,7 +169,7 @@ int check_config(const latentmoe_config* c) {
   // widths that are not multiples of 64 run zero-padded to the next one
   if (c->d % 16 || c->latent % 16 || c->expert_hidden % 16 || c->shared_hidden % 16)
     return LATENTMOE_ERR_UNSUPPORTED;
-  if (c->n_experts % 16 || c->n_experts > 1024) return LATENTMOE_ERR_UNSUPPORTED;
+  if (c->n_experts % 16 || c->n_experts > 4096) return LATENTMOE_ERR_UNSUPPORTED;
   if (c->top_k > c->n_experts || c->top_k > 64) return LATENTMOE_ERR_UNSUPPORTED;
   // the large-tile and FP4 kernels address activation rows with 32-bit byte offsets
   // (bf16 elements): h [T K, m], the gathered z [T, l], x [T, d], h_s [T, m_s] (at

@@ -83,8 +83,8 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __re
                                                     uint32_t* __restrict__ masks, float tail_frac,
                                                     uint32_t* __restrict__ masks_hi,
                                                     uint8_t* __restrict__ paired_out) {
-  __shared__ uint32_t smask[1024];
-  __shared__ uint32_t smask_hi[1024];
+  __shared__ uint32_t smask[SLOTS * 64];
+  __shared__ uint32_t smask_hi[SLOTS * 64];
   __shared__ unsigned long long cand[TOPK_WAVES][64];
   __shared__ float esq[TOPK_WAVES][64];
   const int lane = threadIdx.x & 63;
@@ -193,12 +193,19 @@ void launch_topk(const float* logits, const float* bias, int T, int N, int K, in
                  hipStream_t s) {
   // whole mask groups: every byte of every group's words is written
   const int blocks = (T + TOPK_TOKENS_PER_BLOCK - 1) / TOPK_TOKENS_PER_BLOCK * (TOPK_TOKENS_PER_BLOCK / TOPK_WAVES);
+  // each lane holds N / 64 keys (rounded up to 8, 16, 32 or 64)
+  auto go = [&](auto slots) {
+    topk_kernel<decltype(slots)::value><<<blocks, 64 * TOPK_WAVES, 0, s>>>(
+        logits, bias, T, N, K, idx, gates, masks, tail_frac, masks_hi, paired);
+  };
   if (N <= 512)
-    topk_kernel<8><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, tail_frac,
-                                                      masks_hi, paired);
+    go(std::integral_constant<int, 8>{});
+  else if (N <= 1024)
+    go(std::integral_constant<int, 16>{});
+  else if (N <= 2048)
+    go(std::integral_constant<int, 32>{});
   else
-    topk_kernel<16><<<blocks, 64 * TOPK_WAVES, 0, s>>>(logits, bias, T, N, K, idx, gates, masks, tail_frac,
-                                                       masks_hi, paired);
+    go(std::integral_constant<int, 64>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -307,8 +314,9 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(BucketMasks bm, int n
 }
 
 // nchunk > 0: the prefixes inside chunks and the chunk counts are in place (from
-// bucket_count_kernel); the counts become exclusive chunk offsets here
-template <bool HI>
+// bucket_count_kernel); the counts become exclusive chunk offsets here.  Thread t
+// owns the EPT experts t EPT .. t EPT + EPT - 1 (N <= 1024 EPT).
+template <bool HI, int EPT>
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     BucketMasks bm, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ tile_expert, int* __restrict__ tile_row0,
@@ -317,71 +325,84 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
   __shared__ int scan_a[16];  // wave totals
   __shared__ int scan_b[16];
   __shared__ int scan_c[16];
-  const int e = threadIdx.x;
-  int run_hi = 0, run_lo = 0;
-  if (e < N && nchunk > 0) {
-    for (int c0 = 0; c0 < nchunk; c0 += 16) {  // 16 chunk counts in flight
-      int ch[16], cl[16];
+  const int tid = threadIdx.x;
+  // rows of each of this thread's experts in the two classes
+  int rh[EPT], rl[EPT];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        ch[u] = cl[u] = 0;
-        if (c0 + u < nchunk) {
-          ch[u] = chunk_hi[(long long)(c0 + u) * N + e];
-          if constexpr (HI) cl[u] = chunk_lo[(long long)(c0 + u) * N + e];
+  for (int x = 0; x < EPT; ++x) {
+    const int e = tid * EPT + x;
+    int run_hi = 0, run_lo = 0;
+    if (e < N && nchunk > 0) {
+      for (int c0 = 0; c0 < nchunk; c0 += 16) {  // 16 chunk counts in flight
+        int ch[16], cl[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          ch[u] = cl[u] = 0;
+          if (c0 + u < nchunk) {
+            ch[u] = chunk_hi[(long long)(c0 + u) * N + e];
+            if constexpr (HI) cl[u] = chunk_lo[(long long)(c0 + u) * N + e];
+          }
         }
-      }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (c0 + u < nchunk) {
-          chunk_hi[(long long)(c0 + u) * N + e] = run_hi;
-          run_hi += ch[u];
-          if constexpr (HI) {
-            chunk_lo[(long long)(c0 + u) * N + e] = run_lo;
-            run_lo += cl[u];
+        for (int u = 0; u < 16; ++u) {
+          if (c0 + u < nchunk) {
+            chunk_hi[(long long)(c0 + u) * N + e] = run_hi;
+            run_hi += ch[u];
+            if constexpr (HI) {
+              chunk_lo[(long long)(c0 + u) * N + e] = run_lo;
+              run_lo += cl[u];
+            }
           }
         }
       }
+    } else if (e < N) {
+      // U blocks of masks in flight per step (16, then 4, then 1): the loads do
+      // not wait on the prefix
+      int b = 0;
+      auto steps = [&](auto UC, int b_end) {
+        constexpr int U = decltype(UC)::value;
+        for (; b + U <= b_end; b += U) {
+          uint32_t m[U], mh[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            m[u] = mask16(bm.all[(long long)(b + u) * N + e]);
+            if constexpr (HI) mh[u] = mask16(bm.hi[(long long)(b + u) * N + e]);
+            else mh[u] = m[u];
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const long long be = (long long)(b + u) * N + e;
+            bm.prefix_hi[be] = run_hi;
+            run_hi += __popc(mh[u]);
+            if constexpr (HI) {
+              bm.prefix_lo[be] = run_lo;
+              run_lo += __popc(m[u] & ~mh[u]);
+            }
+          }
+        }
+      };
+      steps(std::integral_constant<int, 16>{}, nblk);
+      steps(std::integral_constant<int, 4>{}, nblk);
+      steps(std::integral_constant<int, 1>{}, nblk);
     }
-    if constexpr (HI) bm.counts_hi[e] = run_hi;
-    counts[e] = run_hi + run_lo;
-  } else if (e < N) {
-    // U blocks of masks in flight per step (16, then 4, then 1): the loads do
-    // not wait on the prefix
-    int b = 0;
-    auto steps = [&](auto UC, int b_end) {
-      constexpr int U = decltype(UC)::value;
-      for (; b + U <= b_end; b += U) {
-        uint32_t m[U], mh[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          m[u] = mask16(bm.all[(long long)(b + u) * N + e]);
-          if constexpr (HI) mh[u] = mask16(bm.hi[(long long)(b + u) * N + e]);
-          else mh[u] = m[u];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const long long be = (long long)(b + u) * N + e;
-          bm.prefix_hi[be] = run_hi;
-          run_hi += __popc(mh[u]);
-          if constexpr (HI) {
-            bm.prefix_lo[be] = run_lo;
-            run_lo += __popc(m[u] & ~mh[u]);
-          }
-        }
-      }
-    };
-    steps(std::integral_constant<int, 16>{}, nblk);
-    steps(std::integral_constant<int, 4>{}, nblk);
-    steps(std::integral_constant<int, 1>{}, nblk);
-    if constexpr (HI) bm.counts_hi[e] = run_hi;
-    counts[e] = run_hi + run_lo;
+    if (e < N) {
+      if constexpr (HI) bm.counts_hi[e] = run_hi;
+      counts[e] = run_hi + run_lo;
+    }
+    rh[x] = run_hi;
+    rl[x] = run_lo;
   }
-  const int run = run_hi + run_lo;
-  const int nt_hi = (e < N) ? (run_hi + tile_rows_max - 1) / tile_rows_max : 0;
-  const int nt_lo = (e < N) ? (run_lo + tile_rows_max - 1) / tile_rows_max : 0;
+  // this thread's totals: rows, hi tiles, other tiles
+  int run = 0, nt_hi = 0, nt_lo = 0;
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    run += rh[x] + rl[x];
+    nt_hi += (rh[x] + tile_rows_max - 1) / tile_rows_max;
+    nt_lo += (rl[x] + tile_rows_max - 1) / tile_rows_max;
+  }
   // inclusive scans at once (rows, hi tiles, other tiles): inside each wave by
   // cross-lane shifts, then the exclusive prefix of the 16 wave totals
-  const int lane = e & 63, wv = e >> 6;
+  const int lane = tid & 63, wv = tid >> 6;
   int a = run, bb = nt_hi, cs = HI ? nt_lo : 0;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -411,14 +432,21 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     tot_b += scan_b[w];
     tot_c += scan_c[w];
   }
-  const int row_start = a - run;
   const int total_hi = tot_b;
-  const int hi_start = bb - nt_hi;
-  const int lo_start = HI ? total_hi + cs - nt_lo : 0;
   const int total_lo = HI ? tot_c : 0;
-  if (e < N) {
+  // this thread's first row, hi tile and other tile; then its experts in order
+  int row_start = a - run;
+  int hi_start = bb - nt_hi;
+  int lo_start = HI ? total_hi + cs - nt_lo : 0;
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int e = tid * EPT + x;
+    if (e >= N) break;
+    const int run_hi = rh[x], run_lo = rl[x];
+    const int eh = (run_hi + tile_rows_max - 1) / tile_rows_max;
+    const int el = (run_lo + tile_rows_max - 1) / tile_rows_max;
     offsets[e] = row_start;
-    for (int i = 0; i < nt_hi; ++i) {
+    for (int i = 0; i < eh; ++i) {
       const int j = hi_start + i;
       if (j < max_tiles) {
         tile_expert[j] = e;
@@ -426,7 +454,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
         tile_rows[j] = min(tile_rows_max, run_hi - i * tile_rows_max);
       }
     }
-    for (int i = 0; HI && i < nt_lo; ++i) {
+    for (int i = 0; HI && i < el; ++i) {
       const int j = lo_start + i;
       if (j < max_tiles) {
         tile_expert[j] = e;
@@ -434,8 +462,11 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
         tile_rows[j] = min(tile_rows_max, run_lo - i * tile_rows_max);
       }
     }
+    row_start += run_hi + run_lo;
+    hi_start += eh;
+    lo_start += el;
   }
-  if (e == 0) {
+  if (tid == 0) {
     offsets[N] = tot_a;
     const int nh = min(total_hi, max_tiles);
     n_tiles[0] = nh;                                        // hi tiles: [0, n_tiles[0])
@@ -464,17 +495,26 @@ void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, 
   const int nchunk = chunk_hi ? bucket_chunks(T) : 0;
   PlaceArgs pa{place_idx, place_gates, T, K, row_src, row_gate, inv};
   BucketMasks bm{masks, masks_hi, prefix_hi, prefix_lo, counts_hi, nullptr, nullptr};
-  if (masks_hi) {
-    if (nchunk) bucket_count_kernel<true><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
-    bucket_scan_kernel<true><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
-                                                tile_expert, tile_row0, tile_rows, n_tiles,
-                                                max_tiles, pa, nchunk, chunk_hi, chunk_lo);
-  } else {
-    if (nchunk) bucket_count_kernel<false><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
-    bucket_scan_kernel<false><<<1, 1024, 0, s>>>(bm, nblk, N, tile_rows_max, counts, offsets,
-                                                 tile_expert, tile_row0, tile_rows, n_tiles,
-                                                 max_tiles, pa, nchunk, chunk_hi, chunk_lo);
-  }
+  auto scan = [&](auto hi, auto ept) {
+    constexpr bool HI = decltype(hi)::value;
+    if (nchunk) bucket_count_kernel<HI><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
+    bucket_scan_kernel<HI, decltype(ept)::value><<<1, 1024, 0, s>>>(
+        bm, nblk, N, tile_rows_max, counts, offsets, tile_expert, tile_row0, tile_rows, n_tiles, max_tiles, pa,
+        nchunk, chunk_hi, chunk_lo);
+  };
+  // experts per scan thread: N <= 1024, 2048, 4096
+  auto by_n = [&](auto hi) {
+    if (N <= 1024)
+      scan(hi, std::integral_constant<int, 1>{});
+    else if (N <= 2048)
+      scan(hi, std::integral_constant<int, 2>{});
+    else
+      scan(hi, std::integral_constant<int, 4>{});
+  };
+  if (masks_hi)
+    by_n(std::true_type{});
+  else
+    by_n(std::false_type{});
 }
 
 __global__ void place_kernel(const int* __restrict__ idx, const float* __restrict__ gates,

@@ -36,7 +36,8 @@ int main() {
   const int Ts[] = {1, 7, 16, 17, 33, 64, 65, 255, 256, 1100, 8192};
   const int shapes[][6] = {{256, 64, 16, 4, 128, 256}, {4096, 1024, 512, 22, 2688, 5376},
                            {8192, 2048, 512, 22, 5120, 10240}, {512, 128, 1024, 64, 192, 320},
-                           {256, 64, 16, 1, 64, 64}};
+                           {256, 64, 16, 1, 64, 64}, {208, 80, 32, 4, 112, 144},
+                           {256, 64, 4096, 64, 128, 256}};
   for (const auto& sh : shapes)
     for (int T : Ts)
       for (int ef = 0; ef < 2; ++ef)
@@ -50,10 +51,11 @@ int main() {
   // rejected shapes and formats
   size_t n = 0;
   latentmoe_config bad[] = {cfg(250, 64, 16, 4, 128, 256, 8), cfg(256, 64, 16, 17, 128, 256, 8),
-                            cfg(256, 64, 20, 4, 128, 256, 8), cfg(256, 64, 2048, 4, 128, 256, 8),
+                            cfg(256, 64, 20, 4, 128, 256, 8), cfg(256, 64, 4112, 4, 128, 256, 8),
                             cfg(256, 64, 128, 65, 128, 256, 8), cfg(256, 64, 16, 4, 128, 256, 8, 7),
                             cfg(256, 64, 16, 4, 128, 256, 8, 0, 2), cfg(256, 64, 16, 4, 128, 256, 8, 0, 0, 1),
-                            cfg(4096, 1024, 512, 22, 2688, 5376, 36315)};
+                            cfg(4096, 1024, 512, 22, 2688, 5376, 36315), cfg(200, 64, 16, 4, 128, 256, 8),
+                            cfg(256, 64, 16, 4, 120, 256, 8)};
   for (auto& c : bad) EXPECT(latentmoe_workspace_bytes(&c, &n) == LATENTMOE_ERR_UNSUPPORTED);
   latentmoe_config zero = cfg(256, 64, 16, 4, 128, 256, 0);
   EXPECT(latentmoe_workspace_bytes(&zero, &n) == LATENTMOE_ERR_INVALID_ARG);

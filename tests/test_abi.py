@@ -69,10 +69,12 @@ def test_status_strings_and_host_side_validation(lib):
     cfg = binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 0)
     n = binding.latentmoe_workspace_bytes(cfg)
     assert n > 0
+    assert binding.latentmoe_workspace_bytes(binding.latentmoe_config(256, 64, 4096, 64, 128, 256, 8, 0)) > n
     bad = [binding.latentmoe_config(250, 64, 16, 4, 128, 256, 8, 0),   # d not a multiple of 16
            binding.latentmoe_config(256, 72, 16, 4, 128, 256, 8, 0),   # l not a multiple of 16
            binding.latentmoe_config(256, 64, 16, 17, 128, 256, 8, 0),  # K > N
            binding.latentmoe_config(256, 64, 20, 4, 128, 256, 8, 0),   # N not a multiple of 16
+           binding.latentmoe_config(256, 64, 4112, 4, 128, 256, 8, 0),  # N above 4096
            binding.latentmoe_config(256, 64, 16, 4, 128, 256, 8, 7)]   # unknown format
     for c in bad:
         with pytest.raises(binding.LatentMoEError) as e:

@@ -186,13 +186,17 @@ def test_split_rows_large_tiles_zipf():
 @pytest.mark.parametrize("T,N,K,path", [
     (40, 1024, 64, "stream"),     # N = 1024 (the 16-slot top-K kernel), K = 64, 2.5 rows per expert
     (1500, 1024, 40, "tiles"),    # N = 1024 with ~59 rows per expert: large tiles, two row classes
+    (40, 2048, 64, "stream"),     # 32 slots per lane, two experts per bucketing thread
+    (40, 4096, 64, "stream"),     # N = 4096: 64 slots per lane, four experts per bucketing thread
+    (3200, 4096, 64, "tiles"),    # N = 4096 at 50 rows per expert: chunked bucketing, large tiles
     (50, 16, 1, "stream"),        # K = 1: each token's gate is 1
     (2100, 16, 1, "tiles"),       # K = 1 at ~131 rows per expert: every row paired (hi + lo)
     (300, 128, 64, "tiles"),      # K = 64 at 150 rows per expert: flat gates, most rows paired
 ])
 def test_extreme_expert_counts(T, N, K, path):
-    """The widest expert count and top-K the boundary accepts (N = 1024, K = 64) and
-    K = 1, on the streaming and the large-tile expert paths."""
+    """The widest expert count and top-K the boundary accepts (N = 4096, K = 64), the
+    top-K kernel's slot counts and K = 1, on the streaming and the large-tile expert
+    paths."""
     wl = small_wl(T=T, d=256, latent=64, n_experts=N, top_k=K, expert_hidden=128, shared_hidden=256)
     avg = T * K / N
     assert (avg > 48) == (path == "tiles")
