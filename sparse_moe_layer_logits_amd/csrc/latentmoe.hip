@@ -455,11 +455,14 @@ struct StageTimer {
   StageTimer(latentmoe_handle_s* h_, hipStream_t s_)
       : h(h_), s(s_), on(h_->profiling && h_->prof_calls < h_->prof_max) {}
   bool want(int stage) const { return on && ((h->prof_mask >> stage) & 1u); }
+  hipEvent_t event(int stage, int end) const {
+    return h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2 + end];
+  }
   void start(int stage, hipStream_t st = nullptr) {
-    if (want(stage)) (void)hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2], st ? st : s);
+    if (want(stage)) (void)hipEventRecord(event(stage, 0), st ? st : s);
   }
   void stop(int stage, hipStream_t st = nullptr) {
-    if (want(stage)) (void)hipEventRecord(h->events[((size_t)h->prof_calls * LATENTMOE_NUM_STAGES + stage) * 2 + 1], st ? st : s);
+    if (want(stage)) (void)hipEventRecord(event(stage, 1), st ? st : s);
   }
   void done() {
     if (on) h->prof_calls++;
@@ -1185,31 +1188,45 @@ int latentmoe_debug_copy(latentmoe_handle_t h, int which, void* dst, size_t byte
   const bool lin = h->last_linear;
   const void* src = nullptr;
   size_t w = 0, pitch = 0, rows = 1;
+  // rows of `width` bf16 values, `wbuf` apart in the buffer
+  auto bf16_rows = [&](const void* p, int width, size_t wbuf, size_t n) {
+    src = p;
+    w = (size_t)width * 2;
+    pitch = wbuf;
+    rows = n;
+  };
+  // one flat run of `n` bytes
+  auto flat = [&](const void* p, size_t n) {
+    src = p;
+    w = pitch = n;
+  };
+  const size_t L2 = (size_t)c.latent * 2, M2 = (size_t)c.expert_hidden * 2, MS2 = (size_t)c.shared_hidden * 2;
   switch (which) {
-    case LATENTMOE_INTER_Z: src = h->b.z; w = u.latent * 2; pitch = c.latent * 2; rows = T; break;
-    case LATENTMOE_INTER_Z_LO: src = h->b.z_lo; w = u.latent * 2; pitch = c.latent * 2; rows = T; break;
+    case LATENTMOE_INTER_Z: bf16_rows(h->b.z, u.latent, L2, T); break;
+    case LATENTMOE_INTER_Z_LO: bf16_rows(h->b.z_lo, u.latent, L2, T); break;
     case LATENTMOE_INTER_Y_LAT:
-      src = lin ? (const void*)h->b.ay : h->b.y_lat; w = u.latent * 2; pitch = lin ? LS : c.latent * 2; rows = T;
+      if (lin) bf16_rows(h->b.ay, u.latent, LS, T);
+      else bf16_rows(h->b.y_lat, u.latent, L2, T);
       break;
     case LATENTMOE_INTER_Y_LAT_LO:
-      src = lin ? (const void*)h->b.ay_lo : h->b.y_lat_lo; w = u.latent * 2; pitch = lin ? LS : c.latent * 2;
-      rows = T;
+      if (lin) bf16_rows(h->b.ay_lo, u.latent, LS, T);
+      else bf16_rows(h->b.y_lat_lo, u.latent, L2, T);
       break;
     case LATENTMOE_INTER_HS_HI:
-      src = lin ? (const void*)(h->b.ay + c.latent) : h->b.hs_hi; w = u.shared_hidden * 2;
-      pitch = lin ? LS : c.shared_hidden * 2; rows = T;
+      if (lin) bf16_rows(h->b.ay + c.latent, u.shared_hidden, LS, T);
+      else bf16_rows(h->b.hs_hi, u.shared_hidden, MS2, T);
       break;
     case LATENTMOE_INTER_HS_LO:
-      src = lin ? (const void*)(h->b.ay_lo + c.latent) : h->b.hs_lo; w = u.shared_hidden * 2;
-      pitch = lin ? LS : c.shared_hidden * 2; rows = T;
+      if (lin) bf16_rows(h->b.ay_lo + c.latent, u.shared_hidden, LS, T);
+      else bf16_rows(h->b.hs_lo, u.shared_hidden, MS2, T);
       break;
-    case LATENTMOE_INTER_H: src = h->b.h; w = u.expert_hidden * 2; pitch = c.expert_hidden * 2; rows = T * K; break;
-    case LATENTMOE_INTER_H_LO: src = h->b.h_lo; w = u.expert_hidden * 2; pitch = c.expert_hidden * 2; rows = T * K; break;
-    case LATENTMOE_INTER_COUNTS: src = h->b.counts; w = pitch = (size_t)c.n_experts * 4; break;
-    case LATENTMOE_INTER_OFFSETS: src = h->b.offsets; w = pitch = (size_t)(c.n_experts + 1) * 4; break;
-    case LATENTMOE_INTER_ROW_SRC: src = h->b.row_src; w = pitch = T * K * 4; break;
-    case LATENTMOE_INTER_INV: src = h->b.inv; w = pitch = T * K * 4; break;
-    case LATENTMOE_INTER_PAIRED: src = h->b.paired; w = pitch = T * K; break;
+    case LATENTMOE_INTER_H: bf16_rows(h->b.h, u.expert_hidden, M2, T * K); break;
+    case LATENTMOE_INTER_H_LO: bf16_rows(h->b.h_lo, u.expert_hidden, M2, T * K); break;
+    case LATENTMOE_INTER_COUNTS: flat(h->b.counts, (size_t)c.n_experts * 4); break;
+    case LATENTMOE_INTER_OFFSETS: flat(h->b.offsets, (size_t)(c.n_experts + 1) * 4); break;
+    case LATENTMOE_INTER_ROW_SRC: flat(h->b.row_src, T * K * 4); break;
+    case LATENTMOE_INTER_INV: flat(h->b.inv, T * K * 4); break;
+    case LATENTMOE_INTER_PAIRED: flat(h->b.paired, T * K); break;
     default: return LATENTMOE_ERR_INVALID_ARG;
   }
   if (bytes > w * rows) return LATENTMOE_ERR_INVALID_ARG;
