@@ -48,9 +48,21 @@ __device__ __forceinline__ int bg_off(int row, int piece) {
   return row * BG_ROWB + ((piece ^ ((row >> 1) & 3)) << 4);
 }
 
-// ring depth: 3 stages of 48 KB (dual) or 4 of 32 KB (single)
+// single mode: rows of two k steps (128 bytes, 8 pieces), piece p of row r at
+// p ^ (r & 7), so that any 8 consecutive rows read at one logical piece cover all
+// 32 banks
+constexpr int BG_PROWB = 2 * BG_ROWB;
+constexpr int BG_PTILEB = 256 * BG_PROWB;  // 32 KB per operand and pair
+__device__ __forceinline__ int bg_poff(int row, int piece) {
+  return row * BG_PROWB + ((piece ^ (row & 7)) << 4);
+}
+
+// ring: 3 stages of one k step, 48 KB each (dual), or 2 slots of two k steps, 64 KB
+// each (single)
 template <bool DUAL>
-constexpr int bg_stages() { return DUAL ? 3 : 4; }
+constexpr int bg_stages() { return DUAL ? 3 : 2; }
+template <bool DUAL>
+constexpr int bg_stage_bytes() { return DUAL ? 3 * BG_TILEB : 2 * BG_PTILEB; }
 
 // 8 waves of 128 x 64 (2 x 4), two waves per SIMD: one wave's LDS reads and waits
 // overlap the other's MFMAs
@@ -218,7 +230,7 @@ template <bool DUAL, int EPI, bool ONESEG>
 __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   constexpr int NPART = DUAL ? 2 : 1;
   constexpr int STAGES = bg_stages<DUAL>();
-  constexpr int STAGEB = BG_TILEB * (1 + NPART);  // weights + activation part(s)
+  constexpr int STAGEB = bg_stage_bytes<DUAL>();  // weights + activation part(s)
   // the epilogue stages half a tile (128 rows, every plane) in the ring's LDS
   static_assert(epi_planes<EPI>() * 128 * BG_BN * epi_bytes<EPI>() <= STAGES * STAGEB,
                 "the staged half of the output tile must fit in the ring");
@@ -284,16 +296,18 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   const int KT = (kend - kbeg) / BG_BK;
   const long long bexp = (long long)expert * p.b_stride;
 
-  // This wave loads 1 KB chunks c = wave + BG_WAVES i of each 16 KB operand
-  // tile: lane l fills slot l of the chunk, i.e. row 16c + l/4, stored piece
-  // l%4, which holds logical piece (l%4) ^ ((row >> 1) & 3).  Rows past the
-  // tile are clamped to a valid row: their products land in outputs that are
-  // never stored.
-  uint32_t w_off[BG_CPW], x_off[BG_CPW];
+  // This wave loads 1 KB chunks c = wave + BG_WAVES i of each operand tile: lane l
+  // fills slot l of the chunk.  Dual: rows of one k step, row 16c + l/4, stored piece
+  // l%4, which holds logical piece (l%4) ^ ((row >> 1) & 3).  Single: rows of two k
+  // steps, row 8c + l/8, stored piece l%8 holding logical piece (l%8) ^ (row & 7).
+  // Rows past the tile are clamped to a valid row: their products land in outputs
+  // that are never stored.
+  constexpr int CPW = DUAL ? BG_CPW : 2 * BG_CPW;  // chunks per wave and operand
+  uint32_t w_off[CPW], x_off[CPW];
 #pragma unroll
-  for (int i = 0; i < BG_CPW; ++i) {
-    const int row = 16 * (wave + BG_WAVES * i) + (lane >> 2);
-    const int piece = (lane & 3) ^ ((row >> 1) & 3);
+  for (int i = 0; i < CPW; ++i) {
+    const int row = DUAL ? 16 * (wave + BG_WAVES * i) + (lane >> 2) : 8 * (wave + BG_WAVES * i) + (lane >> 3);
+    const int piece = DUAL ? (lane & 3) ^ ((row >> 1) & 3) : (lane & 7) ^ (row & 7);
     const int wrow = min(n0 + row, p.N - 1) - n0;
     const int xr = min(row, rows - 1);
     const int src = p.row_index ? p.row_index[row0 + xr] : row0 + xr;
@@ -361,65 +375,89 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   // that hold rows (the wave's first nb) are read and multiplied (wave-uniform).
   const int nb = min(BG_MB, max(0, (((rows + 15) >> 4) - wm + 3) >> 2));
   if constexpr (!DUAL) {
-    // Next step's fragments are read while this step's MFMAs run: after step
-    // kt + 1's barrier the wave reads that step's activation fragments into a
-    // second set and, as soon as the 4 MFMAs of weight fragment a have issued,
-    // reloads fragment a from step kt + 1.  With every wave released by one
-    // barrier, reads issued at the barrier and waited for would otherwise leave the
-    // MFMA pipes idle while 96 KB of fragments stream out of LDS.  A ring slot is
-    // free once every wave holds its fragments in registers, so all STAGES slots
-    // carry loads:
-    //   before step kt's barrier: stages issued 0 .. min(kt - 1 + STAGES, KT - 1);
-    //   stage kt + 1 must be complete: later stages outstanding min(STAGES - 2, KT - 2 - kt)
+    // Paired steps: a ring slot holds two k steps (64 k) of both operands in rows of
+    // 128 bytes, so a direct load of 8 rows x 128 bytes fetches whole lines (the
+    // half-line loads of 32-k rows brought every line into L1 twice).  Two slots.
+    // Step kt reads its fragments during step kt - 1 (after that step's barrier, if
+    // any).  An odd step kt = 2j + 1 waits for pair j + 1 (the only loads in
+    // flight), passes the barrier, and issues pair j + 2 into slot j % 2, which
+    // every wave finished reading in step 2j; an even step needs no wait and no
+    // barrier (its pair was complete at the previous barrier, and it issues no loads).
+    const int KP = KT / 2;  // K is a multiple of 64 (the widths), so KT is even
+    auto issue_pair = [&](int pr, int u) {  // load u < 8 of pair pr: chunk u / 2 of operand u % 2
+      int k = kbeg + pr * 2 * BG_BK;
+      const uint16_t* A = A0;
+      const uint16_t* B = B0;
+      if constexpr (!ONESEG) {
+        if (k >= K0 && p.nseg > 1) {
+          k -= K0;
+          A = A1;
+          B = B1;
+          if (k >= K1 && p.nseg > 2) {
+            k -= K1;
+            A = A2;
+            B = B2;
+          }
+        }
+      }
+      uint8_t* st = smem + (pr & 1) * STAGEB;
+      const int i = u >> 1;
+      uint8_t* dst = st + (u & 1) * BG_PTILEB + (wave + BG_WAVES * i) * 1024;
+      if ((u & 1) == 0) {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(B + k) + (uint64_t)(w_off[i] * 2u), dst,
+                                         16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(A + k) + (uint64_t)(x_off[i] * 2u), dst,
+                                         16, 0, 0);
+      }
+    };
+    // fragment of step kt: row r of operand `op` (0 weights, 1 activations), lane
+    // group g's 16 bytes of the step's half of the 128-byte row
+    auto frag = [&](int kt, int op, int r) {
+      const uint8_t* base = smem + ((kt >> 1) & 1) * STAGEB + op * BG_PTILEB;
+      return *reinterpret_cast<const u32x4_t*>(base + bg_poff(r, (kt & 1) * 4 + g));
+    };
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < KT) issue(s);
-    wait_vmcnt((min(STAGES, KT) - 1) * LOADS);
+    for (int u = 0; u < 8; ++u) issue_pair(0, u);
+    if (KP > 1) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) issue_pair(1, u);
+      wait_vmcnt_c<8>();
+    } else {
+      wait_vmcnt_c<0>();
+    }
     asm volatile("s_barrier" ::: "memory");
     auto single = [&](auto nbc) {
     constexpr int NB = decltype(nbc)::value;
     u32x4_t wf[8], xa[1][BG_MB], xb[1][BG_MB];
-    {
-      const uint8_t* base = smem;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        xa[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
+    for (int b = 0; b < NB; ++b) xa[0][b] = frag(0, 1, (4 * b + wm) * 16 + r16);
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
-        if constexpr (NB > 0) wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
-    }
-    // a step with a next one; every such step has the same shape, so the compiler's
-    // wait insertion sees the current set complete (the explicit wait) and the next
-    // set's reads as the only ones outstanding.  The last step runs on its own.
-    // FAST: a steady-state step (kt + STAGES < KT): stages up to kt - 1 + STAGES were
-    // all issued, so STAGES - 2 stages follow stage kt + 1 (a compile-time wait), and
-    // stage kt + STAGES exists (its loads are issued without a test)
-    auto step = [&](int kt, const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB], auto fast) {
-      constexpr bool FAST = decltype(fast)::value;
-      // this wave's reads of step kt are in registers; after the barrier no wave
-      // reads slot kt % STAGES any more
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-      if constexpr (FAST)
-        wait_vmcnt_c<(STAGES - 2) * LOADS>();
-      else
-        wait_vmcnt(min(STAGES - 2, KT - 2 - kt) * LOADS);
-      asm volatile("s_barrier" ::: "memory");
-      const uint8_t* base = smem + ((kt + 1) % STAGES) * STAGEB;
+    for (int a = 0; a < 8; ++a)
+      if constexpr (NB > 0) wf[a] = frag(0, 0, wn * 128 + a * 16 + r16);
+    // step kt with a next step: ODD steps wait and pass the barrier; ISSUE: pair
+    // kt / 2 + 2 exists (odd steps only).  The compiler's wait insertion sees the
+    // current fragments complete and the next ones as the only reads outstanding.
+    auto step = [&](int kt, const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB], auto odd, auto issue) {
+      constexpr bool ODD = decltype(odd)::value;
+      constexpr bool ISSUE = decltype(issue)::value;
+      if constexpr (ODD) {
+        // this wave's reads of step kt are in registers, and pair kt / 2 + 1 has landed
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+        wait_vmcnt_c<0>();
+        asm volatile("s_barrier" ::: "memory");
+      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        xn[0][b] = *reinterpret_cast<const u32x4_t*>(base + BG_TILEB + bg_off((4 * b + wm) * 16 + r16, g));
+      for (int b = 0; b < NB; ++b) xn[0][b] = frag(kt + 1, 1, (4 * b + wm) * 16 + r16);
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xc[0][b], acc[a][b]);
-        if constexpr (NB > 0) wf[a] = *reinterpret_cast<const u32x4_t*>(base + bg_off(wn * 128 + a * 16 + r16, g));
-        // stage kt + STAGES (into the slot every wave finished reading before this
-        // step's barrier), its loads spread over the step: issued together after
-        // the barrier, all waves' loads queue at the memory unit at once and each
-        // wave's MFMAs wait behind its own loads
-#pragma unroll
-        for (int u = a * LOADS / 8; u < (a + 1) * LOADS / 8; ++u)
-          if (FAST || kt + STAGES < KT) issue_one(kt + STAGES, u);
+        if constexpr (NB > 0) wf[a] = frag(kt + 1, 0, wn * 128 + a * 16 + r16);
+        // pair kt / 2 + 2, its loads spread over the step's MFMAs (issued together
+        // after the barrier, all waves' loads queue at the memory unit at once and
+        // each wave's MFMAs wait behind its own loads)
+        if constexpr (ISSUE) issue_pair(kt / 2 + 2, a);
       }
       // keep the interleave: the activation reads, then NB MFMAs and one read per a
       if constexpr (NB > 0) {
@@ -431,26 +469,23 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
         }
       }
     };
-    const std::integral_constant<bool, true> fast{};
-    const std::integral_constant<bool, false> checked{};
+    const std::true_type yes{};
+    const std::false_type no{};
     int kt = 0;
-    for (; kt + 1 + STAGES < KT; kt += 2) {
-      step(kt, xa, xb, fast);
-      step(kt + 1, xb, xa, fast);
+    for (; kt + 4 < KT; kt += 2) {  // pair kt / 2 + 2 exists
+      step(kt, xa, xb, no, no);
+      step(kt + 1, xb, xa, yes, yes);
     }
-    for (; kt + 2 < KT; kt += 2) {
-      step(kt, xa, xb, checked);
-      step(kt + 1, xb, xa, checked);
+    if (kt + 2 < KT) {  // the last pair but one: nothing left to issue
+      step(kt, xa, xb, no, no);
+      step(kt + 1, xb, xa, yes, no);
+      kt += 2;
     }
-    if (kt + 1 < KT) {  // two steps left: one more with a next step, ending in xb
-      step(kt, xa, xb, checked);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) xa[0][b] = xb[0][b];
-    }
+    step(kt, xa, xb, no, no);  // the last pair: its second step has no next
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xa[0][b], acc[a][b]);
+      for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xb[0][b], acc[a][b]);
     };
     switch (nb) {
       case 4: single(std::integral_constant<int, 4>{}); break;
@@ -528,7 +563,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
 }
 
 template <bool DUAL>
-constexpr int big_lds_bytes() { return bg_stages<DUAL>() * BG_TILEB * (1 + (DUAL ? 2 : 1)); }
+constexpr int big_lds_bytes() { return bg_stages<DUAL>() * bg_stage_bytes<DUAL>(); }
 
 template <bool DUAL, int EPI>
 static hipError_t big_attr() {
