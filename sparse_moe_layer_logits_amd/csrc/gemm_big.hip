@@ -11,25 +11,40 @@
 // no MFMAs), and the interleave spreads them evenly over the four SIMDs (at the
 // Zipf-routed prefill this cut the expert GEMMs by 2-4 %).
 //
-// Operand tiles go from global memory straight into a ring of STAGES LDS
-// buffers (global_load_lds, 16 bytes per lane, no staging registers): while
-// step k computes, the loads of steps k+1 .. k+STAGES-1 are in flight.  Each
-// step waits for its own loads (vmcnt), then one barrier makes every wave's
-// loads visible and frees the buffer the next issue overwrites.
+// Operand tiles go from global memory straight into a ring of LDS buffers
+// (global_load_lds, 16 bytes per lane, no staging registers), and a wave reads a
+// step's fragments while the previous step's MFMAs run.
 //
-// LDS rows are 64 bytes (32 bf16 of one k step); the 16-byte piece p of row r
-// is stored at piece p ^ ((r >> 1) & 3).  A 16-byte LDS read is served four
-// lanes at a time over 32 four-byte banks, so the rows r .. r+7 that neighbouring
-// lanes of a group read must fill the 128 bytes of banks without overlap: rows
-// 2j and 2j+1 take the two 64-byte halves and bits 1..2 of r separate the four
-// pairs.  (An XOR with bits 2..3 doubled up banks and read at 112 B/clk per CU
-// against 198 B/clk conflict-free, measured.)  A direct load writes lane l of a
-// wave to slot l of a 1 KB chunk (16 rows), so each lane fetches the global
-// piece that belongs in its slot.
+// Single mode (one activation part): a ring slot holds two k steps of both
+// operands, rows of 128 bytes, two slots (128 KB).  A direct load then covers 8
+// rows x 128 bytes, whole lines: with one k step per slot each load touched 16
+// half lines, and as the other half came a step later, after 64 KB of other lines,
+// L1 fetched most lines twice (counters: 74 % of tag accesses missed; the loads
+// are what the kernel waits on).  Odd steps wait for the next pair (the only loads
+// in flight), pass a barrier and issue the pair after it into the slot the last
+// pair left; even steps have no wait and no barrier.  The 16-byte piece p of row r
+// sits at p ^ (r & 7), so the 8 rows a lane group reads at one piece fill all 32
+// banks.  Prefill 3.78 -> 3.72 ms.
+//
+// Dual mode (hi + lo activation parts, 48 KB per k step): a ring of 3 one-step
+// stages.  While step k computes, the loads of steps k+1 .. k+2 are in flight;
+// each step waits for its own loads (vmcnt), then one barrier makes every wave's
+// loads visible and frees the buffer the next issue overwrites.  LDS rows are 64
+// bytes (32 bf16 of one k step); the 16-byte piece p of row r is stored at piece
+// p ^ ((r >> 1) & 3).  A 16-byte LDS read is served four lanes at a time over 32
+// four-byte banks, so the rows r .. r+7 that neighbouring lanes of a group read
+// must fill the 128 bytes of banks without overlap: rows 2j and 2j+1 take the two
+// 64-byte halves and bits 1..2 of r separate the four pairs.  (An XOR with bits
+// 2..3 doubled up banks and read at 112 B/clk per CU against 198 B/clk
+// conflict-free, measured.)
+//
+// A direct load writes lane l of a wave to slot l of a 1 KB chunk, so each lane
+// fetches the global piece that belongs in its slot.
 //
 // k layout inside a 32-wide k step: lane group g = lane / 16 holds k = 8g .. 8g+7
-// for both operands.  DUAL: the activation tile comes as two bf16 parts (hi + lo)
-// and every weight fragment feeds both.
+// for both operands (in single mode step 2j + h is half h of pair j's rows).
+// DUAL: the activation tile comes as two bf16 parts (hi + lo) and every weight
+// fragment feeds both.
 #include "common.hpp"
 #include "epilogue.hpp"
 #include "kernels.hpp"
