@@ -249,7 +249,7 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   // the epilogue stages half a tile (128 rows, every plane) in the ring's LDS
   static_assert(epi_planes<EPI>() * 128 * BG_BN * epi_bytes<EPI>() <= STAGES * STAGEB,
                 "the staged half of the output tile must fit in the ring");
-  constexpr int LOADS = BG_CPW * (1 + NPART);     // direct loads per wave per stage
+  constexpr int LOADS = BG_CPW * (1 + NPART);     // dual mode: direct loads per wave per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -340,8 +340,8 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   const uint16_t* B2 = reinterpret_cast<const uint16_t*>(p.seg[2].B) + bexp + (long long)n0 * p.ldb;
   const uint16_t* Alo = reinterpret_cast<const uint16_t*>(p.a_lo);
 
-  // direct load u of stage kt: chunk i = u / (1 + NPART) of the weights (part 0),
-  // the activations (1) or their low halves (2)
+  // dual mode: direct load u of stage kt: chunk i = u / (1 + NPART) of the weights
+  // (part 0), the activations (1) or their low halves (2)
   auto issue_one = [&](int kt, int u) {
     int k = kbeg + kt * BG_BK;
     const uint16_t* A = A0;
