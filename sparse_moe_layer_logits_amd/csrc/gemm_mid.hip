@@ -3,8 +3,9 @@
 // (1; the one launched: FP4 experts take bf16 activations) or a bf16 hi + lo
 // pair (2).
 //
-// Block: W waves (W = 8, 7 or 4, the largest that divides N into 32-row wave
-// slabs); wave w owns two 16-row MFMA tiles of weight rows (n0 + 32w ..)
+// Block: W waves (W = 8 from N = 1024 on, else 8, 7 or 4 as they divide N into
+// 32-row wave slabs; waves past N stage activations and skip their products);
+// wave w owns two 16-row MFMA tiles of weight rows (n0 + 32w ..)
 // against the tile's activation rows in 16-row groups (a tile of r rows runs
 // ceil(r/16) groups, no more).  The k loop runs in stages of 128.  Stage s is
 // loaded into register set s % NS, NS - 1 stages ahead: the activation stage
@@ -70,10 +71,9 @@ __device__ __forceinline__ void mid_body(const GemmParams& p, uint8_t* smem, int
   constexpr int NTH = 64 * W;
   constexpr int BN = 16 * MD_NT * W;  // weight rows per block
   constexpr int XP = (MD_PIECES + NTH - 1) / NTH;
-  // register sets: three fit next to two activation pieces per thread in 128 VGPRs
-  // with 7 waves; 8-wave blocks (one activation piece fewer per thread, but the
-  // same budget) take two
-  constexpr int NS = XP <= 2 && W < 8 ? 3 : 2;  // loads run NS - 1 stages ahead
+  // two register sets (loads run one stage ahead): a third does not fit next to the
+  // activation pieces in the 128 VGPRs of two blocks per CU
+  constexpr int NS = 2;
   // activation parts + scales: every thread stages one weight row's 8 scale bytes
   // (rows past the block's BN are never read)
   constexpr int SLOTB = NP * MD_PARTB + NTH * 8;
@@ -253,8 +253,11 @@ static void mid_launch(const GemmParams& p, hipStream_t s) {
   gemm_mid_kernel<W, EPI, NP><<<(unsigned)blocks, 64 * W, mid_lds_bytes<W, NP>(), s>>>(p);
 }
 
-// waves per block: the largest of 8, 7 that splits N into whole blocks, else 4
-static int mid_waves(int N) { return N % 256 == 0 ? 8 : N % 224 == 0 ? 7 : 4; }
+// waves per block: 8 from N = 1024 on (the idle waves of a partial last block cost
+// less than the activation re-reads of more, narrower blocks: m = 2688 in 11 8-wave
+// blocks ran expert up at 0.244 ms against 0.260 in 12 7-wave blocks), else the
+// largest of 8, 7 that splits N into whole blocks, else 4
+static int mid_waves(int N) { return N >= 1024 || N % 256 == 0 ? 8 : N % 224 == 0 ? 7 : 4; }
 
 template <int EPI, int NP>
 static void mid_launch_w(const GemmParams& p, hipStream_t s) {

@@ -147,6 +147,16 @@ def test_fp4_mid_kernel_waves_past_n():
     full_check(wl, x, W, tol=3e-2)
 
 
+def test_fp4_mid_kernel_partial_last_block():
+    # up-proj N = m = 1088 in 8-wave blocks of 256 rows (N >= 1024 takes 8 waves): the
+    # fifth block has two active waves and six past N
+    wl = small_wl(T=240, d=256, latent=128, n_experts=32, top_k=4, expert_hidden=1088,
+                  shared_hidden=256, experts="fp4")
+    x, W = gen(wl, 18)
+    log("FP4 kernel, partial last block", wl)
+    full_check(wl, x, W, tol=3e-2)
+
+
 def test_fp4_mid_kernel_chunks():
     # the FP4 kernel over many k stages: expert up K = 896 (seven stages of 128, not a
     # multiple of its three register sets), N = 1536 in 8-wave blocks; expert down
