@@ -167,13 +167,19 @@ def stored_mfma(kernel, workload):
                               "algorithmic_tflop_per_launch") if k in d}
 
 
-def stored_traffic(kernel, workload):
-    path = os.path.join(PROFILES, "traffic_%s_%s.json" % (kernel, workload))
+def stored_traffic(kernel, workload, stage=None):
+    """HBM traffic counters stored for a kernel's launch (of a layer stage), if taken
+    on the current sources."""
+    name = "traffic_%s_%s.json" % (kernel, workload) if stage is None else \
+        "traffic_%s_%s_%s.json" % (kernel, workload, stage)
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
     if d.get("source_sha") != source_sha(kernel):
         return None    # the kernel changed since the counters were taken
+    if stage is not None and d.get("stage") != stage:
+        return None
     return d
 
 
@@ -266,7 +272,7 @@ def measure(name, args, steps, warmup, tokens=0, cpu_budget=15.0, cpu_1thread=Fa
     else:
         achieved, peak, unit, bound = kf / dom_s / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     # counter data is stored for the workloads' own batch sizes only
-    tr = None if tokens else stored_traffic(kernel, wl.name)
+    tr = None if tokens else stored_traffic(kernel, wl.name, dom)
     traffic = None if tr is None else tr["hbm_bytes_per_launch"]
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -4,7 +4,7 @@
         per (kernel, grid size) group: calls, average / min / max duration
 
     python -m sparse_moe_layer_logits_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR \\
-            --group SUBSTR@GRID [--group ...] --probe-mib M --source-sha SHA --out FILE.json
+            --group SUBSTR@GRID [--group ...] --probe-mib M --source-sha SHA [--stage S] --out FILE.json
         HBM bytes per launch of a stage (the sum over its kernel groups, one
         launch each) from a FETCH_SIZE run and a WRITE_SIZE run.  Each counter is scaled by what it reads for the plain
         copy launches of the same run (bench.py --copy-probe-mib M: M MiB read
@@ -99,6 +99,8 @@ def cmd_traffic(a):
         res["groups"] = names
     res["hbm_bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
     res["source_sha"] = a.source_sha
+    if a.stage:
+        res["stage"] = a.stage
     res["command"] = a.command
     json.dump(res, open(a.out, "w"), indent=1)
     print(json.dumps(res, indent=1))
@@ -168,6 +170,7 @@ def main(argv=None):
                    help="kernel name substring @ grid size (threads); repeat for a stage of several launches")
     t.add_argument("--probe-mib", type=int, required=True)
     t.add_argument("--source-sha", required=True)
+    t.add_argument("--stage", default="", help="the layer stage the groups make up (e.g. expert_up)")
     t.add_argument("--command", default="")
     t.add_argument("--out", required=True)
     m = sub.add_parser("mfma")
