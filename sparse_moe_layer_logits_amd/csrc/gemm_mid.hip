@@ -268,11 +268,10 @@ static void mid_launch_w(const GemmParams& p, hipStream_t s) {
   }
 }
 
-// epilogues offered: with a hi + lo activation, relu^2 to a pair or the gated fp32
-// rows; with a bf16 activation, relu^2 to bf16 or the gated fp32 rows
+// epilogues offered (FP4 experts take bf16 activations and give bf16 outputs):
+// relu^2 to bf16 (expert up) and the gated rows as bf16 (expert down)
 bool gemm_mid_supports(const GemmParams& p, bool fp4) {
-  // FP4 experts take bf16 activations (no hi + lo pair)
-  const bool epi_ok = !p.a_lo && (p.epi == EPI_SQRELU_BF16 || p.epi == EPI_GATE_F32);
+  const bool epi_ok = !p.a_lo && (p.epi == EPI_SQRELU_BF16 || p.epi == EPI_GATE_BF16);
   return fp4 && p.tile_expert && p.rows_per_tile <= MD_ROWS && p.nseg == 1 && epi_ok &&
          p.b_scale_sm && p.N % 64 == 0 && p.seg[0].K % MD_KS == 0 && p.seg[0].K >= MD_KS;
 }
@@ -286,7 +285,7 @@ static hipError_t mid_attr() {
 template <int W>
 static hipError_t mid_attr_w() {
   hipError_t e = mid_attr<W, EPI_SQRELU_BF16, 1>();
-  if (e == hipSuccess) e = mid_attr<W, EPI_GATE_F32, 1>();
+  if (e == hipSuccess) e = mid_attr<W, EPI_GATE_BF16, 1>();
   return e;
 }
 
@@ -302,7 +301,7 @@ void launch_gemm_mid(const GemmParams& p, bool fp4, hipStream_t s) {
   if (p.epi == EPI_SQRELU_BF16)
     mid_launch_w<EPI_SQRELU_BF16, 1>(p, s);
   else
-    mid_launch_w<EPI_GATE_F32, 1>(p, s);
+    mid_launch_w<EPI_GATE_BF16, 1>(p, s);
 }
 
 // [E][N][K/16] -> [E][K/128][N][8]: one thread per 8-byte group

@@ -995,8 +995,10 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // it.  Per-stage timing keeps the plain order, so each stage times whole launches.
   const bool hi_side = split_rows && !one_stream && !linear;
   // the bf16 class's expert-down rows go out as bf16: their rounding enters y_lat times
-  // a gate below the class threshold, like that of their bf16 z and h
+  // a gate below the class threshold, like that of their bf16 z and h; with FP4 experts
+  // every gated row does (16-bit activations next to 4-bit weights, R17)
   const bool og_mix = split_rows;
+  const bool og_bf16 = fp4 && !split_rows;
   if (hi_side) {
     launch_gemm_big(pu, s);  // expert up, hi tiles
     (void)hipEventRecord(h->ev_hi, s);
@@ -1055,14 +1057,21 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     launch_expert(pu, EPI_SQRELU_BF16, b.h);
     tm.stop(LATENTMOE_STAGE_EXPERT_UP);
     tm.start(LATENTMOE_STAGE_EXPERT_DOWN);
-    launch_expert(pw, og_mix ? EPI_GATE_BF16 : EPI_GATE_F32, og_mix ? (void*)b.og16 : (void*)b.og);
+    if (og_bf16) {
+      GemmParams g = pw;
+      g.epi = EPI_GATE_BF16;
+      g.C = b.og16;
+      launch_expert(g, EPI_GATE_BF16, b.og16);
+    } else {
+      launch_expert(pw, og_mix ? EPI_GATE_BF16 : EPI_GATE_F32, og_mix ? (void*)b.og16 : (void*)b.og);
+    }
     tm.stop(LATENTMOE_STAGE_EXPERT_DOWN);
   }
 
   // ---- 7. combine ----
   tm.start(LATENTMOE_STAGE_COMBINE);
-  launch_combine(b.og, og_mix ? b.og16 : nullptr, b.paired, b.inv, T, K, L, linear ? b.ay : b.y_lat,
-                 linear ? b.ay_lo : b.y_lat_lo, linear ? LS : L, s);
+  launch_combine(b.og, og_mix || og_bf16 ? b.og16 : nullptr, og_mix ? b.paired : nullptr, b.inv, T, K, L,
+                 linear ? b.ay : b.y_lat, linear ? b.ay_lo : b.y_lat_lo, linear ? LS : L, s);
   tm.stop(LATENTMOE_STAGE_COMBINE);
 
   if (linear) {

@@ -123,7 +123,8 @@ void launch_xreduce(const float* partial, int splits, long long pstride, int T, 
 // up-projection sees it to about 16 significant bits.
 //
 // MIX (large-tile path with two row classes): a row of the bf16 class (paired = 0)
-// was written to og16 as bf16, the others to og as fp32.  A row costs one 16-byte
+// was written to og16 as bf16, the others to og as fp32; with no class flags
+// (FP4 experts) every row is in og16.  A row costs one 16-byte
 // load per thread from its own format's row (the first 8 bytes of a bf16 row's load
 // are the thread's 4 values, widened exactly before the add; og16 has 16 bytes of
 // slack past its last row): no branches, so the compiler keeps all loads in flight.
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ o
   if (threadIdx.x < K) {
     const int q = inv[(long long)t * K + threadIdx.x];
     pos[threadIdx.x] = q;
-    wide[threadIdx.x] = !MIX || paired[(long long)t * K + threadIdx.x];  // the class top-K assigned
+    // the class top-K assigned; MIX without class flags: every row is bf16
+    wide[threadIdx.x] = !MIX || (paired && paired[(long long)t * K + threadIdx.x]);
   }
   __syncthreads();
   const int c = (blockIdx.y * 64 + threadIdx.x) * 4;
