@@ -94,13 +94,21 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void topk_kernel(const float* __re
   __syncthreads();
 
   if (t < T) {
+    // every load is issued before the first use (clamped index, no per-slot branch):
+    // guarded loads were each waited for on their own, a chain of global round trips
+    const float* __restrict__ row = logits + (long long)t * N;
+    float lv[SLOTS], bv[SLOTS];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) lv[j] = row[min(j * 64 + lane, N - 1)];
+#pragma unroll
+    for (int j = 0; j < SLOTS; ++j) bv[j] = 0.0f;
+    if (bias) {
+#pragma unroll
+      for (int j = 0; j < SLOTS; ++j) bv[j] = bias[min(j * 64 + lane, N - 1)];
+    }
     uint32_t ok[SLOTS];  // orderable logit; 0 marks an empty slot
 #pragma unroll
-    for (int j = 0; j < SLOTS; ++j) {
-      const int e = j * 64 + lane;
-      ok[j] = 0u;
-      if (e < N) ok[j] = orderable(logits[(long long)t * N + e] + (bias ? bias[e] : 0.0f));
-    }
+    for (int j = 0; j < SLOTS; ++j) ok[j] = j * 64 + lane < N ? orderable(lv[j] + bv[j]) : 0u;
     // tau = the largest key with at least K keys >= it (the K-th largest key)
     uint32_t tau = 0u;
     for (int bit = 31; bit >= 0; --bit) {
@@ -316,7 +324,16 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(BucketMasks bm, int n
 // nchunk > 0: the prefixes inside chunks and the chunk counts are in place (from
 // bucket_count_kernel); the counts become exclusive chunk offsets here.  Thread t
 // owns the EPT experts t EPT .. t EPT + EPT - 1 (N <= 1024 EPT).
-template <bool HI, int EPT>
+// LP (fused placement of a small batch, every (token, k) item by this workgroup):
+// the per-(mask group, expert) words stay in LDS, (prefix << 16) | 16-bit mask of
+// the hi class (all rows without classes), then (prefix_lo << 16) | mask of all rows
+// with classes, beside the expert offsets and hi counts; each thread's items' expert
+// and gate are loaded at the start, so placing costs no global round trip.
+constexpr int LP_ITEMS = 8;  // items per thread: T * K <= 8192 on the fused path
+template <bool HI>
+constexpr int lp_words_per_entry() { return HI ? 2 : 1; }
+
+template <bool HI, int EPT, bool LP>
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     BucketMasks bm, int nblk, int N, int tile_rows_max, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ tile_expert, int* __restrict__ tile_row0,
@@ -325,7 +342,21 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
   __shared__ int scan_a[16];  // wave totals
   __shared__ int scan_b[16];
   __shared__ int scan_c[16];
+  extern __shared__ uint32_t lp_words[];  // LP: [words per entry][nblk][N], offsets [N + 1], hi counts [N]
+  int* const lp_off = reinterpret_cast<int*>(lp_words + lp_words_per_entry<HI>() * nblk * N);
+  int* const lp_cnt = lp_off + N + 1;
   const int tid = threadIdx.x;
+  const int n_items = pa.T * pa.K;
+  int it_e[LP ? LP_ITEMS : 1];
+  float it_g[LP ? LP_ITEMS : 1];
+  if constexpr (LP) {  // clamped, unconditional: all in flight together
+#pragma unroll
+    for (int r = 0; r < LP_ITEMS; ++r) {
+      const int i = min(tid + r * 1024, n_items - 1);
+      it_e[r] = pa.idx[i];
+      it_g[r] = pa.gates[i];
+    }
+  }
   // rows of each of this thread's experts in the two classes
   int rh[EPT], rl[EPT];
 #pragma unroll
@@ -372,12 +403,15 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const long long be = (long long)(b + u) * N + e;
-            bm.prefix_hi[be] = run_hi;
-            run_hi += __popc(mh[u]);
-            if constexpr (HI) {
-              bm.prefix_lo[be] = run_lo;
-              run_lo += __popc(m[u] & ~mh[u]);
+            if constexpr (LP) {
+              lp_words[be] = ((uint32_t)run_hi << 16) | mh[u];
+              if constexpr (HI) lp_words[(long long)nblk * N + be] = ((uint32_t)run_lo << 16) | m[u];
+            } else {
+              bm.prefix_hi[be] = run_hi;
+              if constexpr (HI) bm.prefix_lo[be] = run_lo;
             }
+            run_hi += __popc(mh[u]);
+            if constexpr (HI) run_lo += __popc(m[u] & ~mh[u]);
           }
         }
       };
@@ -387,6 +421,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     }
     if (e < N) {
       if constexpr (HI) bm.counts_hi[e] = run_hi;
+      if constexpr (LP && HI) lp_cnt[e] = run_hi;
       counts[e] = run_hi + run_lo;
     }
     rh[x] = run_hi;
@@ -446,6 +481,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     const int eh = (run_hi + tile_rows_max - 1) / tile_rows_max;
     const int el = (run_lo + tile_rows_max - 1) / tile_rows_max;
     offsets[e] = row_start;
+    if constexpr (LP) lp_off[e] = row_start;
     for (int i = 0; i < eh; ++i) {
       const int j = hi_start + i;
       if (j < max_tiles) {
@@ -472,7 +508,29 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(
     n_tiles[0] = nh;                                        // hi tiles: [0, n_tiles[0])
     n_tiles[1] = min(total_hi + total_lo, max_tiles) - nh;  // then n_tiles[1] others
   }
-  if (pa.idx) {  // small T: the same workgroup places every (token, k)
+  if constexpr (LP) {  // the same workgroup places every (token, k), from LDS
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < LP_ITEMS; ++r) {
+      const int i = tid + r * 1024;
+      if (i >= n_items) break;
+      const int t = i / pa.K, e = it_e[r];
+      const int tl = t % TOPK_TOKENS_PER_BLOCK;
+      const long long be = (long long)(t / TOPK_TOKENS_PER_BLOCK) * N + e;
+      const uint32_t below = (1u << tl) - 1u;
+      const uint32_t w = lp_words[be], mh = w & 0xFFFFu;
+      int pos = lp_off[e];
+      if (!HI || ((mh >> tl) & 1u)) {
+        pos += (int)(w >> 16) + __popc(mh & below);
+      } else {
+        const uint32_t w1 = lp_words[(long long)nblk * N + be];
+        pos += lp_cnt[e] + (int)(w1 >> 16) + __popc(w1 & ~mh & below & 0xFFFFu);
+      }
+      pa.row_src[pos] = t;
+      pa.row_gate[pos] = it_g[r];
+      pa.inv[i] = pos;
+    }
+  } else if (pa.idx) {  // small T: the same workgroup places every (token, k)
     __syncthreads();
     const long long n = (long long)pa.T * pa.K;
     for (long long i = threadIdx.x; i < n; i += blockDim.x)
@@ -497,10 +555,20 @@ void launch_bucket_scan(const uint32_t* masks, const uint32_t* masks_hi, int T, 
   BucketMasks bm{masks, masks_hi, prefix_hi, prefix_lo, counts_hi, nullptr, nullptr};
   auto scan = [&](auto hi, auto ept) {
     constexpr bool HI = decltype(hi)::value;
+    constexpr int EPT = decltype(ept)::value;
     if (nchunk) bucket_count_kernel<HI><<<nchunk, 256, 0, s>>>(bm, nblk, N, chunk_hi, chunk_lo);
-    bucket_scan_kernel<HI, decltype(ept)::value><<<1, 1024, 0, s>>>(
-        bm, nblk, N, tile_rows_max, counts, offsets, tile_expert, tile_row0, tile_rows, n_tiles, max_tiles, pa,
-        nchunk, chunk_hi, chunk_lo);
+    // placement from LDS when the batch's words, offsets and counts fit in 64 KB
+    const long long lp_bytes = 4LL * ((long long)lp_words_per_entry<HI>() * nblk * N + 2 * N + 1);
+    const bool lp = place_idx && !nchunk && (long long)T * K <= 1024LL * LP_ITEMS && T < 65536 &&
+                    lp_bytes <= 65536;
+    if (lp)
+      bucket_scan_kernel<HI, EPT, true><<<1, 1024, (size_t)lp_bytes, s>>>(
+          bm, nblk, N, tile_rows_max, counts, offsets, tile_expert, tile_row0, tile_rows, n_tiles, max_tiles,
+          pa, nchunk, chunk_hi, chunk_lo);
+    else
+      bucket_scan_kernel<HI, EPT, false><<<1, 1024, 0, s>>>(
+          bm, nblk, N, tile_rows_max, counts, offsets, tile_expert, tile_row0, tile_rows, n_tiles, max_tiles,
+          pa, nchunk, chunk_hi, chunk_lo);
   };
   // experts per scan thread: N <= 1024, 2048, 4096
   auto by_n = [&](auto hi) {
