@@ -15,17 +15,20 @@
 // (global_load_lds, 16 bytes per lane, no staging registers), and a wave reads a
 // step's fragments while the previous step's MFMAs run.
 //
-// Single mode (one activation part): a ring slot holds two k steps of both
-// operands, rows of 128 bytes, two slots (128 KB).  A direct load then covers 8
-// rows x 128 bytes, whole lines: with one k step per slot each load touched 16
-// half lines, and as the other half came a step later, after 64 KB of other lines,
-// L1 fetched most lines twice (counters: 74 % of tag accesses missed; the loads
-// are what the kernel waits on).  Odd steps wait for the next pair (the only loads
-// in flight), pass a barrier and issue the pair after it into the slot the last
-// pair left; even steps have no wait and no barrier.  The 16-byte piece p of row r
-// sits at p ^ (r & 7), so the 8 rows a lane group reads at one piece fill all 32
-// banks.  Prefill 3.78 -> 3.72 ms.
-//
+// Single mode (one activation part): a ring slot holds two k steps of one operand,
+// rows of 128 bytes; three slots for the weights and two for the activations fill
+// the 160 KB of LDS.  A direct load then covers 8 rows x 128 bytes, whole lines:
+// with one k step per slot each load touched 16 half lines, and as the other half
+// came a step later, after 64 KB of other lines, L1 fetched most lines twice
+// (counters: 74 % of tag accesses missed; the loads are what the kernel waits on).
+// Odd steps wait for the next pair (the weights of the pair after it may stay in
+// flight), pass a barrier and refill the slots the last pair left: the weights,
+// which come from HBM, are issued three pairs ahead, the activations two.  Even
+// steps have no wait and no barrier.  The 16-byte piece p of row r sits at
+// p ^ (r & 7), so the 8 rows a lane group reads at one piece fill all 32 banks.
+// Prefill 3.78 -> 3.72 ms with paired steps in two shared slots, 3.73 -> 3.53 ms
+// with the split ring (expert up and down 9 % faster each).
+
 // Dual mode (hi + lo activation parts, 48 KB per k step): a ring of 3 one-step
 // stages.  While step k computes, the loads of steps k+1 .. k+2 are in flight;
 // each step waits for its own loads (vmcnt), then one barrier makes every wave's
@@ -72,12 +75,12 @@ __device__ __forceinline__ int bg_poff(int row, int piece) {
   return row * BG_PROWB + ((piece ^ (row & 7)) << 4);
 }
 
-// ring: 3 stages of one k step, 48 KB each (dual), or 2 slots of two k steps, 64 KB
-// each (single)
+// ring: 3 stages of one k step, 48 KB each (dual), or 5 slots of two k steps of one
+// operand, 32 KB each (single: three for the weights, two for the activations)
 template <bool DUAL>
-constexpr int bg_stages() { return DUAL ? 3 : 2; }
+constexpr int bg_stages() { return DUAL ? 3 : 5; }
 template <bool DUAL>
-constexpr int bg_stage_bytes() { return DUAL ? 3 * BG_TILEB : 2 * BG_PTILEB; }
+constexpr int bg_stage_bytes() { return DUAL ? 3 * BG_TILEB : BG_PTILEB; }
 
 // 8 waves of 128 x 64 (2 x 4), two waves per SIMD: one wave's LDS reads and waits
 // overlap the other's MFMAs
@@ -390,54 +393,78 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
   // that hold rows (the wave's first nb) are read and multiplied (wave-uniform).
   const int nb = min(BG_MB, max(0, (((rows + 15) >> 4) - wm + 3) >> 2));
   if constexpr (!DUAL) {
-    // Paired steps: a ring slot holds two k steps (64 k) of both operands in rows of
+    // Paired steps: a ring slot holds two k steps (64 k) of one operand in rows of
     // 128 bytes, so a direct load of 8 rows x 128 bytes fetches whole lines (the
-    // half-line loads of 32-k rows brought every line into L1 twice).  Two slots.
-    // Step kt reads its fragments during step kt - 1 (after that step's barrier, if
-    // any).  An odd step kt = 2j + 1 waits for pair j + 1 (the only loads in
-    // flight), passes the barrier, and issues pair j + 2 into slot j % 2, which
-    // every wave finished reading in step 2j; an even step needs no wait and no
-    // barrier (its pair was complete at the previous barrier, and it issues no loads).
+    // half-line loads of 32-k rows brought every line into L1 twice).  Three weight
+    // slots and two activation slots (160 KB): step kt reads its fragments during
+    // step kt - 1 (after that step's barrier, if any).  An odd step kt = 2j + 1
+    // waits for pair j + 1 (the weights of pair j + 2 may stay in flight), passes
+    // the barrier, and issues the activations of pair j + 2 and the weights of pair
+    // j + 3 into the slots pair j left (every wave finished reading it in step 2j);
+    // an even step needs no wait and no barrier.  The weights, which stream from
+    // HBM, so get three steps more to land than the activations.
     const int KP = KT / 2;  // K is a multiple of 64 (the widths), so KT is even
-    auto issue_pair = [&](int pr, int u) {  // load u < 8 of pair pr: chunk u / 2 of operand u % 2
+    // slot bases: weight slot s at s * 32 KB (pair pr in slot pr % 3), activation
+    // slot t at (3 + t) * 32 KB (pair pr in slot pr % 2)
+    auto wslot = [&](int s) { return smem + s * BG_PTILEB; };
+    auto aslot = [&](int t) { return smem + (3 + t) * BG_PTILEB; };
+    // chunk i of pair pr's weights or activations (a wave's 4 of each operand) into
+    // the slot at dst
+    auto issue_w = [&](int pr, int i, uint8_t* dst) {
       int k = kbeg + pr * 2 * BG_BK;
-      const uint16_t* A = A0;
       const uint16_t* B = B0;
       if constexpr (!ONESEG) {
         if (k >= K0 && p.nseg > 1) {
           k -= K0;
-          A = A1;
           B = B1;
           if (k >= K1 && p.nseg > 2) {
             k -= K1;
-            A = A2;
             B = B2;
           }
         }
       }
-      uint8_t* st = smem + (pr & 1) * STAGEB;
-      const int i = u >> 1;
-      uint8_t* dst = st + (u & 1) * BG_PTILEB + (wave + BG_WAVES * i) * 1024;
-      if ((u & 1) == 0) {
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(B + k) + (uint64_t)(w_off[i] * 2u), dst,
-                                         16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(A + k) + (uint64_t)(x_off[i] * 2u), dst,
-                                         16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(B + k) + (uint64_t)(w_off[i] * 2u),
+                                       dst + (wave + BG_WAVES * i) * 1024, 16, 0, 0);
+    };
+    auto issue_a = [&](int pr, int i, uint8_t* dst) {
+      int k = kbeg + pr * 2 * BG_BK;
+      const uint16_t* A = A0;
+      if constexpr (!ONESEG) {
+        if (k >= K0 && p.nseg > 1) {
+          k -= K0;
+          A = A1;
+          if (k >= K1 && p.nseg > 2) {
+            k -= K1;
+            A = A2;
+          }
+        }
       }
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t*>(A + k) + (uint64_t)(x_off[i] * 2u),
+                                       dst + (wave + BG_WAVES * i) * 1024, 16, 0, 0);
     };
-    // fragment of step kt: row r of operand `op` (0 weights, 1 activations), lane
-    // group g's 16 bytes of the step's half of the 128-byte row
-    auto frag = [&](int kt, int op, int r) {
-      const uint8_t* base = smem + ((kt >> 1) & 1) * STAGEB + op * BG_PTILEB;
-      return *reinterpret_cast<const u32x4_t*>(base + bg_poff(r, (kt & 1) * 4 + g));
+    // fragment: row r of the slot at base, lane group g's 16 bytes of half h of the
+    // 128-byte row (step 2j + h of the slot's pair j)
+    auto frag = [&](const uint8_t* base, int h, int r) {
+      return *reinterpret_cast<const u32x4_t*>(base + bg_poff(r, h * 4 + g));
     };
+    // prologue: W0 A0 W1 A1 W2 in this order, so that pair 1 is complete when only
+    // W2's loads are outstanding
 #pragma unroll
-    for (int u = 0; u < 8; ++u) issue_pair(0, u);
+    for (int i = 0; i < 4; ++i) issue_w(0, i, wslot(0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_a(0, i, aslot(0));
     if (KP > 1) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) issue_pair(1, u);
-      wait_vmcnt_c<8>();
+      for (int i = 0; i < 4; ++i) issue_w(1, i, wslot(1));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) issue_a(1, i, aslot(1));
+      if (KP > 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue_w(2, i, wslot(2));
+        wait_vmcnt_c<12>();
+      } else {
+        wait_vmcnt_c<8>();
+      }
     } else {
       wait_vmcnt_c<0>();
     }
@@ -446,33 +473,46 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     constexpr int NB = decltype(nbc)::value;
     u32x4_t wf[8], xa[1][BG_MB], xb[1][BG_MB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xa[0][b] = frag(0, 1, (4 * b + wm) * 16 + r16);
+    for (int b = 0; b < NB; ++b) xa[0][b] = frag(aslot(0), 0, (4 * b + wm) * 16 + r16);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-      if constexpr (NB > 0) wf[a] = frag(0, 0, wn * 128 + a * 16 + r16);
-    // step kt with a next step: ODD steps wait and pass the barrier; ISSUE: pair
-    // kt / 2 + 2 exists (odd steps only).  The compiler's wait insertion sees the
-    // current fragments complete and the next ones as the only reads outstanding.
-    auto step = [&](int kt, const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB], auto odd, auto issue) {
+      if constexpr (NB > 0) wf[a] = frag(wslot(0), 0, wn * 128 + a * 16 + r16);
+    // step kt with a next step, whose fragments sit in the slots wb and ab.  ODD
+    // steps wait and pass the barrier: WAIT4, the weights of pair kt / 2 + 2 exist
+    // (their 4 loads may stay in flight), which is also when the activations of
+    // that pair are issued (into wa); ISSUEW: the weights of pair kt / 2 + 3 exist
+    // and are issued (into ww).  The compiler's wait insertion sees the current
+    // fragments complete and the next ones as the only reads outstanding.
+    auto step = [&](int kt, const uint8_t* wb, const uint8_t* ab, uint8_t* ww, uint8_t* wa,
+                    const u32x4_t (&xc)[1][BG_MB], u32x4_t (&xn)[1][BG_MB], auto odd, auto wait4, auto issuew) {
       constexpr bool ODD = decltype(odd)::value;
-      constexpr bool ISSUE = decltype(issue)::value;
+      constexpr bool WAIT4 = decltype(wait4)::value;
+      constexpr bool ISSUEW = decltype(issuew)::value;
+      constexpr int H = ODD ? 0 : 1;  // half of the next step's pair
       if constexpr (ODD) {
         // this wave's reads of step kt are in registers, and pair kt / 2 + 1 has landed
         __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-        wait_vmcnt_c<0>();
+        if constexpr (WAIT4)
+          wait_vmcnt_c<4>();
+        else
+          wait_vmcnt_c<0>();
         asm volatile("s_barrier" ::: "memory");
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) xn[0][b] = frag(kt + 1, 1, (4 * b + wm) * 16 + r16);
+      for (int b = 0; b < NB; ++b) xn[0][b] = frag(ab, H, (4 * b + wm) * 16 + r16);
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) acc[a][b] = mfma_16x16x32(wf[a], xc[0][b], acc[a][b]);
-        if constexpr (NB > 0) wf[a] = frag(kt + 1, 0, wn * 128 + a * 16 + r16);
-        // pair kt / 2 + 2, its loads spread over the step's MFMAs (issued together
-        // after the barrier, all waves' loads queue at the memory unit at once and
-        // each wave's MFMAs wait behind its own loads)
-        if constexpr (ISSUE) issue_pair(kt / 2 + 2, a);
+        if constexpr (NB > 0) wf[a] = frag(wb, H, wn * 128 + a * 16 + r16);
+        // the step's loads spread over its MFMAs (issued together after the
+        // barrier, all waves' loads queue at the memory unit at once and each
+        // wave's MFMAs wait behind its own loads): activations first, so that the
+        // next odd step's wait leaves only the newest weights in flight
+        if constexpr (ODD && WAIT4) {
+          if (a < 4) issue_a(kt / 2 + 2, a, wa);
+          else if (ISSUEW) issue_w(kt / 2 + 3, a - 4, ww);
+        }
       }
       // keep the interleave: the activation reads, then NB MFMAs and one read per a
       if constexpr (NB > 0) {
@@ -487,16 +527,22 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_kernel(GemmParams p) {
     const std::true_type yes{};
     const std::false_type no{};
     int kt = 0;
-    for (; kt + 4 < KT; kt += 2) {  // pair kt / 2 + 2 exists
-      step(kt, xa, xb, no, no);
-      step(kt + 1, xb, xa, yes, yes);
-    }
-    if (kt + 2 < KT) {  // the last pair but one: nothing left to issue
-      step(kt, xa, xb, no, no);
-      step(kt + 1, xb, xa, yes, no);
+    int ws = 0;  // weight slot of pair kt / 2
+    // one pair: its even step reads the second half of pair j = kt / 2, its odd step
+    // the first half of pair j + 1 and refills pair j's slots
+    auto pair = [&](auto wait4, auto issuew) {
+      const int ws1 = ws == 2 ? 0 : ws + 1;
+      const int t = (kt >> 1) & 1;
+      step(kt, wslot(ws), aslot(t), nullptr, nullptr, xa, xb, no, no, no);
+      step(kt + 1, wslot(ws1), aslot(t ^ 1), wslot(ws), aslot(t), xb, xa, yes, wait4, issuew);
+      ws = ws1;
       kt += 2;
-    }
-    step(kt, xa, xb, no, no);  // the last pair: its second step has no next
+    };
+    while (kt + 6 < KT) pair(yes, yes);  // pair kt / 2 + 3 exists
+    if (kt + 4 < KT) pair(yes, no);      // pair kt / 2 + 2 is the last
+    if (kt + 2 < KT) pair(no, no);       // pair kt / 2 + 1 is the last: nothing to issue
+    // the last pair: its second step has no next
+    step(kt, wslot(ws), aslot((kt >> 1) & 1), nullptr, nullptr, xa, xb, no, no, no);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
