@@ -760,8 +760,14 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const bool fp4 = c.expert_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16;
   const int shared_fmt = c.shared_format == LATENTMOE_FORMAT_FP4_E2M1_E4M3_B16 ? WF_FP4 : WF_BF16;
   const int proj_fmt = c.proj_format == LATENTMOE_FORMAT_FP8_E4M3 ? WF_FP8 : WF_BF16;
-  const bool shared_a16 = shared_fmt != WF_BF16;  // single bf16 h_s
-  const bool expert_a16 = fp4;                    // single bf16 z, h
+  // single bf16 activations next to FP4 / FP8 weights (R17).  In a layer with FP4
+  // experts the bf16 shared expert's h_s and W_up's input y_lat are single bf16 too
+  // (on the multi-stream path, where the pairs cost a second MFMA pass): the layer's
+  // output is held to the FP4 bound, and the expert path's own bf16 activations
+  // already put ~7e-3 of rms(y) into it; a single h_s adds at most ~8e-3.
+  const bool expert_a16 = fp4;                        // single bf16 z, h
+  const bool shared_a16 = shared_fmt != WF_BF16 || fp4;  // single bf16 h_s
+  const bool ylat_a16 = proj_fmt != WF_BF16 || fp4;      // W_up reads y_lat's high part
   const long long TK = (long long)T * K;
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
@@ -1112,7 +1118,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.start(LATENTMOE_STAGE_UP_PROJ);
   GemmParams pp = base_params();
   pp.seg[0] = GemmSeg{b.y_lat, w.w_up, L};
-  pp.a_lo = proj_fmt != WF_BF16 ? nullptr : b.y_lat_lo;
+  pp.a_lo = ylat_a16 ? nullptr : b.y_lat_lo;
   pp.nseg = 1;
   pp.lda = L;
   pp.ldb = L;
