@@ -62,6 +62,10 @@ constexpr int TARGET_BLOCKS = 256;      // streaming kernel: 8-wave blocks, seve
 // the two stacked GEMMs of the decode-sized path (one block per CU at 256 blocks: the
 // blocks' load latency left HBM idle; 512 put two on each CU, -9 us per forward)
 constexpr int TARGET_BLOCKS_STACKED = 512;
+// mid-sized batches (65 .. STACK_X_ROWS tokens) with the stacked weights run the
+// three GEMMs over x as one large-tile launch and one reduce (their own launches
+// there are short split-K runs of a few row tiles, each with its own reduce)
+constexpr int STACK_X_ROWS = 1024;
 // the decode-sized up-projection alone (the shared expert's S2 ran with expert down)
 constexpr int TARGET_BLOCKS_UP = 256;
 constexpr int TARGET_BLOCKS_BIG = 256;  // large-tile kernel: one 8-wave block per CU
@@ -212,6 +216,10 @@ size_t max_partial_floats(const latentmoe_config& c, bool linear) {
     for (const G& g : gs) {
       Plan p = plan_dense(T, g.N, g.K);
       if (p.splits > 1 || g.always) best = std::max(best, (size_t)p.splits * T * g.N);
+    }
+    if (linear && T > STREAM_ROWS_BIG && T <= STACK_X_ROWS) {  // the stacked GEMM over x
+      const int NX = 3 * c.n_experts + c.latent + c.shared_hidden;
+      best = std::max(best, (size_t)plan_dense(T, NX, c.d).splits * T * NX);
     }
     if (linear && T <= STREAM_ROWS_BIG) {  // the stacked GEMMs always leave partials
       const G lg[] = {{3 * c.n_experts + c.latent + c.shared_hidden, c.d, true},
@@ -794,7 +802,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     record(ev, s);
     wait(to, ev);
   };
-  auto shared_expert = [&]() {
+  auto shared_up = [&]() {
     // ---- shared expert (side stream): h_s = relu(S1 x)^2 as bf16 hi + lo, y = S2 h_s ----
     tm.start(LATENTMOE_STAGE_SHARED_UP, side);
     GemmParams ps = base_params();
@@ -813,7 +821,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     ps.ldc = ms;
     run_dense(h, ps, T, side, false, b.partial2, shared_fmt, b.s1_bf16);
     tm.stop(LATENTMOE_STAGE_SHARED_UP, side);
-
+  };
+  auto shared_down = [&]() {
     tm.start(LATENTMOE_STAGE_SHARED_DOWN, side);
     GemmParams p2 = base_params();
     p2.seg[0] = GemmSeg{b.hs_hi, w.shared_w2, ms};
@@ -856,6 +865,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   // shared expert run on the side streams
   const bool linear = h->linear && T <= STREAM_ROWS_BIG;
   h->last_linear = linear;
+  const bool stack_x = h->linear && !linear && T <= STACK_X_ROWS;
   const int LS = L + ms;  // row length of the stacked activations [y_lat | h_s]
   // bf16 experts on the streaming kernel: the shared expert's GEMMs run inside the
   // expert launches (S1 with expert up, S2 with expert down) instead of in the
@@ -881,6 +891,27 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       tm.start(st);
       tm.stop(st);
     }
+  } else if (stack_x) {
+    // ---- 1. router logits, z = W_down x and h_s = relu(S1 x)^2 in one GEMM over x
+    // (partial sums, then one reduce that sums the router pieces); S2 on the side ----
+    tm.start(LATENTMOE_STAGE_ROUTER);
+    GemmParams px = base_params();
+    px.seg[0] = GemmSeg{x, b.wx, d};
+    px.nseg = 1;
+    px.lda = d;
+    px.ldb = d;
+    px.N = 3 * N + L + ms;
+    px.ldc = px.N;
+    const int splits = run_dense(h, px, T, s, true, b.partial);
+    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, ms, b.logits, b.z, b.z_lo, b.hs_hi,
+                   b.hs_lo, ms, s);
+    tm.stop(LATENTMOE_STAGE_ROUTER);
+    for (int st : {LATENTMOE_STAGE_DOWN_PROJ, LATENTMOE_STAGE_SHARED_UP}) {
+      tm.start(st);
+      tm.stop(st);
+    }
+    fork_to(side, h->ev_fork2);
+    shared_down();
   } else {
     fork_to(side2, h->ev_fork);
     down_proj();
@@ -899,7 +930,8 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
     run_dense(h, pr, T, s, false);
     tm.stop(LATENTMOE_STAGE_ROUTER);
     fork_to(side, h->ev_fork2);
-    shared_expert();
+    shared_up();
+    shared_down();
   }
 
   // ---- 2. top-K + softmax over the logits (plus the bias, when given) ----
@@ -939,7 +971,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_BUCKET);
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
-  if (!linear) wait(s, h->ev_join2);
+  if (!linear && !stack_x) wait(s, h->ev_join2);
 
   // ---- 5/6. grouped expert GEMMs ----
   GemmParams pe = base_params();
