@@ -179,9 +179,13 @@ int latentmoe_forward_graph(latentmoe_handle_t h, const uint16_t* x, int32_t T, 
 
 /* Entry point that allocates nothing, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
- * forbid hipMalloc.  Same layer and results as latentmoe_init + latentmoe_forward
- * (the same kernels, all of them on `stream` in program order) without a handle:
- * the workspace for T tokens is laid out in a file-scope device array of
+ * forbid hipMalloc.  The same layer as latentmoe_init + latentmoe_forward, all
+ * of it on `stream` in program order, without a handle.  It keeps no stacked
+ * weight copies, so the router, W_down and the shared expert run as their own
+ * GEMMs (the handle runs the GEMMs over x as one launch): outputs agree with
+ * latentmoe_forward to rounding (max difference ~1e-5 of rms(y)), top-K sets
+ * equal and gates within ~1e-6 unless two logits tie to rounding.  The workspace
+ * for T tokens is laid out in a file-scope device array of
  * LATENTMOE_STATIC_SCRATCH_BYTES bytes (64 MiB, enough for T = 64 at the Super
  * decode shapes), which each GPU the library runs on holds until the process
  * ends.  Each call derives the router's split weights into that array, clears

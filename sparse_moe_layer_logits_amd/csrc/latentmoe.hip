@@ -217,8 +217,8 @@ size_t max_partial_floats(const latentmoe_config& c, bool linear) {
       Plan p = plan_dense(T, g.N, g.K);
       if (p.splits > 1 || g.always) best = std::max(best, (size_t)p.splits * T * g.N);
     }
-    if (linear && T > STREAM_ROWS_BIG && T <= STACK_X_ROWS) {  // the stacked GEMM over x
-      const int NX = 3 * c.n_experts + c.latent + c.shared_hidden;
+    if (linear && T > STREAM_ROWS_BIG) {  // the stacked GEMM over x
+      const int NX = 3 * c.n_experts + c.latent + (T <= STACK_X_ROWS ? c.shared_hidden : 0);
       best = std::max(best, (size_t)plan_dense(T, NX, c.d).splits * T * NX);
     }
     if (linear && T <= STREAM_ROWS_BIG) {  // the stacked GEMMs always leave partials
@@ -866,6 +866,9 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   const bool linear = h->linear && T <= STREAM_ROWS_BIG;
   h->last_linear = linear;
   const bool stack_x = h->linear && !linear && T <= STACK_X_ROWS;
+  // above that, the router pieces and W_down still share one launch and one reduce,
+  // with the shared expert on the side stream
+  const bool stack_rz = h->linear && !linear && !stack_x;
   const int LS = L + ms;  // row length of the stacked activations [y_lat | h_s]
   // bf16 experts on the streaming kernel: the shared expert's GEMMs run inside the
   // expert launches (S1 with expert up, S2 with expert down) instead of in the
@@ -891,27 +894,36 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
       tm.start(st);
       tm.stop(st);
     }
-  } else if (stack_x) {
-    // ---- 1. router logits, z = W_down x and h_s = relu(S1 x)^2 in one GEMM over x
-    // (partial sums, then one reduce that sums the router pieces); S2 on the side ----
+  } else if (stack_x || stack_rz) {
+    // ---- 1. router logits, z = W_down x and (up to STACK_X_ROWS tokens) h_s =
+    // relu(S1 x)^2 in one GEMM over x (partial sums, then one reduce that sums the
+    // router pieces); the rest of the shared expert on the side stream ----
+    const int MSX = stack_x ? ms : 0;
+    if (stack_rz) {
+      fork_to(side, h->ev_fork2);
+      shared_up();
+      shared_down();
+    }
     tm.start(LATENTMOE_STAGE_ROUTER);
     GemmParams px = base_params();
     px.seg[0] = GemmSeg{x, b.wx, d};
     px.nseg = 1;
     px.lda = d;
     px.ldb = d;
-    px.N = 3 * N + L + ms;
+    px.N = 3 * N + L + MSX;
     px.ldc = px.N;
     const int splits = run_dense(h, px, T, s, true, b.partial);
-    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, ms, b.logits, b.z, b.z_lo, b.hs_hi,
+    launch_xreduce(b.partial, splits, (long long)T * px.N, T, N, L, MSX, b.logits, b.z, b.z_lo, b.hs_hi,
                    b.hs_lo, ms, s);
     tm.stop(LATENTMOE_STAGE_ROUTER);
-    for (int st : {LATENTMOE_STAGE_DOWN_PROJ, LATENTMOE_STAGE_SHARED_UP}) {
-      tm.start(st);
-      tm.stop(st);
+    tm.start(LATENTMOE_STAGE_DOWN_PROJ);
+    tm.stop(LATENTMOE_STAGE_DOWN_PROJ);
+    if (stack_x) {
+      tm.start(LATENTMOE_STAGE_SHARED_UP);
+      tm.stop(LATENTMOE_STAGE_SHARED_UP);
+      fork_to(side, h->ev_fork2);
+      shared_down();
     }
-    fork_to(side, h->ev_fork2);
-    shared_down();
   } else {
     fork_to(side2, h->ev_fork);
     down_proj();
@@ -971,7 +983,7 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   tm.stop(LATENTMOE_STAGE_BUCKET);
 
   // ---- 4. wait for z = W_down x (side stream 2) ----
-  if (!linear && !stack_x) wait(s, h->ev_join2);
+  if (!linear && !stack_x && !stack_rz) wait(s, h->ev_join2);
 
   // ---- 5/6. grouped expert GEMMs ----
   GemmParams pe = base_params();
