@@ -113,7 +113,7 @@ struct Buffers {
   float* logits = nullptr;
   float* partial = nullptr;
   float* partial2 = nullptr;  // split-K partials of the shared expert (side stream)
-  float* partial3 = nullptr;  // split-K partials of W_down (side stream 2)
+  float* partial3 = nullptr;  // split-K partials of W_down (side stream 2, without stacked copies)
   size_t partial_cap = 0;  // floats
   int* idx = nullptr;
   float* gates = nullptr;
@@ -448,7 +448,7 @@ struct latentmoe_handle_s {
   bool last_linear = false;  // the last forward took that path (y_lat, h_s in the stacked rows)
   // the shared expert runs on a side stream forked from the caller's stream
   hipStream_t side = nullptr;
-  hipStream_t side2 = nullptr;  // W_down, concurrent with routing
+  hipStream_t side2 = nullptr;  // W_down without stacked copies; the paired rows' expert down
   hipEvent_t ev_fork = nullptr, ev_fork2 = nullptr, ev_join = nullptr, ev_join2 = nullptr;
   hipEvent_t ev_hi = nullptr, ev_hi_done = nullptr;  // the hi class's expert down beside the bf16 class
   // graph replay of the whole forward (latentmoe_forward_graph)
@@ -780,11 +780,13 @@ void forward_impl(latentmoe_handle_t h, const uint16_t* x, int32_t T, float* y, 
   StageTimer tm(h, s);
   if (!timing) tm.on = false;
 
-  // The shared expert and W_down do not depend on routing: each runs on a side
-  // stream forked from the caller's stream (same priority) and joins before
-  // its consumer.  W_down is forked at the start; the shared expert after the
-  // router GEMM, so the router runs at full speed and the shared expert's
-  // weight stream fills the latency-bound top-K / bucketing chain.
+  // The shared expert and W_down do not depend on routing.  Above 64 tokens the
+  // shared expert (from 65 to STACK_X_ROWS tokens only S2) runs on a side stream
+  // forked from the caller's stream (same priority) and joins before W_up, so its
+  // GEMMs fill the latency-bound top-K / bucketing chain.  With the stacked weight
+  // copies W_down shares the router's launch on the caller's stream; without them
+  // (FP8 projections, an FP4 shared expert) it runs on a second side stream forked
+  // at the start, and the shared expert forks after the router GEMM.
   // Stage-timed calls run in program order on the caller's stream as well, so
   // each stage's events bracket its own kernels with nothing beside them.
   const bool one_stream = h->serial || tm.on;
